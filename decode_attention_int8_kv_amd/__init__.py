@@ -1,0 +1,224 @@
+"""Python binding of libq8kv: q8 single-query decode attention for MI355X.
+
+Argument marshalling only.  Every step of the path runs in the library's HIP
+kernels (include/q8kv.h declares the C ABI); torch tensors are used only as
+device memory and ``torch.cuda.current_stream()`` as the stream.  There is no
+CPU or PyTorch fallback: if ``libq8kv.so`` is missing, importing the library
+handle raises.
+
+Entry points (same names as the C ABI, without the ``q8_`` prefix):
+  kv_append, decode_attn, decode_attn_partial, decode_attn_merge,
+  decode_attn_workspace_bytes, decode_attn_auto_parts, quantize_q,
+  qk_block_partials, abi_version, status_string, last_error.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8kv.so")
+
+Q8_OK, Q8_EINVAL, Q8_EUNSUPPORTED, Q8_EWORKSPACE, Q8_EHIP = 0, -1, -2, -3, -4
+DEV_BAD_SEQ_LEN, DEV_BAD_BLOCK_ID, DEV_BAD_TOKEN = 0x1, 0x2, 0x4
+HEAD_DIM = 128
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        lib = _load()
+        text = lib.q8_status_string(status).decode()
+        detail = lib.q8_last_error().decode() if status == Q8_EHIP else ""
+        super().__init__(f"{where}: {text} ({status}) {detail}".strip())
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("nkv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_bs", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libq8kv.so not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    LP, BP = ctypes.POINTER(_Layer), ctypes.POINTER(_Batch)
+    lib.q8_kv_append.argtypes = [LP, BP, I32, P, P, P, P, P, P]
+    lib.q8_kv_append.restype = I32
+    lib.q8_decode_attn_auto_parts.argtypes = [LP, BP, I32]
+    lib.q8_decode_attn_auto_parts.restype = I32
+    lib.q8_decode_attn_workspace_bytes.argtypes = [LP, BP, I32, I32]
+    lib.q8_decode_attn_workspace_bytes.restype = SZ
+    for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge"):
+        fn = getattr(lib, name)
+        fn.argtypes = [LP, BP, I32, P, F, P, I32, P, SZ, P, P]
+        fn.restype = I32
+    lib.q8_quantize_q.argtypes = [P, I32, I32, P, P, P]
+    lib.q8_quantize_q.restype = I32
+    lib.q8_qk_block_partials.argtypes = [LP, BP, I32, P, P, P, P]
+    lib.q8_qk_block_partials.restype = I32
+    lib.q8_status_string.argtypes = [I32]
+    lib.q8_status_string.restype = ctypes.c_char_p
+    lib.q8_last_error.restype = ctypes.c_char_p
+    lib.q8_abi_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes handle of libq8kv.so (raises ImportError if absent)."""
+    return _load()
+
+
+# ------------------------------------------------------------------ plumbing --
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != Q8_OK:
+        raise Q8Error(status, where)
+
+
+@dataclasses.dataclass
+class KVLayer:
+    """One layer's blocked q8 pool (torch tensors on the GPU, or raw pointers).
+
+    k_codes/v_codes: int8 [num_blocks, kv_bs, nkv_heads * head_dim]
+    k_scale/v_scale: fp32 [num_blocks, kv_bs, nkv_heads]
+    """
+    k_codes: object
+    v_codes: object
+    k_scale: object
+    v_scale: object
+    nkv_heads: int
+    kv_bs: int
+    num_blocks: int
+    head_dim: int = HEAD_DIM
+
+    def c(self) -> _Layer:
+        return _Layer(self.nkv_heads, self.head_dim, self.kv_bs, self.num_blocks,
+                      _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.v_scale))
+
+
+@dataclasses.dataclass
+class Batch:
+    """Per-step batch metadata: block_table int32 [batch, max_blocks_per_seq],
+    seq_lens int32 [batch] (device tensors), and host-side max_seq_len."""
+    block_table: object
+    seq_lens: object
+    batch: int
+    max_blocks_per_seq: int
+    max_seq_len: int
+
+    def c(self) -> _Batch:
+        return _Batch(self.batch, self.max_blocks_per_seq, self.max_seq_len,
+                      _ptr(self.block_table), _ptr(self.seq_lens))
+
+
+def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head_dim: int = HEAD_DIM) -> KVLayer:
+    """Allocate an uninitialised pool with torch (device memory only)."""
+    import torch
+    kc = torch.empty((num_blocks, kv_bs, nkv_heads * head_dim), dtype=torch.int8, device=device)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((num_blocks, kv_bs, nkv_heads), dtype=torch.float32, device=device)
+    vs = torch.empty_like(ks)
+    return KVLayer(kc, vc, ks, vs, nkv_heads, kv_bs, num_blocks, head_dim)
+
+
+def make_batch(block_table, seq_lens, max_seq_len: int) -> Batch:
+    return Batch(block_table, seq_lens, int(block_table.shape[0]), int(block_table.shape[1]), int(max_seq_len))
+
+
+# ------------------------------------------------------------- entry points --
+def kv_append(layer: KVLayer, batch: Batch, tok_seq, tok_pos, k_new, v_new, dev_status=None, stream=None):
+    """q8_kv_append: quantize k_new/v_new [n_tokens, nkv, 128] fp32 into the cache."""
+    n = int(tok_seq.shape[0])
+    st = _load().q8_kv_append(ctypes.byref(layer.c()), ctypes.byref(batch.c()), n, _ptr(tok_seq),
+                              _ptr(tok_pos), _ptr(k_new), _ptr(v_new), _ptr(dev_status), _stream(stream))
+    _check(st, "q8_kv_append")
+
+
+def decode_attn_auto_parts(layer: KVLayer, batch: Batch, nq_heads: int) -> int:
+    return int(_load().q8_decode_attn_auto_parts(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads))
+
+
+def decode_attn_workspace_bytes(layer: KVLayer, batch: Batch, nq_heads: int, nparts: int = 0) -> int:
+    return int(_load().q8_decode_attn_workspace_bytes(ctypes.byref(layer.c()), ctypes.byref(batch.c()),
+                                                      nq_heads, nparts))
+
+
+def _decode(name, layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream):
+    fn = getattr(_load(), name)
+    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    st = fn(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q), float(scale), _ptr(out),
+            nparts, _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream))
+    _check(st, name)
+
+
+def decode_attn(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
+    """q8_decode_attn: out [batch, nq, 128] fp32 from q [batch, nq, 128] fp32."""
+    _decode("q8_decode_attn", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def decode_attn_partial(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
+    _decode("q8_decode_attn_partial", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def decode_attn_merge(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
+    _decode("q8_decode_attn_merge", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def quantize_q(q, codes, qscale, stream=None):
+    """q8_quantize_q test hook: q [rows, 128] fp32 -> codes int8 [rows, 128], qscale fp32 [rows, 4]."""
+    rows = int(q.shape[0])
+    st = _load().q8_quantize_q(_ptr(q), rows, HEAD_DIM, _ptr(codes), _ptr(qscale), _stream(stream))
+    _check(st, "q8_quantize_q")
+
+
+def qk_block_partials(layer, batch, nq_heads, q, partials, dev_status=None, stream=None):
+    """q8_qk_block_partials test hook: partials int32 [batch, nq, max_seq_len, 4]."""
+    st = _load().q8_qk_block_partials(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q),
+                                      _ptr(partials), _ptr(dev_status), _stream(stream))
+    _check(st, "q8_qk_block_partials")
+
+
+def abi_version() -> int:
+    return int(_load().q8_abi_version())
+
+
+def status_string(status: int) -> str:
+    return _load().q8_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _load().q8_last_error().decode()

@@ -1,0 +1,460 @@
+// q8kv_decode.hip -- single-query decode attention over the blocked q8 cache.
+//
+// Method ("9-2 flash_attn_single_q_q8_neon -- 单 q 单遍扫全 KV"):
+//   §2 segment 1: the query is quantized once, in 32-element blocks;
+//   §2 segment 2: per token, int8 dot products give one int32 sum per block,
+//     rescaled by the block's Q scale, then by the K row scale and the
+//     softmax scale; an online softmax keeps the running max M and sum S and
+//     rescales what has been accumulated whenever M rises; V is accumulated
+//     as int8 code times (weight x V row scale), weights staying fp32;
+//   §2 segment 3: one division by S at the end.
+// §1 and §3 of the same page: the cache is read exactly once.
+//
+// GPU organisation (gfx950, wave64):
+//   * The batch's tiles (32 tokens of one sequence) are laid end to end and
+//     cut into `nparts` equal contiguous ranges; one workgroup per range (and
+//     per group of 8 KV heads) walks its range.  Each KV head is one wave, so
+//     the K/V rows of a head are read once for all of its G = nq/nkv query
+//     heads, and a workgroup's waves together read whole token rows.
+//   * Per tile the rescale is applied once with the tile's max (the online
+//     softmax in blocked form, "online softmax 分块语义" in §2 segment 2):
+//     exactly the per-token recurrence up to fp32 rounding.
+//   * Scores are kept in the log2 domain (scale * log2 e folded into the
+//     per-token factor) so the weights are single v_exp_f32 instructions.
+//   * A sequence cut by a range boundary leaves (M, S, acc) partial states
+//     in the workspace; the merge kernel combines them with the same rescale
+//     rule and divides once.  A sequence inside one range is finished in place.
+#include "q8kv_tile.hpp"
+#include "q8kv_internal.hpp"
+
+namespace q8kv {
+
+struct DecodeParams {
+    CacheView cache;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    const float *q;
+    float *out;
+    int32_t *ws_prefix;   // [batch + 1] tile prefix over the batch
+    float2 *ws_ms;        // [nparts][2][nq] (M, S) of cut pieces
+    float *ws_acc;        // [nparts][2][nq][128] accumulators of cut pieces
+    int32_t *dev_status;
+    int32_t batch;
+    int32_t nq;
+    int32_t max_blocks_per_seq;
+    int32_t max_seq_len;
+    int32_t nparts;
+    int32_t head_groups;
+    float sc;             // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ int part_start(int i, int total, int nparts)
+{
+    return (int)(((long long)i * total) / nparts);
+}
+
+// The range that holds tile x (0 <= x < total).
+__device__ __forceinline__ int part_of(int x, int total, int nparts)
+{
+    return (int)((((long long)x + 1) * nparts - 1) / total);
+}
+
+// Tile prefix over the batch into LDS: pref[b] = number of tiles of the
+// sequences before b.  A length outside [0, max_seq_len] counts as empty.
+__device__ void build_prefix(const DecodeParams &p, int *pref, bool report)
+{
+    for (int b = threadIdx.x; b < p.batch; b += blockDim.x) {
+        int n = p.seq_lens[b];
+        if (n < 0 || n > p.max_seq_len) {
+            if (report && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
+            n = 0;
+        }
+        pref[b + 1] = (n + kTile - 1) / kTile;
+    }
+    if (threadIdx.x == 0) pref[0] = 0;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int carry = 0;
+        for (int base = 1; base <= p.batch; base += 64) {
+            const int idx = base + lane;
+            int v = (idx <= p.batch) ? pref[idx] : 0;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int u = __shfl_up(v, off, 64);
+                if (lane >= off) v += u;
+            }
+            if (idx <= p.batch) pref[idx] = v + carry;
+            carry += __shfl(v, 63, 64);
+        }
+    }
+    __syncthreads();
+}
+
+// One wave: attention of the G query heads of KV head kh over tiles
+// [lt0, lt1) of sequence b (length n).
+template <int G>
+__device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
+                                             int lt0, int lt1, int n, bool whole, int part,
+                                             int slot)
+{
+    const int c = lane & 7, tslot = lane >> 3;
+
+    // Q quantized once per (sequence, head) ("9-2" §2 segment 1).
+    uint4 qc[G];
+    float qs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        quantize_q_quarter(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim, c, qc[g], qs[g]);
+
+    float M[G], S[G], acc[G][16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        M[g] = -INFINITY;
+        S[g] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+    }
+
+    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
+
+    auto process = [&](const Tile &t) {
+        float s[4][G];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bool ok = (t.valid >> kk) & 1u;
+            const float f = t.ks[kk] * p.sc;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                // exact int32 block sum, then x Q block scale, summed over the 4 blocks
+                float x = (float)block_partial(t.k[kk], qc[g]) * qs[g];
+                x += dpp_f<kDppQuadXor2>(x);
+                x += dpp_f<kDppHalfMirror>(x);
+                s[kk][g] = ok ? x * f : -INFINITY;
+            }
+        }
+        // Tile max, rescale of what has accumulated if M rises.
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float m = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]));
+            m = max_over_slots(m);
+            if (m > M[g]) {
+                const float a = __builtin_amdgcn_exp2f(M[g] - m);
+                S[g] *= a;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[g][j] *= a;
+                M[g] = m;
+            }
+        }
+        // Weights and V accumulation: acc += code_v * (w * vs).
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bool ok = (t.valid >> kk) & 1u;
+            float w[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                // masked tokens contribute nothing (their scale may be any bit pattern)
+                const float pw = ok ? __builtin_amdgcn_exp2f(s[kk][g] - M[g]) : 0.0f;
+                S[g] += pw;
+                w[g] = ok ? pw * t.vs[kk] : 0.0f;
+            }
+            const uint32_t words[4] = {t.v[kk].x, t.v[kk].y, t.v[kk].z, t.v[kk].w};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float vf = byte_f(words[j >> 2], j & 3);
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g][j] = fmaf(w[g], vf, acc[g][j]);
+            }
+        }
+    };
+
+    // Two register tiles: the next tile's loads are in flight while the
+    // current one is processed.
+    Tile ta, tb;
+    int lt = lt0;
+    load_tile<true>(p.cache, bt, kh, lane, lt * kTile, n, p.dev_status, ta);
+    while (true) {
+        if (lt + 1 < lt1) load_tile<true>(p.cache, bt, kh, lane, (lt + 1) * kTile, n, p.dev_status, tb);
+        process(ta);
+        if (++lt >= lt1) break;
+        if (lt + 1 < lt1) load_tile<true>(p.cache, bt, kh, lane, (lt + 1) * kTile, n, p.dev_status, ta);
+        process(tb);
+        if (++lt >= lt1) break;
+    }
+
+    // Sum the 8 token slots of the wave.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        S[g] = sum_over_slots(S[g]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[g][j] = sum_over_slots(acc[g][j]);
+    }
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (tslot != g) continue;
+        const int h = kh * G + g;
+        if (whole) {
+            // one division at the end ("9-2" §2 segment 3)
+            const float sg = S[g];
+            float4 *o = reinterpret_cast<float4 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float4 r;
+                r.x = sg > 0.0f ? acc[g][4 * j + 0] / sg : 0.0f;
+                r.y = sg > 0.0f ? acc[g][4 * j + 1] / sg : 0.0f;
+                r.z = sg > 0.0f ? acc[g][4 * j + 2] / sg : 0.0f;
+                r.w = sg > 0.0f ? acc[g][4 * j + 3] / sg : 0.0f;
+                o[j] = r;
+            }
+        } else {
+            const size_t idx = ((size_t)part * 2 + slot) * p.nq + h;
+            float4 *a = reinterpret_cast<float4 *>(p.ws_acc + idx * kHeadDim + 16 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                a[j] = make_float4(acc[g][4 * j], acc[g][4 * j + 1], acc[g][4 * j + 2], acc[g][4 * j + 3]);
+            if (c == 0) p.ws_ms[idx] = make_float2(M[g], S[g]);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
+{
+    __shared__ int pref[kMaxBatch + 1];
+    const int part = blockIdx.x / p.head_groups;
+    const int hg = blockIdx.x - part * p.head_groups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kh = hg * kMaxWavesPerWG + wave;
+
+    build_prefix(p, pref, blockIdx.x == 0);
+    if (blockIdx.x == 0)
+        for (int b = threadIdx.x; b <= p.batch; b += blockDim.x) p.ws_prefix[b] = pref[b];
+
+    const int total = pref[p.batch];
+    const int start = part_start(part, total, p.nparts);
+    const int end = part_start(part + 1, total, p.nparts);
+
+    if (kh < p.cache.nkv && start < end) {
+        // the sequence holding tile `start`: the largest b with pref[b] <= start
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pref[mid] <= start) lo = mid; else hi = mid - 1;
+        }
+        int b = uniform(lo);
+        int x = start;
+        while (x < end) {
+            while (pref[b + 1] <= x) ++b;
+            b = uniform(b);
+            const int a0 = uniform(pref[b]), e0 = uniform(pref[b + 1]);
+            const int x1 = min(end, e0);
+            const bool whole = (x == a0) && (x1 == e0);
+            const int slot = (x == start) ? 0 : 1;
+            int n = p.seq_lens[b];
+            n = uniform(n);
+            attend_piece<G>(p, b, kh, lane, x - a0, x1 - a0, n, whole, part, slot);
+            x = x1;
+        }
+    }
+
+    // Zero the output rows of empty sequences whose tile position lies in
+    // this range (the last range also takes those at the very end).
+    if (hg == 0) {
+        int lo = 0, hi = p.batch;   // first b with pref[b] >= start
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pref[mid] < start) lo = mid + 1; else hi = mid;
+        }
+        const bool last = (part == p.nparts - 1);
+        for (int b = lo; b < p.batch && (pref[b] < end || (last && pref[b] <= total)); ++b) {
+            if (pref[b + 1] != pref[b]) continue;
+            float4 *o = reinterpret_cast<float4 *>(p.out + (size_t)b * p.nq * kHeadDim);
+            for (int i = threadIdx.x; i < p.nq * (kHeadDim / 4); i += blockDim.x)
+                o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- merge ----
+struct MergeParams {
+    const int32_t *ws_prefix;
+    const float2 *ws_ms;
+    const float *ws_acc;
+    float *out;
+    int32_t batch;
+    int32_t nq;
+    int32_t nparts;
+};
+
+constexpr int kMaxMergeWaves = 16;
+
+// One workgroup per (sequence, query head) whose tiles span several ranges:
+// combines the pieces' (M, S, acc) with the online-softmax rescale rule
+// ("9-2" §2 segment 2 applied to whole partial states), in a fixed order,
+// then divides once.
+__global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(MergeParams p)
+{
+    const int b = blockIdx.x / p.nq, h = blockIdx.x - b * p.nq;
+    const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1], total = p.ws_prefix[p.batch];
+    if (e0 == a0) return;
+    const int i0 = part_of(a0, total, p.nparts), i1 = part_of(e0 - 1, total, p.nparts);
+    if (i0 == i1) return;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
+    for (int i = i0 + wave; i <= i1; i += waves) {
+        const int st = part_start(i, total, p.nparts), en = part_start(i + 1, total, p.nparts);
+        if (st == en) continue;
+        const int slot = (i == i0 && st < a0) ? 1 : 0;
+        const size_t idx = ((size_t)i * 2 + slot) * p.nq + h;
+        const float2 ms = p.ws_ms[idx];
+        const float2 av = reinterpret_cast<const float2 *>(p.ws_acc + idx * kHeadDim)[lane];
+        if (ms.x == -INFINITY) continue;
+        const float mn = fmaxf(m, ms.x);
+        const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ms.x - mn);
+        s = s * fo + ms.y * fn;
+        ax = ax * fo + av.x * fn;
+        ay = ay * fo + av.y * fn;
+        m = mn;
+    }
+
+    __shared__ float sh_m[kMaxMergeWaves], sh_s[kMaxMergeWaves];
+    __shared__ float2 sh_a[kMaxMergeWaves][64];
+    if (lane == 0) {
+        sh_m[wave] = m;
+        sh_s[wave] = s;
+    }
+    sh_a[wave][lane] = make_float2(ax, ay);
+    __syncthreads();
+    if (wave != 0) return;
+    m = -INFINITY;
+    s = 0.0f;
+    ax = ay = 0.0f;
+    for (int w = 0; w < waves; ++w) {
+        const float mw = sh_m[w];
+        if (mw == -INFINITY) continue;
+        const float mn = fmaxf(m, mw);
+        const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(mw - mn);
+        const float2 aw = sh_a[w][lane];
+        s = s * fo + sh_s[w] * fn;
+        ax = ax * fo + aw.x * fn;
+        ay = ay * fo + aw.y * fn;
+        m = mn;
+    }
+    float2 r = make_float2(0.0f, 0.0f);
+    if (s > 0.0f) r = make_float2(ax / s, ay / s);
+    reinterpret_cast<float2 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim)[lane] = r;
+}
+
+// ----------------------------------------------------------------- host ----
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int decode_blocks_per_cu(int group, int waves)
+{
+    int nb = 0;
+    const void *fn = nullptr;
+    switch (group) {
+    case 1: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<1>); break;
+    case 2: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<4>); break;
+    default: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<8>); break;
+    }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, waves * 64, 0) != hipSuccess || nb < 1)
+        nb = 1;
+    return nb;
+}
+
+int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq)
+{
+    const int waves = layer.nkv_heads < kMaxWavesPerWG ? layer.nkv_heads : kMaxWavesPerWG;
+    const int head_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+    }
+    const long long slots = (long long)cus * decode_blocks_per_cu(nq / layer.nkv_heads, waves) / head_groups;
+    const long long tiles_ub = (long long)batch.batch * ((batch.max_seq_len + kTile - 1) / kTile);
+    long long parts = slots < tiles_ub ? slots : tiles_ub;
+    if (parts < 1) parts = 1;
+    return (int)parts;
+}
+
+DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts)
+{
+    DecodePlan pl;
+    pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
+    pl.head_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    pl.waves = layer.nkv_heads < kMaxWavesPerWG ? layer.nkv_heads : kMaxWavesPerWG;
+    // merge waves: about the number of pieces a sequence is cut into
+    long long per_seq = (long long)pl.nparts / (batch.batch > 0 ? batch.batch : 1) + 2;
+    int mw = 1;
+    while (mw < kMaxMergeWaves && mw < per_seq) mw <<= 1;
+    pl.merge_waves = mw;
+    pl.off_prefix = 0;
+    pl.off_ms = align_up(sizeof(int32_t) * ((size_t)batch.batch + 1), 256);
+    pl.off_acc = pl.off_ms + align_up(sizeof(float) * 2 * 2 * (size_t)pl.nparts * nq, 256);
+    pl.bytes = pl.off_acc + sizeof(float) * 2 * (size_t)pl.nparts * nq * kHeadDim;
+    return pl;
+}
+
+hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
+                                 const float *q, float scale, float *out, const DecodePlan &plan,
+                                 void *workspace, int32_t *dev_status, hipStream_t stream)
+{
+    DecodeParams p;
+    p.cache.k_codes = layer.k_codes;
+    p.cache.v_codes = layer.v_codes;
+    p.cache.k_scale = layer.k_scale;
+    p.cache.v_scale = layer.v_scale;
+    p.cache.nkv = layer.nkv_heads;
+    p.cache.kv_bs_log2 = ilog2(layer.kv_bs);
+    p.cache.num_blocks = layer.num_blocks;
+    p.block_table = batch.block_table;
+    p.seq_lens = batch.seq_lens;
+    p.q = q;
+    p.out = out;
+    char *ws = static_cast<char *>(workspace);
+    p.ws_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
+    p.ws_ms = reinterpret_cast<float2 *>(ws + plan.off_ms);
+    p.ws_acc = reinterpret_cast<float *>(ws + plan.off_acc);
+    p.dev_status = dev_status;
+    p.batch = batch.batch;
+    p.nq = nq;
+    p.max_blocks_per_seq = batch.max_blocks_per_seq;
+    p.max_seq_len = batch.max_seq_len;
+    p.nparts = plan.nparts;
+    p.head_groups = plan.head_groups;
+    p.sc = (float)((double)scale * 1.4426950408889634);
+    const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
+    switch (nq / layer.nkv_heads) {
+    case 1: hipLaunchKernelGGL(q8_attn_partial_kernel<1>, grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(q8_attn_partial_kernel<2>, grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(q8_attn_partial_kernel<4>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(q8_attn_partial_kernel<8>, grid, block, 0, stream, p); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,
+                               const DecodePlan &plan, void *workspace, hipStream_t stream)
+{
+    (void)layer;
+    if (plan.nparts <= 1) return hipSuccess;
+    MergeParams p;
+    char *ws = static_cast<char *>(workspace);
+    p.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan.off_prefix);
+    p.ws_ms = reinterpret_cast<const float2 *>(ws + plan.off_ms);
+    p.ws_acc = reinterpret_cast<const float *>(ws + plan.off_acc);
+    p.out = out;
+    p.batch = batch.batch;
+    p.nq = nq;
+    p.nparts = plan.nparts;
+    hipLaunchKernelGGL(q8_attn_merge_kernel, dim3(batch.batch * nq), dim3(plan.merge_waves * 64), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace q8kv

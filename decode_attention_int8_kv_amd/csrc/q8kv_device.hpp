@@ -1,0 +1,183 @@
+// q8kv_device.hpp -- device routines shared by every kernel of libq8kv (gfx950).
+//
+// The quantizer routines follow two pages (cited by title and section):
+//   "9-2 flash_attn_single_q_q8_neon -- 单 q 单遍扫全 KV" §2 segment 1 (the
+//   query is cut into 32-element blocks, each with its own max-abs scale) and
+//   "9-3 q8 KV 精度对照实验" §2 (one max-abs/127 scale per (token, KV head)
+//   row, codes rounded and clamped to +-127).
+// Every fp32 step of the two quantizers is one IEEE operation (the products
+// use __fmul_rn so that nothing can be fused into them; fp32 division is the
+// correctly rounded default lowering), so codes and scales are reproducible
+// bit for bit by any IEEE implementation of the same steps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8kv {
+
+constexpr int kHeadDim = 128;     // supported head_dim
+constexpr int kQBlock = 32;       // query block length
+constexpr int kTile = 32;         // tokens per decode tile
+constexpr int kSub = 8;           // tokens per wave load (8 lanes x 16 bytes per token row)
+constexpr int kMaxBatch = 4096;
+constexpr int kMaxWavesPerWG = 8; // KV heads handled by one decode workgroup
+constexpr float kInv127 = 1.0f / 127.0f;   // fl(1/127) = 0x3C010204
+constexpr float kGuard = 1e-6f;            // max-abs below this counts as 1
+constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr int32_t kDevBadSeqLen = 0x1;
+constexpr int32_t kDevBadBlockId = 0x2;
+constexpr int32_t kDevBadToken = 0x4;
+
+// ------------------------------------------------------------------ quantizers
+// K/V row: given the row's max-abs a, the stored step d and the reciprocal r.
+struct RowQuant {
+    float step;
+    float recip;
+};
+
+__device__ __forceinline__ RowQuant kv_row_params(float amax)
+{
+    float a = (amax < kGuard) ? 1.0f : amax;
+    RowQuant q;
+    q.step = __fmul_rn(a, kInv127);
+    q.recip = 127.0f / a;   // IEEE division (div_scale / div_fmas / div_fixup)
+    return q;
+}
+
+// code = clamp(roundf(x * r), -127, 127); roundf rounds halves away from zero.
+__device__ __forceinline__ int kv_code(float x, float r)
+{
+    float y = roundf(__fmul_rn(x, r));
+    y = fminf(fmaxf(y, -127.0f), 127.0f);
+    return (int)y;
+}
+
+// Q block: given the block's max-abs m, the block scale and the reciprocal.
+struct BlockQuant {
+    float qscale;
+    float recip;
+};
+
+__device__ __forceinline__ BlockQuant q_block_params(float mabs)
+{
+    float m = (mabs < kGuard) ? 1.0f : mabs;
+    BlockQuant q;
+    q.qscale = __fmul_rn(m, kInv127);
+    q.recip = 127.0f / m;
+    return q;
+}
+
+// code = conversion toward zero of clamp(q * r, -128, 127).
+__device__ __forceinline__ int q_code(float x, float r)
+{
+    float y = __fmul_rn(x, r);
+    y = fminf(fmaxf(y, -128.0f), 127.0f);
+    return (int)y;    // v_cvt_i32_f32 truncates toward zero
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d)
+{
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// ------------------------------------------------------------ lane exchanges
+// DPP controls (within rows of 16 lanes).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i of each 8 reads lane 7-i
+constexpr int kDppRor8 = 0x128;         // lane i of each 16 reads lane (i+8) mod 16
+
+template <int Ctrl>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, Ctrl, 0xF, 0xF, false);
+}
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float xor16_f(float v) { return __shfl_xor(v, 16, 64); }
+__device__ __forceinline__ float xor32_f(float v) { return __shfl_xor(v, 32, 64); }
+
+// Sum / max over the 8 token slots of a wave (lanes that share lane % 8).
+__device__ __forceinline__ float sum_over_slots(float v)
+{
+    v += dpp_f<kDppRor8>(v);
+    v += xor16_f(v);
+    v += xor32_f(v);
+    return v;
+}
+
+__device__ __forceinline__ float max_over_slots(float v)
+{
+    v = fmaxf(v, dpp_f<kDppRor8>(v));
+    v = fmaxf(v, xor16_f(v));
+    v = fmaxf(v, xor32_f(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// ------------------------------------------------------------ int8 dot helpers
+// Sum of 16 int8 x int8 products (one lane's quarter of a 32-block pair).
+__device__ __forceinline__ int dot16_i8(const uint4 &k, const uint4 &q)
+{
+    int acc = 0;
+    acc = __builtin_amdgcn_sdot4((int)k.x, (int)q.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)k.y, (int)q.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)k.z, (int)q.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)k.w, (int)q.w, acc, false);
+    return acc;
+}
+
+// Exact 32-block sum: each block is held by two neighbouring lanes (c, c^1).
+__device__ __forceinline__ int block_partial(const uint4 &k, const uint4 &q)
+{
+    int p = dot16_i8(k, q);
+    return p + dpp_i<kDppQuadXor1>(p);
+}
+
+// int8 byte b of word w, sign-extended, as float (one v_cvt_f32_i32 with SDWA).
+__device__ __forceinline__ float byte_f(uint32_t w, int b)
+{
+    return (float)(int)(int8_t)((w >> (8 * b)) & 0xff);
+}
+
+// ------------------------------------------------------ query quantization
+// Lane (slot, c) of a wave owns elements [16c, 16c+16) of a 128-element query
+// row; the 32-block of those elements is shared with lane c^1.  Quantizes the
+// lane's 16 elements and returns their codes (16 bytes) and the block scale.
+__device__ __forceinline__ void quantize_q_quarter(const float *__restrict__ qrow, int c,
+                                                   uint4 &codes, float &qscale)
+{
+    const float4 *p = reinterpret_cast<const float4 *>(qrow + 16 * c);
+    float4 a = p[0], b = p[1], d = p[2], e = p[3];
+    float x[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, d.x, d.y, d.z, d.w, e.x, e.y, e.z, e.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
+    m = fmaxf(m, dpp_f<kDppQuadXor1>(m));   // max over the whole 32-block
+    BlockQuant bq = q_block_params(m);
+    int cd[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cd[i] = q_code(x[i], bq.recip);
+    codes.x = pack4_i8(cd[0], cd[1], cd[2], cd[3]);
+    codes.y = pack4_i8(cd[4], cd[5], cd[6], cd[7]);
+    codes.z = pack4_i8(cd[8], cd[9], cd[10], cd[11]);
+    codes.w = pack4_i8(cd[12], cd[13], cd[14], cd[15]);
+    qscale = bq.qscale;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace q8kv

@@ -1,0 +1,53 @@
+// q8kv_internal.hpp -- launchers shared between the kernel translation units
+// and the C-ABI layer (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/q8kv.h"
+
+namespace q8kv {
+
+inline int ilog2(int v)
+{
+    int r = 0;
+    while ((1 << (r + 1)) <= v) ++r;
+    return r;
+}
+
+// Resolved launch plan of one decode call.
+struct DecodePlan {
+    int nparts;          // equal ranges of the batch's tile sequence
+    int head_groups;     // workgroups per range (8 KV heads each)
+    int waves;           // waves per decode workgroup
+    int merge_waves;     // waves per merge workgroup
+    size_t off_prefix, off_ms, off_acc, bytes;
+};
+
+DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);
+int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq);
+
+hipError_t launch_append(const q8_kv_layer &layer, const q8_batch &batch, int32_t n_tokens,
+                         const int32_t *tok_seq, const int32_t *tok_pos, const float *k_new,
+                         const float *v_new, int32_t *dev_status, hipStream_t stream);
+
+hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
+                                 const float *q, float scale, float *out, const DecodePlan &plan,
+                                 void *workspace, int32_t *dev_status, hipStream_t stream);
+
+hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,
+                               const DecodePlan &plan, void *workspace, hipStream_t stream);
+
+// Resident workgroups per CU of the decode kernel for this group size.
+int decode_blocks_per_cu(int group, int waves);
+
+hipError_t launch_quantize_q(const float *q, int32_t rows, int8_t *codes, float *qscale,
+                             hipStream_t stream);
+
+hipError_t launch_qk_partials(const q8_kv_layer &layer, const q8_batch &batch, int nq,
+                              const float *q, int32_t *partials, int32_t *dev_status,
+                              hipStream_t stream);
+
+}  // namespace q8kv

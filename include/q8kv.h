@@ -1,0 +1,188 @@
+/*
+ * q8kv.h -- C ABI of the MI355X (gfx950) q8 single-query decode-attention
+ * library (libq8kv.so).
+ *
+ * What it computes (pages cited by title and section):
+ *   - "9-3 q8 KV 精度对照实验" §2: every new (token, KV head) row of K and V is
+ *     quantized on append with one fp32 scale per row (max-abs/127) and int8
+ *     codes (round, clamp to +-127).
+ *   - "9-2 flash_attn_single_q_q8_neon -- 单 q 单遍扫全 KV" §2: decode attention
+ *     for one query per sequence and head, in one pass over that sequence's
+ *     blocked int8 KV: Q quantized once in 32-element blocks (segment 1), int8
+ *     dot products with int32 block sums rescaled by the Q block scale, the K
+ *     row scale and the softmax scale, an online softmax with running max M and
+ *     sum S that rescales the accumulator whenever M rises, V accumulated as
+ *     int8 code times (weight x V row scale) (segment 2), and a single
+ *     division by S at the end (segment 3).
+ *
+ * Data layout (device memory, owned by the caller; one pool per layer):
+ *   k_codes, v_codes : int8  [num_blocks][kv_bs][nkv_heads * head_dim]
+ *   k_scale, v_scale : fp32  [num_blocks][kv_bs][nkv_heads]
+ *     Token t of sequence b lives in physical block block_table[b][t / kv_bs]
+ *     at row t % kv_bs; head kh occupies bytes [kh*head_dim, (kh+1)*head_dim)
+ *     of that row ("9-2" §2 segment 2).  The scale stored for a row is the
+ *     step d = max-abs * fl(1/127); a dequantized value is code * d.
+ *   block_table : int32 [batch][max_blocks_per_seq] (physical block ids)
+ *   seq_lens    : int32 [batch] (tokens visible to attention, including the
+ *                 token appended this step)
+ *   q, out      : fp32  [batch][nq_heads][head_dim]
+ *   Query head h reads KV head h / (nq_heads / nkv_heads).
+ *
+ * Supported shapes: head_dim == 128; kv_bs a power of two in [8, 1024];
+ * nkv_heads in [1, 16]; nq_heads / nkv_heads in {1, 2, 4, 8}; batch in
+ * [1, 4096].  Everything else returns Q8_EUNSUPPORTED.
+ *
+ * Execution: every call only validates its host-visible arguments and
+ * enqueues kernels on `stream` (a hipStream_t; NULL = the null stream).  No
+ * call allocates device memory, synchronizes, or keeps state between calls,
+ * so calls are re-entrant; calls that write the same buffers must be ordered
+ * by the caller.  Inputs must be finite.
+ *
+ * Errors: host-detected errors return before anything is enqueued.  Errors
+ * only the device can see (a sequence length outside [0, max_seq_len], a
+ * block id outside [0, num_blocks), an append position outside its sequence)
+ * OR a Q8_DEV_* bit into *dev_status (if non-NULL; the caller zeroes it and
+ * reads it after synchronizing).  The affected work is skipped: an appended
+ * row is not written; a sequence with a bad length reads as empty (its output
+ * row is zeros); a block with a bad id is left out of the attention.
+ */
+#ifndef Q8KV_H
+#define Q8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8KV_ABI_VERSION 1
+
+typedef enum q8_status {
+    Q8_OK = 0,
+    Q8_EINVAL = -1,        /* NULL or misaligned pointer, negative or inconsistent size */
+    Q8_EUNSUPPORTED = -2,  /* shape outside the supported set listed above */
+    Q8_EWORKSPACE = -3,    /* workspace NULL or smaller than q8_decode_attn_workspace_bytes() */
+    Q8_EHIP = -4           /* a HIP runtime call failed; q8_last_error() holds its text */
+} q8_status;
+
+/* Bits OR-ed into *dev_status by the device. */
+#define Q8_DEV_BAD_SEQ_LEN  0x1  /* seq_lens[b] < 0 or > max_seq_len */
+#define Q8_DEV_BAD_BLOCK_ID 0x2  /* block_table entry outside [0, num_blocks) */
+#define Q8_DEV_BAD_TOKEN    0x4  /* append: tok_seq outside [0, batch) or tok_pos outside [0, seq_lens[seq]) */
+
+/* One layer's physical block pool (pointers to device memory).
+ * Alignment: k_codes and v_codes 16 bytes, k_scale and v_scale 4 bytes. */
+typedef struct q8_kv_layer {
+    int32_t nkv_heads;
+    int32_t head_dim;
+    int32_t kv_bs;
+    int32_t num_blocks;
+    int8_t *k_codes;
+    int8_t *v_codes;
+    float *k_scale;
+    float *v_scale;
+} q8_kv_layer;
+
+/* Per-step batch metadata, shared by all layers.  batch, max_blocks_per_seq
+ * and max_seq_len are host values; the arrays are device memory.
+ * max_seq_len must not exceed max_blocks_per_seq * kv_bs. */
+typedef struct q8_batch {
+    int32_t batch;
+    int32_t max_blocks_per_seq;
+    int32_t max_seq_len;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+} q8_batch;
+
+/* kv_quantize_per_head append ("9-3" §2; stored layout "9-2" §2 segment 2).
+ * For each of n_tokens new tokens j and each KV head kh, quantizes the row
+ * k_new[j][kh][0:head_dim] (and likewise v_new): a = max |x| (a := 1 when
+ * a < 1e-6), d = a * fl(1/127), r = 127 / a (IEEE fp32 division),
+ * code = clamp(roundf(x * r), -127, 127) with roundf rounding halves away
+ * from zero; writes the codes and d at sequence tok_seq[j], position
+ * tok_pos[j] of the cache.  tok_seq, tok_pos: device int32 [n_tokens];
+ * k_new, v_new: device fp32 [n_tokens][nkv_heads][head_dim], 16-byte
+ * aligned.  n_tokens == 0 is a no-op.  Positions must lie inside
+ * [0, seq_lens[seq]); a decode step appends tok_pos = seq_lens - 1 and then
+ * calls q8_decode_attn.  Two tokens with the same (seq, pos) race. */
+q8_status q8_kv_append(const q8_kv_layer *layer, const q8_batch *batch,
+                       int32_t n_tokens, const int32_t *tok_seq, const int32_t *tok_pos,
+                       const float *k_new, const float *v_new,
+                       int32_t *dev_status, void *stream);
+
+/* Number of work partitions q8_decode_attn uses when asked for nparts = 0:
+ * one per workgroup slot resident on the current device, capped at the
+ * batch's largest possible tile count (tiles are 32 tokens). */
+int32_t q8_decode_attn_auto_parts(const q8_kv_layer *layer, const q8_batch *batch,
+                                  int32_t nq_heads);
+
+/* Device workspace q8_decode_attn needs for this shape and partition count
+ * (nparts = 0: the automatic count above).  Returns 0 on invalid arguments. */
+size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *batch,
+                                      int32_t nq_heads, int32_t nparts);
+
+/* Decode attention ("9-2" §2, all three segments) for every sequence b and
+ * query head h of the batch:
+ *   out[b][h] = sum_t softmax_t(s) * vhat_t,  s_t = scale * <qhat, khat_t>,
+ * over t < seq_lens[b], where qhat, khat, vhat are the dequantized query
+ * (32-blocks, see q8_quantize_q) and cache rows, computed in one pass with an
+ * online softmax.  `scale` is the caller's softmax scale (1/sqrt(head_dim) in
+ * the pages).  The batch's total tile count is cut into `nparts` equal
+ * contiguous ranges (nparts = 0: automatic), one workgroup each; a sequence
+ * cut across ranges is finished by a merge of the partial (M, S, acc) states
+ * with the same rescale rule ("9-2" §2 segment 2 applied to whole partial
+ * states).  A sequence of length 0 gives a zero row.  Results are
+ * deterministic for a given nparts.  workspace: device memory of at least
+ * q8_decode_attn_workspace_bytes(..., nparts) bytes, 256-byte aligned, no
+ * initialization needed; it must not be shared by calls that may overlap. */
+q8_status q8_decode_attn(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                         const float *q, float scale, float *out, int32_t nparts,
+                         void *workspace, size_t workspace_bytes,
+                         int32_t *dev_status, void *stream);
+
+/* The two kernels q8_decode_attn enqueues, exposed so a caller can time them
+ * or interleave other work; calling _partial then _merge with identical
+ * arguments is exactly q8_decode_attn.  _merge is a no-op when the resolved
+ * nparts is 1. */
+q8_status q8_decode_attn_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                 const float *q, float scale, float *out, int32_t nparts,
+                                 void *workspace, size_t workspace_bytes,
+                                 int32_t *dev_status, void *stream);
+q8_status q8_decode_attn_merge(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                               const float *q, float scale, float *out, int32_t nparts,
+                               void *workspace, size_t workspace_bytes,
+                               int32_t *dev_status, void *stream);
+
+/* Test hook: the Q quantizer of the decode kernel ("9-2" §2 segment 1) on
+ * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1
+ * when m < 1e-6), qscale = m * fl(1/127), r = 127 / m,
+ * code = (int8) truncation toward zero of clamp(q * r, -128, 127).
+ * q: device fp32 [rows][head_dim] (16-byte aligned); codes: device int8
+ * [rows][head_dim]; qscale: device fp32 [rows][head_dim / 32].
+ * Runs the same device routine as q8_decode_attn. */
+q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim,
+                        int8_t *codes, float *qscale, void *stream);
+
+/* Test hook: the exact int32 block sums the decode kernel forms ("9-2" §2
+ * segment 2), P[b][h][t][blk] = sum over i in block blk of qcode[i] *
+ * kcode_t[i], for every sequence b, query head h and t < seq_lens[b];
+ * entries with seq_lens[b] <= t < max_seq_len are written as 0.
+ * partials: device int32 [batch][nq_heads][max_seq_len][head_dim / 32].
+ * Runs the same device routines as q8_decode_attn. */
+q8_status q8_qk_block_partials(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                               const float *q, int32_t *partials,
+                               int32_t *dev_status, void *stream);
+
+/* Short English name of a status code (static string). */
+const char *q8_status_string(int32_t status);
+/* Text of the last Q8_EHIP error on the calling thread ("" if none). */
+const char *q8_last_error(void);
+/* Q8KV_ABI_VERSION of the loaded library. */
+int32_t q8_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8KV_H */

@@ -1,0 +1,140 @@
+"""Helpers for the GPU tests: put seeded inputs through the library's C ABI
+and read results back.  Inputs come from ``workloads``; expected values come
+only from ``oracle``."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+TOL_REL = 2e-5
+TOL_ABS = 1e-6
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def q8():
+    import decode_attention_int8_kv_amd as m
+    m.lib()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+class DeviceCache:
+    """One layer on the GPU plus its batch metadata."""
+
+    def __init__(self, lens, nkv, kv_bs, seed, spare=2, device="cuda", garbage=True):
+        t = torch()
+        m = q8()
+        self.lens = np.asarray(lens, np.int32)
+        self.nkv, self.kv_bs = nkv, kv_bs
+        self.table, self.num_blocks = workloads.block_table(self.lens, kv_bs, seed, spare_blocks=spare)
+        self.layer = m.alloc_layer(self.num_blocks, kv_bs, nkv, device)
+        if garbage:
+            # rows no token occupies hold junk codes and NaN scales: masking must ignore them
+            g = t.Generator(device=device)
+            g.manual_seed(seed)
+            self.layer.k_codes.copy_(t.randint(-128, 128, self.layer.k_codes.shape, generator=g, device=device,
+                                               dtype=t.int8))
+            self.layer.v_codes.copy_(t.randint(-128, 128, self.layer.v_codes.shape, generator=g, device=device,
+                                               dtype=t.int8))
+            self.layer.k_scale.fill_(float("nan"))
+            self.layer.v_scale.fill_(float("nan"))
+        self.table_t = t.from_numpy(self.table).to(device)
+        self.lens_t = t.from_numpy(self.lens).to(device)
+        self.max_seq_len = int(max(1, self.lens.max()))
+        self.batch = m.make_batch(self.table_t, self.lens_t, self.max_seq_len)
+        self.status = t.zeros(1, dtype=t.int32, device=device)
+
+    def append_dense(self, k, v, t0=0):
+        """Append tokens [t0, len_b) of every sequence from dense fp32 host
+        arrays k, v [batch, >= len, nkv, hd] through q8_kv_append."""
+        t = torch()
+        seqs, poss, ks, vs = [], [], [], []
+        for b, n in enumerate(self.lens):
+            if n <= t0:
+                continue
+            seqs.append(np.full(n - t0, b, np.int32))
+            poss.append(np.arange(t0, n, dtype=np.int32))
+            ks.append(k[b, t0:n])
+            vs.append(v[b, t0:n])
+        if not seqs:
+            return
+        dev = self.layer.k_codes.device
+        q8().kv_append(self.layer, self.batch,
+                       t.from_numpy(np.concatenate(seqs)).to(dev), t.from_numpy(np.concatenate(poss)).to(dev),
+                       t.from_numpy(np.ascontiguousarray(np.concatenate(ks), np.float32)).to(dev),
+                       t.from_numpy(np.ascontiguousarray(np.concatenate(vs), np.float32)).to(dev),
+                       dev_status=self.status)
+
+    def host(self):
+        """The cache as an oracle.Cache (codes and steps copied back)."""
+        L = self.layer
+        return oracle.Cache(L.k_codes.cpu().numpy(), L.v_codes.cpu().numpy(), L.k_scale.cpu().numpy(),
+                            L.v_scale.cpu().numpy(), self.table, self.lens, self.nkv, 128)
+
+    def decode(self, q, nq, scale, nparts=0, out=None):
+        t = torch()
+        m = q8()
+        dev = self.layer.k_codes.device
+        qd = q if isinstance(q, t.Tensor) else t.from_numpy(np.ascontiguousarray(q, np.float32)).to(dev)
+        if out is None:
+            out = t.full((self.batch.batch, nq, 128), float("nan"), dtype=t.float32, device=dev)
+        nbytes = m.decode_attn_workspace_bytes(self.layer, self.batch, nq, nparts)
+        ws = t.empty(nbytes, dtype=t.uint8, device=dev)
+        m.decode_attn(self.layer, self.batch, nq, qd, scale, out, ws, nparts=nparts, dev_status=self.status)
+        return out
+
+    def status_word(self):
+        torch().cuda.synchronize()
+        return int(self.status.item())
+
+
+def dense_kv(lens, nkv, seed, dist="normal", hd=128):
+    rng = np.random.default_rng([seed, 77])
+    max_len = int(max(1, np.max(lens)))
+    shape = (len(lens), max_len, nkv, hd)
+    if dist == "normal":
+        return (rng.standard_normal(shape, dtype=np.float32), rng.standard_normal(shape, dtype=np.float32))
+    w = workloads.Workload("t", nkv, nkv, len(lens), 1, ("fixed", max_len), "student3x3", seed)
+    k, v = workloads.kv_host(w, np.asarray(lens, np.int32))
+    return k, v
+
+
+def expected_codes(dc: DeviceCache, k, v):
+    """Oracle codes/steps of every appended token, gathered at its cache slot."""
+    rows_k, rows_v, steps_k, steps_v, slots = [], [], [], [], []
+    for b, n in enumerate(dc.lens):
+        if n == 0:
+            continue
+        ck, dk = oracle.quantize_kv(k[b, :n])
+        cv, dv = oracle.quantize_kv(v[b, :n])
+        t = np.arange(n)
+        slots.append(dc.table[b, t // dc.kv_bs] * dc.kv_bs + t % dc.kv_bs)
+        rows_k.append(ck), rows_v.append(cv), steps_k.append(dk), steps_v.append(dv)
+    return (np.concatenate(slots), np.concatenate(rows_k), np.concatenate(rows_v),
+            np.concatenate(steps_k), np.concatenate(steps_v))
+
+
+def row_errors(got, want):
+    """Per (b, h) row: max |got - want| and the allowed tolerance."""
+    got = np.asarray(got, np.float64).reshape(-1, 128)
+    want = np.asarray(want, np.float64).reshape(-1, 128)
+    err = np.abs(got - want).max(1)
+    tol = TOL_REL * np.abs(want).max(1) + TOL_ABS
+    return err, tol
+
+
+def assert_rows_close(got, want, what=""):
+    err, tol = row_errors(got, want)
+    bad = np.nonzero(~(err <= tol))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} rows out of tolerance; worst row {bad[np.argmax(err[bad] / tol[bad])]} "
+                           f"err {err[bad].max():.3e} tol {tol[bad].min():.3e}")
+    return float((err / tol).max()) if err.size else 0.0

@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+function include/q8kv.h declares, and rejects bad arguments on the host
+before anything is enqueued.  No test here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8kv.h")
+
+
+@pytest.fixture(scope="module")
+def q8():
+    import decode_attention_int8_kv_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from decode_attention_int8_kv_amd import build
+        build.build()
+    m._load()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("q8_kv_append", "q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge",
+                 "q8_decode_attn_workspace_bytes", "q8_decode_attn_auto_parts", "q8_quantize_q",
+                 "q8_qk_block_partials", "q8_status_string", "q8_last_error", "q8_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(q8):
+    lib = ctypes.CDLL(q8.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(q8):
+    assert q8.abi_version() == 1
+    assert q8.status_string(0) == "ok"
+    assert q8.status_string(-3).startswith("workspace")
+    assert q8.last_error() == ""
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def layer(q8, **kw):
+    d = dict(k_codes=FAKE, v_codes=FAKE, k_scale=FAKE, v_scale=FAKE, nkv_heads=8, kv_bs=32, num_blocks=100)
+    d.update(kw)
+    return q8.KVLayer(**d)
+
+
+def batch(q8, **kw):
+    d = dict(block_table=FAKE, seq_lens=FAKE, batch=4, max_blocks_per_seq=10, max_seq_len=300)
+    d.update(kw)
+    return q8.Batch(**d)
+
+
+def call_append(q8, L, B, n=1, **ptrs):
+    p = dict(tok_seq=FAKE, tok_pos=FAKE, k_new=FAKE, v_new=FAKE)
+    p.update(ptrs)
+    return q8.lib().q8_kv_append(ctypes.byref(L.c()), ctypes.byref(B.c()), n, p["tok_seq"], p["tok_pos"],
+                                 p["k_new"], p["v_new"], None, None)
+
+
+def call_decode(q8, L, B, nq=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, nparts=4):
+    return q8.lib().q8_decode_attn(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, q, 0.088, out, nparts,
+                                   ws, ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), -2), (dict(kv_bs=24), -2), (dict(kv_bs=4), -2), (dict(kv_bs=2048), -2),
+    (dict(nkv_heads=0), -2), (dict(nkv_heads=17), -2), (dict(num_blocks=0), -1),
+    (dict(k_codes=0), -1), (dict(v_codes=FAKE + 8), -1), (dict(k_scale=FAKE + 2), -1),
+])
+def test_layer_validation(q8, kw, status):
+    assert call_append(q8, layer(q8, **kw), batch(q8)) == status
+    assert call_decode(q8, layer(q8, **kw), batch(q8)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -1), (dict(batch=5000), -2), (dict(max_blocks_per_seq=0), -1),
+    (dict(max_seq_len=-1), -1), (dict(max_seq_len=321), -1), (dict(block_table=0), -1),
+    (dict(seq_lens=FAKE + 1), -1),
+])
+def test_batch_validation(q8, kw, status):
+    assert call_append(q8, layer(q8), batch(q8, **kw)) == status
+    assert call_decode(q8, layer(q8), batch(q8, **kw)) == status
+
+
+def test_append_argument_validation(q8):
+    L, B = layer(q8), batch(q8)
+    assert call_append(q8, L, B, n=0) == 0            # no-op, nothing enqueued
+    assert call_append(q8, L, B, n=-1) == -1
+    assert call_append(q8, L, B, tok_seq=0) == -1
+    assert call_append(q8, L, B, k_new=FAKE + 4) == -1  # 16-byte alignment
+
+
+def test_decode_argument_validation(q8):
+    L, B = layer(q8), batch(q8)
+    assert call_decode(q8, L, B, nq=12) == -1           # nq % nkv != 0
+    assert call_decode(q8, L, B, nq=24) == -2           # group 3
+    assert call_decode(q8, L, B, nq=128) == -2          # group 16
+    assert call_decode(q8, L, B, q=0) == -1
+    assert call_decode(q8, L, B, out=FAKE + 4) == -1
+    assert call_decode(q8, L, B, nparts=-1) == -1
+    assert call_decode(q8, L, B, ws=0) == -3
+    assert call_decode(q8, L, B, ws=FAKE + 64) == -3    # 256-byte alignment
+    need = q8.decode_attn_workspace_bytes(L, B, 16, 4)
+    assert need > 0
+    assert call_decode(q8, L, B, ws_bytes=need - 1) == -3
+
+
+def test_workspace_size_grows_with_parts_and_heads(q8):
+    L, B = layer(q8), batch(q8)
+    a = q8.decode_attn_workspace_bytes(L, B, 16, 4)
+    b = q8.decode_attn_workspace_bytes(L, B, 16, 8)
+    c = q8.decode_attn_workspace_bytes(L, B, 32, 8)
+    assert 0 < a < b < c
+    # every range can leave two cut pieces of (M, S, acc[128]) per query head
+    assert b - a >= 4 * 2 * 16 * (128 + 2) * 4
+    assert q8.decode_attn_workspace_bytes(L, B, 12, 4) == 0
+
+
+def test_hook_validation(q8):
+    lib = q8.lib()
+    assert lib.q8_quantize_q(FAKE, 4, 64, FAKE, FAKE, None) == -2
+    assert lib.q8_quantize_q(FAKE, -1, 128, FAKE, FAKE, None) == -1
+    assert lib.q8_quantize_q(FAKE, 0, 128, FAKE, FAKE, None) == 0
+    assert lib.q8_quantize_q(FAKE + 4, 1, 128, FAKE, FAKE, None) == -1
+    L, B = layer(q8), batch(q8)
+    assert lib.q8_qk_block_partials(ctypes.byref(L.c()), ctypes.byref(B.c()), 12, FAKE, FAKE, None, None) == -1
+    assert lib.q8_qk_block_partials(ctypes.byref(L.c()), ctypes.byref(B.c()), 16, FAKE, 0, None, None) == -1
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    import decode_attention_int8_kv_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        m.lib()
