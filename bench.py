@@ -1,0 +1,251 @@
+"""Benchmark: q8 decode-attention decode steps on one MI355X.
+
+One step = for every layer of the workload: append one new token per sequence
+through q8_kv_append, then q8_decode_attn over every sequence's whole history
+(partial kernel + merge kernel).  Inputs (cache history, the step's q and new
+K/V, block tables) are resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0): achieved algorithmic HBM GB/s of the whole step
+as `value`, plus a `roofline` object for the dominant kernel (the decode
+partial kernel, timed with HIP events on its own stream) and a `cpu_baseline`
+object (the CPU oracle on one layer-step of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+POOL_TOKENS = 65536            # N(0,1) source rows the history is appended from
+FILL_CHUNK = 32768
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen2b_b64_ragged", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int):
+    """Bytes one layer-step must move at least once.
+    attention: K and V codes and scales of every visible token, read once per
+    KV head (n * nkv * (2*128 + 8)); q in and out (B*nq*128*4*2); block-table
+    entries and lengths.  append: fp32 K and V in (T*nkv*128*4*2), codes and
+    scales out (T*nkv*(2*128 + 8)), token indices (T*8)."""
+    n = lens.astype(np.int64)
+    kv = int(n.sum()) * w.nkv * (2 * w.head_dim + 8)
+    qo = w.batch * w.nq * w.head_dim * 4 * 2
+    meta = int(((n + kv_bs - 1) // kv_bs).sum()) * 4 + w.batch * 4
+    t = w.batch * w.append_per_step
+    app = t * w.nkv * w.head_dim * 4 * 2 + t * w.nkv * (2 * w.head_dim + 8) + t * 8
+    return kv + qo + meta, app
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each GPU would run the same kernels on its own share of sequences or KV heads). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_attention_int8_kv_amd as q8
+
+    q8.lib()   # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    layers = args.layers or w.layers
+    lens = workloads.seq_lens(w)
+    kv_bs = w.kv_bs
+    B, nq, nkv, hd = w.batch, w.nq, w.nkv, w.head_dim
+    scale = float(workloads.softmax_scale(hd))
+    t_setup = time.perf_counter()
+
+    # ---- cache: one pool per layer, blocks of every sequence scattered at random
+    table, nblocks = workloads.block_table(lens, kv_bs, w.seed)
+    table_t = torch.from_numpy(table).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    batch = q8.make_batch(table_t, lens_t, int(lens.max()))
+    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev) for _ in range(layers)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # history: every position but the last, appended from an N(0,1) source pool
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    src_k = torch.randn((POOL_TOKENS + FILL_CHUNK, nkv, hd), generator=gen, device=dev)
+    src_v = torch.randn((POOL_TOKENS + FILL_CHUNK, nkv, hd), generator=gen, device=dev)
+    hist_seq = np.concatenate([np.full(max(n - 1, 0), b, np.int32) for b, n in enumerate(lens)])
+    hist_pos = np.concatenate([np.arange(max(n - 1, 0), dtype=np.int32) for n in lens])
+    hist_seq_t = torch.from_numpy(hist_seq).to(dev)
+    hist_pos_t = torch.from_numpy(hist_pos).to(dev)
+    rng = np.random.default_rng(w.seed)
+    for li, pool in enumerate(pools):
+        for c0 in range(0, hist_seq.size, FILL_CHUNK):
+            c1 = min(hist_seq.size, c0 + FILL_CHUNK)
+            off = int(rng.integers(0, POOL_TOKENS))
+            q8.kv_append(pool, batch, hist_seq_t[c0:c1], hist_pos_t[c0:c1],
+                         src_k[off:off + c1 - c0], src_v[off:off + c1 - c0], dev_status=status)
+    del src_k, src_v
+
+    # the step's inputs: one new token per sequence (position n_b - 1) and q, per layer
+    step_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    step_pos = (lens_t - 1).clamp(min=0).to(torch.int32)
+    new_k = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
+    new_v = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
+    qs = torch.randn((layers, B, nq, hd), generator=gen, device=dev)
+    outs = torch.empty((layers, B, nq, hd), dtype=torch.float32, device=dev)
+    nparts = args.nparts or q8.decode_attn_auto_parts(pools[0], batch, nq)
+    ws = torch.empty(q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set during fill"
+    setup_s = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    n_ev = (args.warmup + args.steps) * layers
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+
+    def step(s):
+        for li in range(layers):
+            e = ev[s * layers + li]
+            e[0].record(stream)
+            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+            e[1].record(stream)
+            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                   dev_status=status)
+            e[2].record(stream)
+            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                 dev_status=status)
+            e[3].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0, "device status set during timing"
+
+    timed = [ev[s * layers + li] for s in range(args.warmup, args.warmup + args.steps) for li in range(layers)]
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e3     # us
+    t_partial = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e3
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e3
+    t_layer = np.array([e[0].elapsed_time(e[3]) for e in timed]) * 1e3
+    step_us = np.array([ev[s * layers][0].elapsed_time(ev[s * layers + layers - 1][3])
+                        for s in range(args.warmup, args.warmup + args.steps)]) * 1e3
+
+    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs)
+    step_bytes = layers * (attn_b + app_b)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the decode partial kernel; its algorithmic bytes are the
+    # attention bytes (the merge traffic is overhead and not counted)
+    part_us = float(t_partial.mean())
+    achieved = attn_b / (part_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f).get(args.workload)
+        if tr and tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "q8_attn_partial_kernel", "kernel_us": round(part_us, 2),
+                "algorithmic_bytes_per_launch": int(attn_b)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, lens, table, nblocks, attn_b)
+
+    line = {
+        "metric": "q8 decode-attn achieved HBM GB/s (% of peak) + us/layer-step, batch x ctx sweep",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8/fp32", "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
+            "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": nparts,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "us_per_layer_step": round(float(np.median(t_layer)), 2),
+            "us_per_layer_step_p10_p90": [round(float(np.percentile(t_layer, 10)), 2),
+                                          round(float(np.percentile(t_layer, 90)), 2)],
+            "us_append": round(float(np.median(t_append)), 2),
+            "us_decode_partial": round(float(np.median(t_partial)), 2),
+            "us_decode_merge": round(float(np.median(t_merge)), 2),
+            "us_per_step_events": round(float(np.median(step_us)), 1),
+            "bytes_per_layer_step": int(attn_b + app_b), "setup_s": round(setup_s, 1),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def kernel_hash() -> str:
+    """Hash of the kernel sources: counter figures taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_int8_kv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, lens, table, nblocks, attn_bytes):
+    """The CPU oracle, as it stands, on a bounded sample of one layer-step of
+    the workload: the first sequences up to ~96K tokens, every query head.
+    Their K/V are N(0,1) rows drawn on the host and quantized by the oracle's
+    own quantizer.  The oracle decode is repeated until ~10 s have passed;
+    returns GB/s of the same algorithmic attention bytes."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    keep = np.cumsum(lens) <= 98304
+    keep[0] = True
+    sl = lens[keep]
+    sub = workloads.Workload(w.name, w.nq, w.nkv, int(keep.sum()), 1, ("fixed", int(sl.max())), w.dist, w.seed)
+    t0 = time.perf_counter()
+    k, v = workloads.kv_host(sub, sl)
+    tab, nb = workloads.block_table(sl, w.kv_bs, w.seed)
+    cache = oracle.build_cache(k, v, sl, tab, nb, w.kv_bs)
+    del k, v
+    q = workloads.query(sub)
+    print(f"[cpu_baseline] sample ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attn(cache, q, w.nq, float(workloads.softmax_scale(w.head_dim)), nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 200:
+            break
+    n = sl.astype(np.int64)
+    b = int(n.sum()) * w.nkv * (2 * w.head_dim + 8) + sub.batch * w.nq * w.head_dim * 8
+    return {"value": round(b * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sub.batch} of {w.batch} sequences ({int(n.sum())} tokens, all {w.nq} query heads) "
+                      f"of one layer-step, oracle decode_attn repeated {reps}x in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
