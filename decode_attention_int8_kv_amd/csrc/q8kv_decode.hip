@@ -93,7 +93,7 @@ __device__ void build_prefix(const DecodeParams &p, int *pref, bool report)
 
 // One wave: attention of the G query heads of KV head kh over tiles
 // [lt0, lt1) of sequence b (length n).
-template <int G>
+template <int G, bool Big>
 __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
                                              int lt0, int lt1, int n, bool whole, int part,
                                              int slot)
@@ -117,13 +117,20 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     }
 
     const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
+    const int log2bs = p.cache.kv_bs_log2;
+    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
 
     auto process = [&](const Tile &t) {
+        float ks[4], vs[4];
+        tile_scales<0>(t, c, ks[0], vs[0]);
+        tile_scales<1>(t, c, ks[1], vs[1]);
+        tile_scales<2>(t, c, ks[2], vs[2]);
+        tile_scales<3>(t, c, ks[3], vs[3]);
         float s[4][G];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const bool ok = (t.valid >> kk) & 1u;
-            const float f = t.ks[kk] * p.sc;
+            const float f = ks[kk] * p.sc;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 // exact int32 block sum, then x Q block scale, summed over the 4 blocks
@@ -156,7 +163,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
                 // masked tokens contribute nothing (their scale may be any bit pattern)
                 const float pw = ok ? __builtin_amdgcn_exp2f(s[kk][g] - M[g]) : 0.0f;
                 S[g] += pw;
-                w[g] = ok ? pw * t.vs[kk] : 0.0f;
+                w[g] = ok ? pw * vs[kk] : 0.0f;
             }
             const uint32_t words[4] = {t.v[kk].x, t.v[kk].y, t.v[kk].z, t.v[kk].w};
 #pragma unroll
@@ -169,15 +176,23 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     };
 
     // Two register tiles: the next tile's loads are in flight while the
-    // current one is processed.
+    // current one is processed; block ids run one more tile ahead.  Tokens
+    // past the piece count as past the end, so the one tile loaded beyond the
+    // piece costs no HBM traffic.
+    const int ne = min(n, lt1 * kTile);
     Tile ta, tb;
+    TileBlocks ba, bb;
     int lt = lt0;
-    load_tile<true>(p.cache, bt, kh, lane, lt * kTile, n, p.dev_status, ta);
+    fetch_blocks(bt, log2bs, lt * kTile, ne, ba);
+    load_tile<true, Big>(p.cache, ba, lo, lane, lt * kTile, ne, p.dev_status, ta);
+    fetch_blocks(bt, log2bs, (lt + 1) * kTile, ne, bb);
     while (true) {
-        if (lt + 1 < lt1) load_tile<true>(p.cache, bt, kh, lane, (lt + 1) * kTile, n, p.dev_status, tb);
+        load_tile<true, Big>(p.cache, bb, lo, lane, (lt + 1) * kTile, ne, p.dev_status, tb);
+        fetch_blocks(bt, log2bs, (lt + 2) * kTile, ne, ba);
         process(ta);
         if (++lt >= lt1) break;
-        if (lt + 1 < lt1) load_tile<true>(p.cache, bt, kh, lane, (lt + 1) * kTile, n, p.dev_status, ta);
+        load_tile<true, Big>(p.cache, ba, lo, lane, (lt + 1) * kTile, ne, p.dev_status, ta);
+        fetch_blocks(bt, log2bs, (lt + 2) * kTile, ne, bb);
         process(tb);
         if (++lt >= lt1) break;
     }
@@ -218,7 +233,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     }
 }
 
-template <int G>
+template <int G, bool Big>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
     __shared__ int pref[kMaxBatch + 1];
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
             const int slot = (x == start) ? 0 : 1;
             int n = p.seq_lens[b];
             n = uniform(n);
-            attend_piece<G>(p, b, kh, lane, x - a0, x1 - a0, n, whole, part, slot);
+            attend_piece<G, Big>(p, b, kh, lane, x - a0, x1 - a0, n, whole, part, slot);
             x = x1;
         }
     }
@@ -350,17 +365,24 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
 // ----------------------------------------------------------------- host ----
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+template <int G, bool Big>
+static const void *partial_fn() { return reinterpret_cast<const void *>(&q8_attn_partial_kernel<G, Big>); }
+
+static const void *partial_kernel(int group, bool big)
+{
+    switch (group) {
+    case 1: return big ? partial_fn<1, true>() : partial_fn<1, false>();
+    case 2: return big ? partial_fn<2, true>() : partial_fn<2, false>();
+    case 4: return big ? partial_fn<4, true>() : partial_fn<4, false>();
+    default: return big ? partial_fn<8, true>() : partial_fn<8, false>();
+    }
+}
+
 int decode_blocks_per_cu(int group, int waves)
 {
     int nb = 0;
-    const void *fn = nullptr;
-    switch (group) {
-    case 1: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<1>); break;
-    case 2: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<4>); break;
-    default: fn = reinterpret_cast<const void *>(&q8_attn_partial_kernel<8>); break;
-    }
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, waves * 64, 0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, true), waves * 64, 0) !=
+            hipSuccess || nb < 1)
         nb = 1;
     return nb;
 }
@@ -429,13 +451,10 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     p.head_groups = plan.head_groups;
     p.sc = (float)((double)scale * 1.4426950408889634);
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
-    switch (nq / layer.nkv_heads) {
-    case 1: hipLaunchKernelGGL(q8_attn_partial_kernel<1>, grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(q8_attn_partial_kernel<2>, grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(q8_attn_partial_kernel<4>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(q8_attn_partial_kernel<8>, grid, block, 0, stream, p); break;
-    }
-    return hipGetLastError();
+    const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile);
+    void *args[] = {&p};
+    const hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,

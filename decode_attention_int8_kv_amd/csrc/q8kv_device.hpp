@@ -102,24 +102,43 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float xor16_f(float v) { return __shfl_xor(v, 16, 64); }
-__device__ __forceinline__ float xor32_f(float v) { return __shfl_xor(v, 32, 64); }
+// Across rows: v_permlane16_swap / v_permlane32_swap (VALU, no LDS round
+// trip).  Swapping a register with itself leaves, in every lane, its own
+// value and the value of the lane 16 (32) away, one in each result; the
+// reductions below combine the two symmetrically, so every lane gets the
+// same bits.
+__device__ __forceinline__ float sum_rows16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_rows32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_rows16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_rows32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Sum / max over the 8 token slots of a wave (lanes that share lane % 8).
 __device__ __forceinline__ float sum_over_slots(float v)
 {
     v += dpp_f<kDppRor8>(v);
-    v += xor16_f(v);
-    v += xor32_f(v);
-    return v;
+    return sum_rows32(sum_rows16(v));
 }
 
 __device__ __forceinline__ float max_over_slots(float v)
 {
     v = fmaxf(v, dpp_f<kDppRor8>(v));
-    v = fmaxf(v, xor16_f(v));
-    v = fmaxf(v, xor32_f(v));
-    return v;
+    return max_rows32(max_rows16(v));
 }
 
 __device__ __forceinline__ float wave_max(float v)

@@ -62,9 +62,11 @@ __global__ __launch_bounds__(64) void q8_qk_partials_kernel(PartialsParams p)
         n = 0;
     }
     n = uniform(n);
+    TileBlocks tb;
+    fetch_blocks(p.block_table + (size_t)b * p.max_blocks_per_seq, p.cache.kv_bs_log2, t0, n, tb);
     Tile t;
-    load_tile<false>(p.cache, p.block_table + (size_t)b * p.max_blocks_per_seq, kh, lane, t0, n,
-                     p.dev_status, t);
+    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
+    load_tile<false, false>(p.cache, tb, lo, lane, t0, n, p.dev_status, t);
     for (int g = 0; g < p.group; ++g) {
         const int h = kh * p.group + g;
         uint4 qc;

@@ -9,6 +9,12 @@
 // Lane (slot, c) = (lane / 8, lane % 8) loads bytes [16c, 16c + 16) of the
 // head's row for token t0 + 8 k + slot, k = 0..3: eight lanes cover one
 // 128-byte row, so every 16-byte load is part of a fully used 128-byte line.
+//
+// No K/V load of the tile walk waits on another vector load: the block ids
+// come from scalar loads issued a tile ahead, and each lane loads one scale
+// per tile -- lane (slot, c) the K (c < 4) or V (c >= 4) scale of token
+// t0 + 8 (c % 4) + slot -- which DPP moves then hand to the lanes that need
+// them.
 #pragma once
 
 #include "q8kv_device.hpp"
@@ -25,58 +31,153 @@ struct CacheView {
     int32_t num_blocks;
 };
 
+using const_i32 = const __attribute__((address_space(4))) int32_t;
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return 0 without touching memory (raw buffer, stride 0).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+constexpr int kOutOfRange = 0x7ffffff0;   // a lane offset past any resource
+
 struct Tile {
     uint4 k[4];
     uint4 v[4];
-    float ks[4];
-    float vs[4];
-    uint32_t valid;   // bit k: this lane's token of sub-tile k is inside the sequence
+    float sc;         // this lane's scale: K (c < 4) or V (c >= 4) of token t0 + 8 (c % 4) + slot
+    uint32_t valid;   // bit k: token t0 + 8 k + slot is inside the sequence (and its block id is good)
 };
 
-// Loads tile [t0, t0 + 32) of one sequence (length n) for KV head kh.  Sub-
-// tiles that start at or past n are not touched (their block may not exist).
-// Rows past n inside a loaded sub-tile are read (they lie inside a real block)
-// and masked by `valid`.  A block id outside [0, num_blocks) is reported in
-// *status and its sub-tile is masked.
-template <bool WithV>
-__device__ __forceinline__ void load_tile(const CacheView &cv, const int32_t *__restrict__ bt,
-                                          int kh, int lane, int t0, int n, int32_t *status,
-                                          Tile &t)
+// Physical block ids of the 4 sub-tiles of tile [t0, t0 + 32), read with
+// scalar loads (the table is read-only for the kernel's lifetime; scalar
+// loads are counted apart from the vector loads, so waiting for them never
+// drains the K/V loads in flight).  Sub-tiles at or past n get -1.
+struct TileBlocks {
+    int id[4];
+};
+
+__device__ __forceinline__ void fetch_blocks(const int32_t *bt, int log2bs, int t0, int n, TileBlocks &b)
+{
+    const_i32 *sbt = (const_i32 *)bt;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int tk = t0 + kSub * kk;
+        b.id[kk] = (tk < n) ? sbt[tk >> log2bs] : -1;
+    }
+}
+
+// Per-lane constants of the tile walk (loop invariant).
+struct LaneOffsets {
+    int code;     // byte offset of this lane's 16 bytes inside an 8-row sub-tile
+    int scale_k;  // byte offset of this lane's K scale inside a 32-row tile, or out of range
+    int scale_v;  // same for V
+    int scale_sub;// byte offset of this lane's scale inside an 8-row sub-tile
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh, int lane)
+{
+    const int slot = lane >> 3, c = lane & 7;
+    const int row_bytes = cv.nkv * kHeadDim;
+    LaneOffsets o;
+    o.code = slot * row_bytes + kh * kHeadDim + 16 * c;
+    const int in_tile = ((kSub * (c & 3) + slot) * cv.nkv + kh) * 4;
+    o.scale_k = (c < 4) ? in_tile : kOutOfRange;
+    o.scale_v = (c < 4) ? kOutOfRange : in_tile;
+    o.scale_sub = (slot * cv.nkv + kh) * 4;
+    return o;
+}
+
+// Loads tile [t0, t0 + 32) of one sequence for KV head kh, given its block
+// ids; tokens at or past n are masked by `valid`.  Every call issues the
+// same number of loads whatever the tile holds, so the compiler waits for
+// exactly the loads a tile needs and leaves the next tile's in flight: a
+// sub-tile that starts at or past n, or whose block id is outside
+// [0, num_blocks) (reported in *status), gets an empty buffer resource and
+// reads zeros without touching memory.  Rows past n inside a real sub-tile
+// are read (they lie inside a real block) and masked.
+//
+// BigBlocks (kv_bs >= 32): a tile lies inside one block, so one resource per
+// array covers it (sub-tiles are 8-row steps of the SGPR offset) and the
+// scales come in two loads.  Otherwise every sub-tile has its own resources.
+template <bool WithV, bool BigBlocks>
+__device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks &tb, const LaneOffsets &lo,
+                                          int lane, int t0, int n, int32_t *status, Tile &t)
 {
     const int slot = lane >> 3, c = lane & 7;
     const int bs_mask = (1 << cv.kv_bs_log2) - 1;
+    const int row_bytes = cv.nkv * kHeadDim;
+    bool ok[4];
     t.valid = 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int tk = t0 + kSub * kk;
-        bool ok = tk < n;
-        int blk = 0;
-        if (ok) {
-            blk = uniform(bt[tk >> cv.kv_bs_log2]);
-            if (blk < 0 || blk >= cv.num_blocks) {
-                if (lane == 0 && status) atomicOr(status, kDevBadBlockId);
-                ok = false;
-            }
+        const int blk = tb.id[kk];
+        ok[kk] = tk < n;
+        if (ok[kk] && (blk < 0 || blk >= cv.num_blocks)) {
+            if (lane == 0 && status) atomicOr(status, kDevBadBlockId);
+            ok[kk] = false;
         }
-        if (ok) {
-            const size_t row = ((size_t)blk << cv.kv_bs_log2) + (size_t)((tk & bs_mask) + slot);
-            const size_t s = row * (size_t)cv.nkv + kh;
-            t.k[kk] = *reinterpret_cast<const uint4 *>(cv.k_codes + s * kHeadDim + 16 * c);
-            t.ks[kk] = cv.k_scale[s];
-            if (WithV) {
-                t.v[kk] = *reinterpret_cast<const uint4 *>(cv.v_codes + s * kHeadDim + 16 * c);
-                t.vs[kk] = cv.v_scale[s];
-            }
-            t.valid |= (tk + slot < n) ? (1u << kk) : 0u;
-        } else {
-            t.k[kk] = make_uint4(0, 0, 0, 0);
-            t.ks[kk] = 0.0f;
-            if (WithV) {
-                t.v[kk] = make_uint4(0, 0, 0, 0);
-                t.vs[kk] = 0.0f;
-            }
-        }
+        t.valid |= (ok[kk] && tk + slot < n) ? (1u << kk) : 0u;
     }
+    if (BigBlocks) {
+        const bool tok = ok[0];   // the tile's sub-tiles share block tb.id[0]
+        const size_t row0 = ((size_t)(tok ? tb.id[0] : 0) << cv.kv_bs_log2) + (size_t)(t0 & bs_mask);
+        const int bytes = tok ? kTile * row_bytes : 0;
+        const auto rk = make_rsrc(cv.k_codes + row0 * row_bytes, bytes);
+        const auto rv = make_rsrc(cv.v_codes + row0 * row_bytes, bytes);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            t.k[kk] = buf_load16(rk, lo.code, kk * kSub * row_bytes);
+            if (WithV) t.v[kk] = buf_load16(rv, lo.code, kk * kSub * row_bytes);
+        }
+        if (WithV) {
+            const int sbytes = tok ? kTile * cv.nkv * 4 : 0;
+            const auto sk = make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes);
+            const auto sv = make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes);
+            t.sc = buf_load4(sk, lo.scale_k, 0) + buf_load4(sv, lo.scale_v, 0);
+        }
+    } else {
+        float sc = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int tk = t0 + kSub * kk;
+            const size_t row0 = ((size_t)(ok[kk] ? tb.id[kk] : 0) << cv.kv_bs_log2) + (size_t)(tk & bs_mask);
+            const int bytes = ok[kk] ? kSub * row_bytes : 0;
+            t.k[kk] = buf_load16(make_rsrc(cv.k_codes + row0 * row_bytes, bytes), lo.code, 0);
+            if (WithV) {
+                t.v[kk] = buf_load16(make_rsrc(cv.v_codes + row0 * row_bytes, bytes), lo.code, 0);
+                const int sbytes = ok[kk] ? kSub * cv.nkv * 4 : 0;
+                const int mine = ((c & 3) == kk) ? lo.scale_sub : kOutOfRange;
+                sc += buf_load4(make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes), (c < 4) ? mine : kOutOfRange, 0);
+                sc += buf_load4(make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes), (c < 4) ? kOutOfRange : mine, 0);
+            }
+        }
+        if (WithV) t.sc = sc;
+    }
+}
+
+// K and V scales of this lane's token in sub-tile kk, from the lanes of the
+// same 8-lane group that loaded them (see Tile::sc).
+template <int KK>
+__device__ __forceinline__ void tile_scales(const Tile &t, int c, float &ks, float &vs)
+{
+    const float b = dpp_f<0x55 * KK>(t.sc);   // quad_perm [KK, KK, KK, KK]
+    const float m = dpp_f<kDppHalfMirror>(b);   // the other quad's value
+    ks = (c < 4) ? b : m;
+    vs = (c < 4) ? m : b;
 }
 
 }  // namespace q8kv
