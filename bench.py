@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     return ap.parse_args()
@@ -73,6 +77,9 @@ def main():
     q8.lib()   # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(torch, dev, args.copy_probe, args.steps)
+        return
     w = workloads.WORKLOADS[args.workload]
     layers = args.layers or w.layers
     lens = workloads.seq_lens(w)
@@ -120,40 +127,58 @@ def main():
     assert int(status.item()) == 0, "device status set during fill"
     setup_s = time.perf_counter() - t_setup
 
-    stream = torch.cuda.current_stream()
-    n_ev = (args.warmup + args.steps) * layers
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
-
-    def step(s):
+    def step_plain():
         for li in range(layers):
-            e = ev[s * layers + li]
-            e[0].record(stream)
             q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
-            e[1].record(stream)
             q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
                                    dev_status=status)
-            e[2].record(stream)
             q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
                                  dev_status=status)
-            e[3].record(stream)
 
-    for s in range(args.warmup):
-        step(s)
+    # ---- timed region 1: whole steps (one HIP graph per step unless --eager)
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_plain()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_plain()
+    run = graph.replay if graph is not None else step_plain
+    for _ in range(args.warmup):
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        step(s)
+    for _ in range(args.steps):
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(status.item()) == 0, "device status set during timing"
 
-    timed = [ev[s * layers + li] for s in range(args.warmup, args.warmup + args.steps) for li in range(layers)]
-    t_append = np.array([e[0].elapsed_time(e[1]) for e in timed]) * 1e3     # us
-    t_partial = np.array([e[1].elapsed_time(e[2]) for e in timed]) * 1e3
-    t_merge = np.array([e[2].elapsed_time(e[3]) for e in timed]) * 1e3
-    t_layer = np.array([e[0].elapsed_time(e[3]) for e in timed]) * 1e3
-    step_us = np.array([ev[s * layers][0].elapsed_time(ev[s * layers + layers - 1][3])
-                        for s in range(args.warmup, args.warmup + args.steps)]) * 1e3
+    # ---- timed region 2: eager launches with HIP events around each kernel on
+    # the stream the library launches on (the roofline's per-kernel durations)
+    stream = torch.cuda.current_stream()
+    ev_steps = max(2, min(args.steps, 5))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ev_steps * layers)]
+    for s_ in range(ev_steps + 1):
+        for li in range(layers):
+            e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
+            if e: e[0].record(stream)
+            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+            if e: e[1].record(stream)
+            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                   dev_status=status)
+            if e: e[2].record(stream)
+            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                 dev_status=status)
+            if e: e[3].record(stream)
+    torch.cuda.synchronize()
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
+    t_partial = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
 
     attn_b, app_b = algorithmic_bytes(w, lens, kv_bs)
     step_bytes = layers * (attn_b + app_b)
@@ -188,19 +213,29 @@ def main():
             "workload": w.name, "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": nparts,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "us_per_layer_step": round(float(np.median(t_layer)), 2),
-            "us_per_layer_step_p10_p90": [round(float(np.percentile(t_layer, 10)), 2),
-                                          round(float(np.percentile(t_layer, 90)), 2)],
+            "us_per_layer_step": round(ms_per_step * 1e3 / layers, 2),
+            "us_per_layer_step_eager_p10_p50_p90": [round(float(np.percentile(t_layer, q)), 2) for q in (10, 50, 90)],
             "us_append": round(float(np.median(t_append)), 2),
             "us_decode_partial": round(float(np.median(t_partial)), 2),
             "us_decode_merge": round(float(np.median(t_merge)), 2),
-            "us_per_step_events": round(float(np.median(step_us)), 1),
+            "graph": graph is not None,
             "bytes_per_layer_step": int(attn_b + app_b), "setup_s": round(setup_s, 1),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(torch, dev, mib, reps):
+    """A plain device-to-device copy of a known size, so hardware byte counters
+    can be scaled: FETCH_SIZE and WRITE_SIZE of one copy should read mib MiB."""
+    src = torch.ones(mib * 2 ** 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mib * 2 ** 20, "reps": reps}), flush=True)
 
 
 def kernel_hash() -> str:

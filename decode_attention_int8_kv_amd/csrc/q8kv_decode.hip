@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
     const int part = blockIdx.x / p.head_groups;
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int kh = hg * kMaxWavesPerWG + wave;
+    const int kh = hg * (int)(blockDim.x >> 6) + wave;
 
     build_prefix(p, pref, blockIdx.x == 0);
     if (blockIdx.x == 0)
@@ -387,10 +387,25 @@ int decode_blocks_per_cu(int group, int waves)
     return nb;
 }
 
+// Workgroup width (KV heads per workgroup): 8 waves share every token row's
+// lines inside one CU; 4 waves may let more waves stay resident per CU.
+// Picks the width with the most resident waves (ties: the wider one).
+static void choose_width(int nkv, int group, int &waves, int &head_groups)
+{
+    if (nkv <= 4) {
+        waves = nkv;
+    } else {
+        const int r8 = decode_blocks_per_cu(group, 8) * 8;
+        const int r4 = decode_blocks_per_cu(group, 4) * 4;
+        waves = (r4 > r8) ? 4 : 8;
+    }
+    head_groups = (nkv + waves - 1) / waves;
+}
+
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq)
 {
-    const int waves = layer.nkv_heads < kMaxWavesPerWG ? layer.nkv_heads : kMaxWavesPerWG;
-    const int head_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    int waves, head_groups;
+    choose_width(layer.nkv_heads, nq / layer.nkv_heads, waves, head_groups);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
@@ -408,8 +423,7 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
 {
     DecodePlan pl;
     pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
-    pl.head_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
-    pl.waves = layer.nkv_heads < kMaxWavesPerWG ? layer.nkv_heads : kMaxWavesPerWG;
+    choose_width(layer.nkv_heads, nq / layer.nkv_heads, pl.waves, pl.head_groups);
     // merge waves: about the number of pieces a sequence is cut into
     long long per_seq = (long long)pl.nparts / (batch.batch > 0 ? batch.batch : 1) + 2;
     int mw = 1;

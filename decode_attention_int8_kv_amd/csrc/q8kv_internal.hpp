@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/q8kv.h"
+#include "q8kv.h"
 
 namespace q8kv {
 

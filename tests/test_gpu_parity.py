@@ -266,3 +266,48 @@ def test_phase_entry_points_equal_one_call():
     m.decode_attn_partial(dc.layer, dc.batch, 16, q, SCALE, out, ws, nparts=9)
     m.decode_attn_merge(dc.layer, dc.batch, 16, q, SCALE, out, ws, nparts=9)
     assert t.equal(out, one)
+
+
+def test_graph_replays_match_eager():
+    # The append + decode sequence captured in one HIP graph and replayed
+    # several times, with eager work and synchronizations in between, gives
+    # the eager bits every time (no memset nodes are involved).
+    t = torch()
+    say("[graph] capture / replay")
+    lens = np.array([700, 65, 1, 300], np.int32)
+    k, v = dense_kv(lens, 8, seed=81)
+    dc = DeviceCache(lens, 8, 32, seed=81)
+    dc.append_dense(k, v)
+    m = q8()
+    rng = np.random.default_rng(81)
+    q = t.from_numpy(rng.standard_normal((4, 16, 128)).astype(np.float32)).cuda()
+    kn = t.from_numpy(rng.standard_normal((4, 8, 128)).astype(np.float32)).cuda()
+    vn = t.from_numpy(rng.standard_normal((4, 8, 128)).astype(np.float32)).cuda()
+    seqs = t.arange(4, dtype=t.int32, device="cuda")
+    pos = (dc.lens_t - 1).to(t.int32)
+    ws = t.empty(m.decode_attn_workspace_bytes(dc.layer, dc.batch, 16, 0), dtype=t.uint8, device="cuda")
+    out = t.empty((4, 16, 128), dtype=t.float32, device="cuda")
+
+    def body():
+        m.kv_append(dc.layer, dc.batch, seqs, pos, kn, vn, dev_status=dc.status)
+        m.decode_attn(dc.layer, dc.batch, 16, q, SCALE, out, ws, dev_status=dc.status)
+
+    body()
+    t.cuda.synchronize()
+    eager = out.clone()
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        body()
+    t.cuda.current_stream().wait_stream(side)
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        body()
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)                      # eager work touching the workspace in between
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(out, eager), f"replay {i}"
+    assert dc.status_word() == 0
