@@ -57,7 +57,7 @@ constexpr int kOutOfRange = 0x7ffffff0;   // a lane offset past any resource
 struct Tile {
     uint4 k[4];
     uint4 v[4];
-    float sc;         // this lane's scale: K (c < 4) or V (c >= 4) of token t0 + 8 (c % 4) + slot
+    float sk, sv;     // this lane's scale: K (c < 4, sv = 0) or V (c >= 4, sk = 0) of token t0 + 8 (c % 4) + slot
     uint32_t valid;   // bit k: token t0 + 8 k + slot is inside the sequence (and its block id is good)
 };
 
@@ -120,18 +120,18 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
     const int bs_mask = (1 << cv.kv_bs_log2) - 1;
     const int row_bytes = cv.nkv * kHeadDim;
     bool ok[4];
+    bool bad = false;
     t.valid = 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int tk = t0 + kSub * kk;
-        const int blk = tb.id[kk];
-        ok[kk] = tk < n;
-        if (ok[kk] && (blk < 0 || blk >= cv.num_blocks)) {
-            if (lane == 0 && status) atomicOr(status, kDevBadBlockId);
-            ok[kk] = false;
-        }
+        const bool want = tk < n;
+        const bool good = (unsigned)tb.id[kk] < (unsigned)cv.num_blocks;
+        ok[kk] = want && good;
+        bad = bad || (want && !good);
         t.valid |= (ok[kk] && tk + slot < n) ? (1u << kk) : 0u;
     }
+    if (bad && lane == 0 && status) atomicOr(status, kDevBadBlockId);
     if (BigBlocks) {
         const bool tok = ok[0];   // the tile's sub-tiles share block tb.id[0]
         const size_t row0 = ((size_t)(tok ? tb.id[0] : 0) << cv.kv_bs_log2) + (size_t)(t0 & bs_mask);
@@ -147,10 +147,12 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
             const int sbytes = tok ? kTile * cv.nkv * 4 : 0;
             const auto sk = make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes);
             const auto sv = make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes);
-            t.sc = buf_load4(sk, lo.scale_k, 0) + buf_load4(sv, lo.scale_v, 0);
+            // kept apart: adding them here would make the loop wait for them
+            t.sk = buf_load4(sk, lo.scale_k, 0);
+            t.sv = buf_load4(sv, lo.scale_v, 0);
         }
     } else {
-        float sc = 0.0f;
+        float sk = 0.0f, sv = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int tk = t0 + kSub * kk;
@@ -161,11 +163,14 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
                 t.v[kk] = buf_load16(make_rsrc(cv.v_codes + row0 * row_bytes, bytes), lo.code, 0);
                 const int sbytes = ok[kk] ? kSub * cv.nkv * 4 : 0;
                 const int mine = ((c & 3) == kk) ? lo.scale_sub : kOutOfRange;
-                sc += buf_load4(make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes), (c < 4) ? mine : kOutOfRange, 0);
-                sc += buf_load4(make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes), (c < 4) ? kOutOfRange : mine, 0);
+                sk += buf_load4(make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes), (c < 4) ? mine : kOutOfRange, 0);
+                sv += buf_load4(make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes), (c < 4) ? kOutOfRange : mine, 0);
             }
         }
-        if (WithV) t.sc = sc;
+        if (WithV) {
+            t.sk = sk;
+            t.sv = sv;
+        }
     }
 }
 
@@ -174,7 +179,8 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
 template <int KK>
 __device__ __forceinline__ void tile_scales(const Tile &t, int c, float &ks, float &vs)
 {
-    const float b = dpp_f<0x55 * KK>(t.sc);   // quad_perm [KK, KK, KK, KK]
+    const float sc = t.sk + t.sv;              // one of the two is 0
+    const float b = dpp_f<0x55 * KK>(sc);       // quad_perm [KK, KK, KK, KK]
     const float m = dpp_f<kDppHalfMirror>(b);   // the other quad's value
     ks = (c < 4) ? b : m;
     vs = (c < 4) ? m : b;
