@@ -46,6 +46,9 @@ def parse():
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="no GPU work: read rocprofv3 counter CSVs under DIR/{copyf,copyw,fetch,write} "
+                         "and record the workload's bytes per partial launch in --traffic")
     return ap.parse_args()
 
 
@@ -64,8 +67,73 @@ def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int):
     return kv + qo + meta, app
 
 
+def _counter_values(path: str, counter: str, kernel_substr: str) -> list:
+    import csv
+    import glob
+    vals = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    return vals
+
+
+def traffic_from(args):
+    """Copy-calibrated HBM bytes per decode partial launch.  FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) are read for a plain copy of a known size
+    (bench.py --copy-probe) and for the partial kernel of the workload; each
+    counter is scaled by (copy bytes / counter reading of the copy)."""
+    d = args.traffic_from
+    probe = None
+    for name in ("copyf", "copyw"):
+        log = os.path.join(d, name + ".log")
+        if os.path.exists(log):
+            for line in open(log):
+                if line.startswith("{") and "copy_probe_bytes" in line:
+                    probe = json.loads(line)["copy_probe_bytes"]
+    if probe is None:
+        raise SystemExit("no copy-probe size found in copyf.log / copyw.log")
+    kib = probe / 1024.0
+
+    def factor(sub, counter):
+        v = sorted(_counter_values(os.path.join(d, sub), counter, "copyBuffer"))
+        v = [x for x in v if x > 0.5 * kib / 4]   # the probe's copies, not small blits
+        if not v:
+            raise SystemExit(f"no copy dispatches with {counter} under {sub}")
+        return kib / float(np.median(v)), float(np.median(v))
+
+    ff, fcopy = factor("copyf", "FETCH_SIZE")
+    fw, wcopy = factor("copyw", "WRITE_SIZE")
+    fetch = _counter_values(os.path.join(d, "fetch"), "FETCH_SIZE", "q8_attn_partial_kernel")
+    write = _counter_values(os.path.join(d, "write"), "WRITE_SIZE", "q8_attn_partial_kernel")
+    if not fetch or not write:
+        raise SystemExit("no q8_attn_partial_kernel dispatches in fetch/ or write/")
+    fk, wk = float(np.median(fetch)), float(np.median(write))
+    total = (fk * ff + wk * fw) * 1024.0
+    rec = {}
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            rec = json.load(f)
+    rec[args.workload] = {
+        "kernel": "q8_attn_partial_kernel", "kernel_hash": kernel_hash(),
+        "bytes_per_launch": int(round(total)),
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "dispatches": [len(fetch), len(write)],
+        "copy_probe_bytes": probe, "copy_fetch_kib": round(fcopy, 1), "copy_write_kib": round(wcopy, 1),
+        "fetch_factor": round(ff, 4), "write_factor": round(fw, 4),
+    }
+    with open(args.traffic, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec[args.workload]))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(each GPU would run the same kernels on its own share of sequences or KV heads). "
@@ -273,7 +341,7 @@ def cpu_baseline(w, lens, table, nblocks, attn_bytes):
         oracle.decode_attn(cache, q, w.nq, float(workloads.softmax_scale(w.head_dim)), nthreads=threads)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 200:
+        if dt >= 10.0 or reps >= 20000:
             break
     n = sl.astype(np.int64)
     b = int(n.sum()) * w.nkv * (2 * w.head_dim + 8) + sub.batch * w.nq * w.head_dim * 8
