@@ -303,11 +303,15 @@ struct MergeParams {
 };
 
 constexpr int kMaxMergeWaves = 16;
+constexpr int kMergeBatch = 8;   // pieces whose loads a wave has in flight together
 
 // One workgroup per (sequence, query head) whose tiles span several ranges:
 // combines the pieces' (M, S, acc) with the online-softmax rescale rule
-// ("9-2" §2 segment 2 applied to whole partial states), in a fixed order,
-// then divides once.
+// ("9-2" §2 segment 2 applied to whole partial states).  Wave w takes pieces
+// w, w + waves, ..., kMergeBatch of them per round with all their loads
+// issued before any is used, and keeps its own running max; the waves' states
+// are then combined in wave order, so the result does not depend on timing.
+// A batch with fewer pieces than waves * kMergeBatch costs one round trip.
 __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(MergeParams p)
 {
     const int b = blockIdx.x / p.nq, h = blockIdx.x - b * p.nq;
@@ -315,22 +319,43 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     if (e0 == a0) return;
     const int i0 = part_of(a0, total, p.nparts), i1 = part_of(e0 - 1, total, p.nparts);
     if (i0 == i1) return;
-
+    const int np = i1 - i0 + 1;
+    // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
+    const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+
     float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
-    for (int i = i0 + wave; i <= i1; i += waves) {
-        const int st = part_start(i, total, p.nparts), en = part_start(i + 1, total, p.nparts);
-        if (st == en) continue;
-        const int slot = (i == i0 && st < a0) ? 1 : 0;
-        const size_t idx = ((size_t)i * 2 + slot) * p.nq + h;
-        const float2 ms = p.ws_ms[idx];
-        const float2 av = reinterpret_cast<const float2 *>(p.ws_acc + idx * kHeadDim)[lane];
-        if (ms.x == -INFINITY) continue;
-        const float mn = fmaxf(m, ms.x);
-        const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ms.x - mn);
-        s = s * fo + ms.y * fn;
-        ax = ax * fo + av.x * fn;
-        ay = ay * fo + av.y * fn;
+    for (int j0 = wave; j0 < np; j0 += kMergeBatch * waves) {
+        float2 ms[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int j = j0 + u * waves, i = i0 + j;
+            // an empty range (more ranges than tiles) wrote no record
+            const bool have = j < np && part_start(i, total, p.nparts) != part_start(i + 1, total, p.nparts);
+            if (have) {
+                const size_t r = ((size_t)i * 2 + (j == 0 ? slot0 : 0)) * p.nq + h;
+                ms[u] = p.ws_ms[r];
+                av[u] = reinterpret_cast<const float2 *>(p.ws_acc + r * kHeadDim)[lane];
+            } else {
+                ms[u] = make_float2(-INFINITY, 0.0f);
+                av[u] = make_float2(0.0f, 0.0f);
+            }
+        }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) mn = fmaxf(mn, ms[u].x);
+        if (mn == -INFINITY) continue;   // nothing visible yet
+        const float fo = __builtin_amdgcn_exp2f(m - mn);   // 0 while m is -inf
+        s *= fo;
+        ax *= fo;
+        ay *= fo;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const float f = __builtin_amdgcn_exp2f(ms[u].x - mn);   // 0 for an empty piece
+            s = fmaf(ms[u].y, f, s);
+            ax = fmaf(av[u].x, f, ax);
+            ay = fmaf(av[u].y, f, ay);
+        }
         m = mn;
     }
 
@@ -343,23 +368,21 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     sh_a[wave][lane] = make_float2(ax, ay);
     __syncthreads();
     if (wave != 0) return;
-    m = -INFINITY;
+    float mx = -INFINITY;
+    for (int w = 0; w < waves; ++w) mx = fmaxf(mx, sh_m[w]);
     s = 0.0f;
     ax = ay = 0.0f;
-    for (int w = 0; w < waves; ++w) {
-        const float mw = sh_m[w];
-        if (mw == -INFINITY) continue;
-        const float mn = fmaxf(m, mw);
-        const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(mw - mn);
-        const float2 aw = sh_a[w][lane];
-        s = s * fo + sh_s[w] * fn;
-        ax = ax * fo + aw.x * fn;
-        ay = ay * fo + aw.y * fn;
-        m = mn;
+    if (mx != -INFINITY) {
+        for (int w = 0; w < waves; ++w) {
+            const float f = __builtin_amdgcn_exp2f(sh_m[w] - mx);   // 0 for a wave that saw nothing
+            const float2 aw = sh_a[w][lane];
+            s = fmaf(sh_s[w], f, s);
+            ax = fmaf(aw.x, f, ax);
+            ay = fmaf(aw.y, f, ay);
+        }
     }
-    float2 r = make_float2(0.0f, 0.0f);
-    if (s > 0.0f) r = make_float2(ax / s, ay / s);
-    reinterpret_cast<float2 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim)[lane] = r;
+    float2 *o = reinterpret_cast<float2 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim);
+    o[lane] = s > 0.0f ? make_float2(ax / s, ay / s) : make_float2(0.0f, 0.0f);
 }
 
 // ----------------------------------------------------------------- host ----
