@@ -99,6 +99,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
                                              int slot)
 {
     const int c = lane & 7, tslot = lane >> 3;
+    const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
 
     // Q quantized once per (sequence, head) ("9-2" §2 segment 1).
     uint4 qc[G];
@@ -107,13 +108,32 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     for (int g = 0; g < G; ++g)
         quantize_q_quarter(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim, c, qc[g], qs[g]);
 
+    // PV on the matrix cores for groups of four heads: lane (slot, c) is in
+    // the 4-lane block of token slot and bytes [16c, 16c + 16); with the
+    // weight of head 4q + c % 4 as its a operand and its byte j as its b
+    // operand, one v_mfma_f32_4x4x1 adds w[4q + i] * v[16c + j] to register
+    // i of accm[q][j] -- the same per-lane accumulators as the VALU path,
+    // with the 64 fp32 multiply-adds per lane and sub-tile moved off the
+    // VALU.  (Groups of 8 would take two MFMAs per byte; that variant spills
+    // and stays on the VALU path.)
+    constexpr bool kPvMfma = G == 4;
+    constexpr int NQ = kPvMfma ? G / 4 : 1;
     float M[G], S[G], acc[G][16];
+    v4f accm[NQ][16];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         M[g] = -INFINITY;
         S[g] = 0.0f;
+        if constexpr (!kPvMfma) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+            for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+        }
+    }
+    if constexpr (kPvMfma) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) accm[q][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
     const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
@@ -148,29 +168,66 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
             if (m > M[g]) {
                 const float a = __builtin_amdgcn_exp2f(M[g] - m);
                 S[g] *= a;
+                if constexpr (kPvMfma) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc[g][j] *= a;
+                    for (int j = 0; j < 16; ++j) accm[g >> 2][j][g & 3] *= a;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) acc[g][j] *= a;
+                }
                 M[g] = m;
             }
         }
         // Weights and V accumulation: acc += code_v * (w * vs).
+        float Mf[G];   // M, or 0 while no token has been seen (then every weight is 0)
+#pragma unroll
+        for (int g = 0; g < G; ++g) Mf[g] = M[g] == -INFINITY ? 0.0f : M[g];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const bool ok = (t.valid >> kk) & 1u;
-            float w[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                // masked tokens contribute nothing (their scale may be any bit pattern)
-                const float pw = ok ? __builtin_amdgcn_exp2f(s[kk][g] - M[g]) : 0.0f;
-                S[g] += pw;
-                w[g] = ok ? pw * vs[kk] : 0.0f;
-            }
             const uint32_t words[4] = {t.v[kk].x, t.v[kk].y, t.v[kk].z, t.v[kk].w};
+            // masked tokens contribute nothing (their scale may be any bit pattern)
+            if constexpr (kPvMfma) {
+                // branch-free: a masked token's score is -inf, so its weight
+                // is exp2(-inf) = 0 against the finite reference Mf
+                float pw[G];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float vf = byte_f(words[j >> 2], j & 3);
+                for (int g = 0; g < G; ++g) {
+                    pw[g] = __builtin_amdgcn_exp2f(s[kk][g] - Mf[g]);
+                    S[g] += pw[g];
+                }
+                const uint32_t okm = ok ? 0xffffffffu : 0u;
+                float wa[NQ];
 #pragma unroll
-                for (int g = 0; g < G; ++g) acc[g][j] = fmaf(w[g], vf, acc[g][j]);
+                for (int q = 0; q < NQ; ++q) {
+                    // the weight of head 4q + c % 4, picked with bit masks
+                    const uint32_t lo2 = bitsel(m1, __float_as_uint(pw[4 * q + 1]), __float_as_uint(pw[4 * q]));
+                    const uint32_t hi2 = bitsel(m1, __float_as_uint(pw[4 * q + 3]), __float_as_uint(pw[4 * q + 2]));
+                    const float w = __uint_as_float(bitsel(m2, hi2, lo2)) * vs[kk];
+                    wa[q] = __uint_as_float(__float_as_uint(w) & okm);
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float vf = byte_f(words[j >> 2], j & 3);
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) accm[q][j] = mfma_outer4(wa[q], vf, accm[q][j]);
+                }
+            } else {
+                float pw[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    pw[g] = ok ? __builtin_amdgcn_exp2f(s[kk][g] - M[g]) : 0.0f;
+                    S[g] += pw[g];
+                }
+                float w[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) w[g] = ok ? pw[g] * vs[kk] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float vf = byte_f(words[j >> 2], j & 3);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) acc[g][j] = fmaf(w[g], vf, acc[g][j]);
+                }
             }
         }
     };
@@ -195,6 +252,13 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
         fetch_blocks(bt, log2bs, (lt + 2) * kTile, ne, bb);
         process(tb);
         if (++lt >= lt1) break;
+    }
+
+    if constexpr (kPvMfma) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[g][j] = accm[g >> 2][j][g & 3];
     }
 
     // Sum the 8 token slots of the wave.

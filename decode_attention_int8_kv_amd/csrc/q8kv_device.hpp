@@ -172,6 +172,23 @@ __device__ __forceinline__ float byte_f(uint32_t w, int b)
     return (float)(int)(int8_t)((w >> (8 * b)) & 0xff);
 }
 
+// Bits of a where m is set, of b elsewhere (v_bfi_b32).
+__device__ __forceinline__ uint32_t bitsel(uint32_t m, uint32_t a, uint32_t b)
+{
+    return (m & a) | (~m & b);
+}
+
+// --------------------------------------------------------- matrix cores
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_4x4x1_16b_f32: the wave is 16 blocks of 4 lanes; in block b,
+// register i of lane 4b + j gains a(lane 4b + i) * b(lane 4b + j) -- an fp32
+// outer product of the block's 4 a values and 4 b values.
+__device__ __forceinline__ v4f mfma_outer4(float a, float b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
 // ------------------------------------------------------ query quantization
 // Lane (slot, c) of a wave owns elements [16c, 16c+16) of a 128-element query
 // row; the 32-block of those elements is shared with lane c^1.  Quantizes the
