@@ -114,7 +114,7 @@ class KVLayer:
     """One layer's blocked q8 pool (torch tensors on the GPU, or raw pointers).
 
     k_codes/v_codes: int8 [num_blocks, kv_bs, nkv_heads * head_dim]
-    k_scale/v_scale: fp32 [num_blocks, kv_bs, nkv_heads]
+    k_scale/v_scale: fp32 [num_blocks, nkv_heads, kv_bs]
     """
     k_codes: object
     v_codes: object
@@ -150,7 +150,7 @@ def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head
     import torch
     kc = torch.empty((num_blocks, kv_bs, nkv_heads * head_dim), dtype=torch.int8, device=device)
     vc = torch.empty_like(kc)
-    ks = torch.empty((num_blocks, kv_bs, nkv_heads), dtype=torch.float32, device=device)
+    ks = torch.empty((num_blocks, nkv_heads, kv_bs), dtype=torch.float32, device=device)
     vs = torch.empty_like(ks)
     return KVLayer(kc, vc, ks, vs, nkv_heads, kv_bs, num_blocks, head_dim)
 

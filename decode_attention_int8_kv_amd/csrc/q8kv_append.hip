@@ -74,16 +74,18 @@ __global__ __launch_bounds__(64 * kAppendWaves) void q8_append_kernel(AppendPara
     const RowQuant kq = kv_row_params(ka);
     const RowQuant vq = kv_row_params(va);
 
-    const size_t cache_row = ((size_t)blk << p.kv_bs_log2) + (pos & ((1 << p.kv_bs_log2) - 1));
-    const size_t slot = cache_row * p.nkv + kh;
-    const size_t dst = slot * kHeadDim + 2 * lane;
+    const int row_in_blk = pos & ((1 << p.kv_bs_log2) - 1);
+    const size_t cache_row = ((size_t)blk << p.kv_bs_log2) + row_in_blk;
+    const size_t dst = (cache_row * p.nkv + kh) * kHeadDim + 2 * lane;
+    // scales: [block][kv head][row], a head's rows of a block side by side
+    const size_t sdst = (((size_t)blk * p.nkv + kh) << p.kv_bs_log2) + row_in_blk;
     const uint16_t kc = (uint16_t)((kv_code(k.x, kq.recip) & 0xff) | ((kv_code(k.y, kq.recip) & 0xff) << 8));
     const uint16_t vc = (uint16_t)((kv_code(v.x, vq.recip) & 0xff) | ((kv_code(v.y, vq.recip) & 0xff) << 8));
     *reinterpret_cast<uint16_t *>(p.k_codes + dst) = kc;
     *reinterpret_cast<uint16_t *>(p.v_codes + dst) = vc;
     if (lane == 0) {
-        p.k_scale[slot] = kq.step;
-        p.v_scale[slot] = vq.step;
+        p.k_scale[sdst] = kq.step;
+        p.v_scale[sdst] = vq.step;
     }
 }
 

@@ -474,19 +474,16 @@ int decode_blocks_per_cu(int group, int waves)
     return nb;
 }
 
-// Workgroup width (KV heads per workgroup): 8 waves share every token row's
-// lines inside one CU; 4 waves may let more waves stay resident per CU.
-// Picks the width with the most resident waves (ties: the wider one).
+// Workgroup width (KV heads per workgroup): one workgroup per token range for
+// up to 8 KV heads, else the heads split evenly over the fewest workgroups.
+// The waves of a workgroup then read whole 1 KB token rows together; on the
+// ragged 2B batch this measured the same time as two 4-wave workgroups with
+// three resident per CU, with half the workgroups to set up.
 static void choose_width(int nkv, int group, int &waves, int &head_groups)
 {
-    if (nkv <= 4) {
-        waves = nkv;
-    } else {
-        const int r8 = decode_blocks_per_cu(group, 8) * 8;
-        const int r4 = decode_blocks_per_cu(group, 4) * 4;
-        waves = (r4 > r8) ? 4 : 8;
-    }
-    head_groups = (nkv + waves - 1) / waves;
+    (void)group;
+    head_groups = (nkv + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    waves = (nkv + head_groups - 1) / head_groups;
 }
 
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq)

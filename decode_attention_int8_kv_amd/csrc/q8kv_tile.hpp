@@ -14,7 +14,9 @@
 // come from scalar loads issued a tile ahead, and each lane loads one scale
 // per tile -- lane (slot, c) the K (c < 4) or V (c >= 4) scale of token
 // t0 + 8 (c % 4) + slot -- which DPP moves then hand to the lanes that need
-// them.
+// them.  Scales are stored [block][kv head][row], so the 32 scales of one
+// head in a tile are one 128-byte line per array: a wave reads only its own
+// head's lines, and every scale line is fetched once.
 #pragma once
 
 #include "q8kv_device.hpp"
@@ -82,9 +84,10 @@ __device__ __forceinline__ void fetch_blocks(const int32_t *bt, int log2bs, int 
 // Per-lane constants of the tile walk (loop invariant).
 struct LaneOffsets {
     int code;     // byte offset of this lane's 16 bytes inside an 8-row sub-tile
-    int scale_k;  // byte offset of this lane's K scale inside a 32-row tile, or out of range
+    int scale_k;  // byte offset of this lane's K scale among the head's 32 tile rows, or out of range
     int scale_v;  // same for V
     int scale_sub;// byte offset of this lane's scale inside an 8-row sub-tile
+    int kh;       // the wave's KV head
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh, int lane)
@@ -93,10 +96,11 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh,
     const int row_bytes = cv.nkv * kHeadDim;
     LaneOffsets o;
     o.code = slot * row_bytes + kh * kHeadDim + 16 * c;
-    const int in_tile = ((kSub * (c & 3) + slot) * cv.nkv + kh) * 4;
+    const int in_tile = (kSub * (c & 3) + slot) * 4;
     o.scale_k = (c < 4) ? in_tile : kOutOfRange;
     o.scale_v = (c < 4) ? kOutOfRange : in_tile;
-    o.scale_sub = (slot * cv.nkv + kh) * 4;
+    o.scale_sub = slot * 4;
+    o.kh = kh;
     return o;
 }
 
@@ -136,20 +140,23 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
         const bool tok = ok[0];   // the tile's sub-tiles share block tb.id[0]
         const size_t row0 = ((size_t)(tok ? tb.id[0] : 0) << cv.kv_bs_log2) + (size_t)(t0 & bs_mask);
         const int bytes = tok ? kTile * row_bytes : 0;
+        if (WithV) {
+            // the head's 32 scales of the tile ([block][kv head][row])
+            const size_t s0 = ((((size_t)(tok ? tb.id[0] : 0) * cv.nkv + lo.kh) << cv.kv_bs_log2) +
+                               (size_t)(t0 & bs_mask));
+            const int sbytes = tok ? kTile * 4 : 0;
+            const auto sk = make_rsrc(cv.k_scale + s0, sbytes);
+            const auto sv = make_rsrc(cv.v_scale + s0, sbytes);
+            // kept apart: adding them here would make the loop wait for them
+            t.sk = buf_load4(sk, lo.scale_k, 0);
+            t.sv = buf_load4(sv, lo.scale_v, 0);
+        }
         const auto rk = make_rsrc(cv.k_codes + row0 * row_bytes, bytes);
         const auto rv = make_rsrc(cv.v_codes + row0 * row_bytes, bytes);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             t.k[kk] = buf_load16(rk, lo.code, kk * kSub * row_bytes);
             if (WithV) t.v[kk] = buf_load16(rv, lo.code, kk * kSub * row_bytes);
-        }
-        if (WithV) {
-            const int sbytes = tok ? kTile * cv.nkv * 4 : 0;
-            const auto sk = make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes);
-            const auto sv = make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes);
-            // kept apart: adding them here would make the loop wait for them
-            t.sk = buf_load4(sk, lo.scale_k, 0);
-            t.sv = buf_load4(sv, lo.scale_v, 0);
         }
     } else {
         float sk = 0.0f, sv = 0.0f;
@@ -161,10 +168,12 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
             t.k[kk] = buf_load16(make_rsrc(cv.k_codes + row0 * row_bytes, bytes), lo.code, 0);
             if (WithV) {
                 t.v[kk] = buf_load16(make_rsrc(cv.v_codes + row0 * row_bytes, bytes), lo.code, 0);
-                const int sbytes = ok[kk] ? kSub * cv.nkv * 4 : 0;
+                const size_t s0 = ((((size_t)(ok[kk] ? tb.id[kk] : 0) * cv.nkv + lo.kh) << cv.kv_bs_log2) +
+                                   (size_t)(tk & bs_mask));
+                const int sbytes = ok[kk] ? kSub * 4 : 0;
                 const int mine = ((c & 3) == kk) ? lo.scale_sub : kOutOfRange;
-                sk += buf_load4(make_rsrc(cv.k_scale + row0 * cv.nkv, sbytes), (c < 4) ? mine : kOutOfRange, 0);
-                sv += buf_load4(make_rsrc(cv.v_scale + row0 * cv.nkv, sbytes), (c < 4) ? kOutOfRange : mine, 0);
+                sk += buf_load4(make_rsrc(cv.k_scale + s0, sbytes), (c < 4) ? mine : kOutOfRange, 0);
+                sv += buf_load4(make_rsrc(cv.v_scale + s0, sbytes), (c < 4) ? kOutOfRange : mine, 0);
             }
         }
         if (WithV) {

@@ -17,11 +17,13 @@
  *
  * Data layout (device memory, owned by the caller; one pool per layer):
  *   k_codes, v_codes : int8  [num_blocks][kv_bs][nkv_heads * head_dim]
- *   k_scale, v_scale : fp32  [num_blocks][kv_bs][nkv_heads]
+ *   k_scale, v_scale : fp32  [num_blocks][nkv_heads][kv_bs]
  *     Token t of sequence b lives in physical block block_table[b][t / kv_bs]
  *     at row t % kv_bs; head kh occupies bytes [kh*head_dim, (kh+1)*head_dim)
- *     of that row ("9-2" §2 segment 2).  The scale stored for a row is the
- *     step d = max-abs * fl(1/127); a dequantized value is code * d.
+ *     of that row ("9-2" §2 segment 2), and its scale is element
+ *     [block][kh][t % kv_bs] -- per block, one head's scales side by side.
+ *     The scale stored for a row is the step d = max-abs * fl(1/127); a
+ *     dequantized value is code * d.
  *   block_table : int32 [batch][max_blocks_per_seq] (physical block ids)
  *   seq_lens    : int32 [batch] (tokens visible to attention, including the
  *                 token appended this step)

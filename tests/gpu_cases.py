@@ -77,8 +77,11 @@ class DeviceCache:
     def host(self):
         """The cache as an oracle.Cache (codes and steps copied back)."""
         L = self.layer
-        return oracle.Cache(L.k_codes.cpu().numpy(), L.v_codes.cpu().numpy(), L.k_scale.cpu().numpy(),
-                            L.v_scale.cpu().numpy(), self.table, self.lens, self.nkv, 128)
+        # the library stores scales [block][kv head][row]; the oracle takes [block][row][kv head]
+        ks = np.ascontiguousarray(L.k_scale.cpu().numpy().transpose(0, 2, 1))
+        vs = np.ascontiguousarray(L.v_scale.cpu().numpy().transpose(0, 2, 1))
+        return oracle.Cache(L.k_codes.cpu().numpy(), L.v_codes.cpu().numpy(), ks, vs,
+                            self.table, self.lens, self.nkv, 128)
 
     def decode(self, q, nq, scale, nparts=0, out=None):
         t = torch()
