@@ -100,7 +100,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh,
     o.scale_k = (c < 4) ? in_tile : kOutOfRange;
     o.scale_v = (c < 4) ? kOutOfRange : in_tile;
     o.scale_sub = slot * 4;
-    o.kh = kh;
+    o.kh = uniform(kh);   // wave-uniform: the scale resources live in SGPRs
     return o;
 }
 
