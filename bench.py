@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--eager", action="store_true",
@@ -129,6 +131,144 @@ def traffic_from(args):
     print(json.dumps(rec[args.workload]))
 
 
+# Configurations measured beside the headline workload, each with the
+# workload's own layer count and a distinct cache pool per layer (so every
+# layer's cache is cold in the 256 MB last-level cache whenever a layer
+# exceeds it).
+SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n4059",
+         "qwen8b_b32_n32k", "qwen8b_b1_n128k", "qwen8b_b128_stress")
+
+
+def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False):
+    """One workload: fill `layers` cache pools, then time whole decode steps
+    (graph replay unless eager) and, in an eager pass with HIP events on the
+    library's stream, each kernel.  Returns a dict of figures."""
+    lens = workloads.seq_lens(w)
+    kv_bs = w.kv_bs
+    B, nq, nkv, hd = w.batch, w.nq, w.nkv, w.head_dim
+    scale = float(workloads.softmax_scale(hd))
+    t_setup = time.perf_counter()
+
+    # ---- cache: one pool per layer, blocks of every sequence scattered at random
+    table, nblocks = workloads.block_table(lens, kv_bs, w.seed)
+    table_t = torch.from_numpy(table).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    batch = q8.make_batch(table_t, lens_t, int(max(1, lens.max())))
+    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev) for _ in range(layers)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # history: every position but the last, appended from a source pool drawn
+    # with the workload's value distribution
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    src_k = workloads.kv_pool_torch(w, POOL_TOKENS + FILL_CHUNK, gen, dev)
+    src_v = workloads.kv_pool_torch(w, POOL_TOKENS + FILL_CHUNK, gen, dev)
+    hist_seq = np.concatenate([np.full(max(n - 1, 0), b, np.int32) for b, n in enumerate(lens)])
+    hist_pos = np.concatenate([np.arange(max(n - 1, 0), dtype=np.int32) for n in lens])
+    hist_seq_t = torch.from_numpy(hist_seq).to(dev)
+    hist_pos_t = torch.from_numpy(hist_pos).to(dev)
+    rng = np.random.default_rng(w.seed)
+    for li, pool in enumerate(pools):
+        for c0 in range(0, hist_seq.size, FILL_CHUNK):
+            c1 = min(hist_seq.size, c0 + FILL_CHUNK)
+            off = int(rng.integers(0, POOL_TOKENS))
+            q8.kv_append(pool, batch, hist_seq_t[c0:c1], hist_pos_t[c0:c1],
+                         src_k[off:off + c1 - c0], src_v[off:off + c1 - c0], dev_status=status)
+    del src_k, src_v
+
+    # the step's inputs: one new token per sequence (position n_b - 1) and q, per layer
+    step_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    step_pos = (lens_t - 1).clamp(min=0).to(torch.int32)
+    new_k = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
+    new_v = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
+    qs = torch.randn((layers, B, nq, hd), generator=gen, device=dev)
+    outs = torch.empty((layers, B, nq, hd), dtype=torch.float32, device=dev)
+    nparts = nparts_arg or q8.decode_attn_auto_parts(pools[0], batch, nq)
+    ws = torch.empty(q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set during fill"
+    setup_s = time.perf_counter() - t_setup
+
+    def step_plain():
+        for li in range(layers):
+            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                   dev_status=status)
+            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                 dev_status=status)
+
+    # ---- timed region 1: whole steps (one HIP graph per step unless eager)
+    graph = None
+    if not eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_plain()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_plain()
+    run = graph.replay if graph is not None else step_plain
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0, "device status set during timing"
+
+    # ---- timed region 2: eager launches with HIP events around each kernel on
+    # the stream the library launches on (the roofline's per-kernel durations)
+    stream = torch.cuda.current_stream()
+    ev_steps = max(2, min(steps, 5))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ev_steps * layers)]
+    for s_ in range(ev_steps + 1):
+        for li in range(layers):
+            e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
+            if e: e[0].record(stream)
+            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+            if e: e[1].record(stream)
+            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                   dev_status=status)
+            if e: e[2].record(stream)
+            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
+                                 dev_status=status)
+            if e: e[3].record(stream)
+    torch.cuda.synchronize()
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
+    t_partial = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
+
+    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs)
+    ms_per_step = wall * 1e3 / steps
+    del pools, outs, qs, new_k, new_v, ws
+    return {
+        "lens": lens, "table": table, "nblocks": nblocks, "nparts": nparts, "layers": layers,
+        "ms_per_step": ms_per_step, "attn_bytes": attn_b, "append_bytes": app_b,
+        "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
+        "graph": graph is not None, "setup_s": setup_s,
+    }
+
+
+def sweep_entry(w, m):
+    step_bytes = m["layers"] * (m["attn_bytes"] + m["append_bytes"])
+    gbs = step_bytes / (m["ms_per_step"] * 1e-3) / 1e9
+    part_us = float(m["t_partial"].mean())
+    return {
+        "workload": w.name, "batch": w.batch, "nq_heads": w.nq, "nkv_heads": w.nkv, "ctx": list(w.lens),
+        "layers": m["layers"], "nparts": m["nparts"],
+        "us_per_layer_step": round(m["ms_per_step"] * 1e3 / m["layers"], 2),
+        "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_decode_partial": round(float(np.median(m["t_partial"])), 2),
+        "partial_GBps": round(m["attn_bytes"] / (part_us * 1e-6) / 1e9, 1),
+        "us_decode_merge": round(float(np.median(m["t_merge"])), 2),
+        "us_append": round(float(np.median(m["t_append"])), 2),
+    }
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -150,108 +290,14 @@ def main():
         return
     w = workloads.WORKLOADS[args.workload]
     layers = args.layers or w.layers
-    lens = workloads.seq_lens(w)
-    kv_bs = w.kv_bs
-    B, nq, nkv, hd = w.batch, w.nq, w.nkv, w.head_dim
-    scale = float(workloads.softmax_scale(hd))
-    t_setup = time.perf_counter()
-
-    # ---- cache: one pool per layer, blocks of every sequence scattered at random
-    table, nblocks = workloads.block_table(lens, kv_bs, w.seed)
-    table_t = torch.from_numpy(table).to(dev)
-    lens_t = torch.from_numpy(lens).to(dev)
-    batch = q8.make_batch(table_t, lens_t, int(lens.max()))
-    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev) for _ in range(layers)]
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    # history: every position but the last, appended from an N(0,1) source pool
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
-    src_k = torch.randn((POOL_TOKENS + FILL_CHUNK, nkv, hd), generator=gen, device=dev)
-    src_v = torch.randn((POOL_TOKENS + FILL_CHUNK, nkv, hd), generator=gen, device=dev)
-    hist_seq = np.concatenate([np.full(max(n - 1, 0), b, np.int32) for b, n in enumerate(lens)])
-    hist_pos = np.concatenate([np.arange(max(n - 1, 0), dtype=np.int32) for n in lens])
-    hist_seq_t = torch.from_numpy(hist_seq).to(dev)
-    hist_pos_t = torch.from_numpy(hist_pos).to(dev)
-    rng = np.random.default_rng(w.seed)
-    for li, pool in enumerate(pools):
-        for c0 in range(0, hist_seq.size, FILL_CHUNK):
-            c1 = min(hist_seq.size, c0 + FILL_CHUNK)
-            off = int(rng.integers(0, POOL_TOKENS))
-            q8.kv_append(pool, batch, hist_seq_t[c0:c1], hist_pos_t[c0:c1],
-                         src_k[off:off + c1 - c0], src_v[off:off + c1 - c0], dev_status=status)
-    del src_k, src_v
-
-    # the step's inputs: one new token per sequence (position n_b - 1) and q, per layer
-    step_seq = torch.arange(B, dtype=torch.int32, device=dev)
-    step_pos = (lens_t - 1).clamp(min=0).to(torch.int32)
-    new_k = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
-    new_v = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
-    qs = torch.randn((layers, B, nq, hd), generator=gen, device=dev)
-    outs = torch.empty((layers, B, nq, hd), dtype=torch.float32, device=dev)
-    nparts = args.nparts or q8.decode_attn_auto_parts(pools[0], batch, nq)
-    ws = torch.empty(q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status set during fill"
-    setup_s = time.perf_counter() - t_setup
-
-    def step_plain():
-        for li in range(layers):
-            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
-            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                   dev_status=status)
-            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                 dev_status=status)
-
-    # ---- timed region 1: whole steps (one HIP graph per step unless --eager)
-    graph = None
-    if not args.eager:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step_plain()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step_plain()
-    run = graph.replay if graph is not None else step_plain
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert int(status.item()) == 0, "device status set during timing"
-
-    # ---- timed region 2: eager launches with HIP events around each kernel on
-    # the stream the library launches on (the roofline's per-kernel durations)
-    stream = torch.cuda.current_stream()
-    ev_steps = max(2, min(args.steps, 5))
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ev_steps * layers)]
-    for s_ in range(ev_steps + 1):
-        for li in range(layers):
-            e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
-            if e: e[0].record(stream)
-            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
-            if e: e[1].record(stream)
-            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                   dev_status=status)
-            if e: e[2].record(stream)
-            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                 dev_status=status)
-            if e: e[3].record(stream)
-    torch.cuda.synchronize()
-    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
-    t_partial = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
-    t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
-    t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
-
-    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs)
+    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager)
+    lens = m["lens"]
+    B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
+    attn_b, app_b = m["attn_bytes"], m["append_bytes"]
     step_bytes = layers * (attn_b + app_b)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = m["ms_per_step"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    t_partial, t_merge, t_append, t_layer = m["t_partial"], m["t_merge"], m["t_append"], m["t_layer"]
 
     # dominant kernel: the decode partial kernel; its algorithmic bytes are the
     # attention bytes (the merge traffic is overhead and not counted)
@@ -268,9 +314,20 @@ def main():
                 "kernel": "q8_attn_partial_kernel", "kernel_us": round(part_us, 2),
                 "algorithmic_bytes_per_launch": int(attn_b)}
 
+    sweep = None
+    if not args.no_sweep:
+        sweep = []
+        for name in SWEEP:
+            if name == args.workload:
+                continue
+            ws_ = workloads.WORKLOADS[name]
+            sweep.append(sweep_entry(ws_, measure(torch, q8, dev, ws_, ws_.layers, 10, 2, 0, args.eager)))
+            torch.cuda.empty_cache()
+            print(f"[sweep] {name} done", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, lens, table, nblocks, attn_b)
+        cpu = cpu_baseline(w, lens, m["table"], m["nblocks"], attn_b)
 
     line = {
         "metric": "q8 decode-attn achieved HBM GB/s (% of peak) + us/layer-step, batch x ctx sweep",
@@ -279,15 +336,16 @@ def main():
         "vs_baseline": None, "dtype": "int8/fp32", "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
-            "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": nparts,
+            "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "us_per_layer_step": round(ms_per_step * 1e3 / layers, 2),
             "us_per_layer_step_eager_p10_p50_p90": [round(float(np.percentile(t_layer, q)), 2) for q in (10, 50, 90)],
             "us_append": round(float(np.median(t_append)), 2),
             "us_decode_partial": round(float(np.median(t_partial)), 2),
             "us_decode_merge": round(float(np.median(t_merge)), 2),
-            "graph": graph is not None,
-            "bytes_per_layer_step": int(attn_b + app_b), "setup_s": round(setup_s, 1),
+            "graph": m["graph"],
+            "bytes_per_layer_step": int(attn_b + app_b), "setup_s": round(m["setup_s"], 1),
+            "sweep": sweep,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

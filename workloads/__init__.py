@@ -161,6 +161,23 @@ def kv_chunk_torch(w: Workload, layer: int, b: int, chunk: int, which: int, devi
     return x
 
 
+def kv_pool_torch(w: Workload, n: int, gen, device):
+    """n rows [n, nkv, head_dim] fp32 with the workload's value distribution,
+    drawn from torch generator ``gen`` (bench.py appends cache history from
+    such a pool at random offsets)."""
+    import torch
+    shape = (n, w.nkv, w.head_dim)
+    if w.dist == "normal":
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    z = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    e = torch.randn((3,) + shape, generator=gen, device=device, dtype=torch.float32)
+    x = 3.0 * z / torch.sqrt((e * e).sum(0) / 3.0)
+    u = torch.rand(shape[:-1], generator=gen, device=device)
+    x = torch.where((u < 0.01)[..., None], x * 1e-7, x)
+    x = torch.where(((u >= 0.01) & (u < 0.012))[..., None], torch.zeros_like(x), x)
+    return x
+
+
 def kv_range_torch(w: Workload, layer: int, b: int, t0: int, t1: int, which: int, device):
     """Tokens [t0, t1) of sequence b, assembled from their chunks."""
     import torch
