@@ -66,6 +66,8 @@ def _load():
     lib.orc_qk_partials.argtypes = [I, I, I, I, I, P, I, P, I, I, P, P, P]
     lib.orc_qk_partials.restype = I
     lib.orc_single_pass.argtypes = [P, P, P, P, P, P, I64, I, F, P, P]
+    lib.orc_decode_attn_f32.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, P, I, P, I]
+    lib.orc_decode_attn_f32.restype = I
     lib.orc_num_threads_available.restype = I
     _lib = lib
     return lib
@@ -254,3 +256,65 @@ def build_cache(k: np.ndarray, v: np.ndarray, seq_lens, block_table, num_blocks:
         ks[blk, row] = dk
         vs[blk, row] = dv
     return Cache(kc, vc, ks, vs, block_table, seq_lens, nkv, hd)
+
+
+class MirrorCache:
+    """Host copy of one layer's fp32 mirror cache ("9-3" §3 closing note: the
+    write path also stores every new K/V row in a float cache) plus batch
+    metadata.
+
+    k_f32/v_f32: [num_blocks, kv_bs, nkv*hd] fp32 (the code layout, fp32 elements)
+    block_table: [batch, max_blocks_per_seq] int32; seq_lens: [batch] int32
+    """
+
+    def __init__(self, k_f32, v_f32, block_table, seq_lens, nkv, hd):
+        self.k_f32 = _c(k_f32, np.float32)
+        self.v_f32 = _c(v_f32, np.float32)
+        self.block_table = _c(block_table, np.int32)
+        self.seq_lens = _c(seq_lens, np.int32)
+        self.nkv, self.hd = int(nkv), int(hd)
+        self.num_blocks, self.kv_bs = self.k_f32.shape[0], self.k_f32.shape[1]
+        self.batch, self.max_blocks_per_seq = self.block_table.shape
+
+
+def decode_attn_f32(cache: MirrorCache, q: np.ndarray, nq: int, scale: float, rows_bh=None,
+                    nthreads: int = 0) -> np.ndarray:
+    """Exact decode attention over the fp32 mirror ("9-3" §1: scores of the
+    raw fp32 q and K, max-subtracted softmax, weighted raw V; three passes in
+    double).  Every (b, h) -> [batch, nq, hd], or the rows b * nq + h listed in
+    rows_bh -> [len(rows_bh), hd]."""
+    q = _c(q, np.float32)
+    nthreads = nthreads or threads_available()
+    if rows_bh is None:
+        out = np.empty((cache.batch, nq, cache.hd), np.float32)
+        rows_p, n_rows = None, cache.batch * nq
+    else:
+        rows = _c(np.asarray(rows_bh), np.int64)
+        out = np.empty((rows.size, cache.hd), np.float32)
+        rows_p, n_rows = _p(rows), rows.size
+    rc = _load().orc_decode_attn_f32(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
+                                     _p(cache.block_table), cache.max_blocks_per_seq,
+                                     _p(cache.seq_lens), cache.num_blocks,
+                                     _p(cache.k_f32), _p(cache.v_f32),
+                                     _p(q), float(np.float32(scale)), rows_p, n_rows, _p(out), nthreads)
+    if rc:
+        raise ValueError("oracle: bad sequence length or block id")
+    return out
+
+
+def build_mirror(k: np.ndarray, v: np.ndarray, seq_lens, block_table, num_blocks: int, kv_bs: int) -> MirrorCache:
+    """Scatter dense fp32 K/V ([batch, max_len, nkv, hd]) into a blocked fp32
+    mirror through ``block_table``; rows no token occupies stay zero."""
+    batch, _, nkv, hd = k.shape
+    kf = np.zeros((num_blocks, kv_bs, nkv * hd), np.float32)
+    vf = np.zeros_like(kf)
+    for b in range(batch):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        blk = np.asarray(block_table)[b, t // kv_bs]
+        row = t % kv_bs
+        kf[blk, row] = k[b, :n].reshape(n, nkv * hd)
+        vf[blk, row] = v[b, :n].reshape(n, nkv * hd)
+    return MirrorCache(kf, vf, block_table, seq_lens, nkv, hd)

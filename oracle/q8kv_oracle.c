@@ -275,6 +275,75 @@ int orc_decode_attn_rows(int nq, int nkv, int hd, int kv_bs,
     return status;
 }
 
+/* ------------------------------------------------------------ O10 ------- */
+/* The fp32 mirror cache and its exact attention ([9-3] §3 closing note: the
+ * engine also stores every new K/V row in a float cache, so quantized and
+ * exact attention coexist; [9-3] §1: the exact baseline is the standard
+ * attention over the raw fp32 K/V).  Mirror layout = the code layout with
+ * fp32 elements: [num_blocks][kv_bs][nkv * hd].  The query is used as given
+ * (no quantization); everything else as O5-O8: one (b, h) row, three passes
+ * in double, zeros for length 0, -1 on a bad length or block id. */
+static int orc_one_row_f32(int b, int h, int nq, int nkv, int hd, int kv_bs,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *seq_lens, int num_blocks,
+                           const float *k_f32, const float *v_f32,
+                           const float *q_row, float scale, float *o)
+{
+    int kh = h / (nq / nkv);
+    int64_t n = seq_lens[b];
+    for (int i = 0; i < hd; ++i) o[i] = 0.0f;
+    if (n < 0 || n > (int64_t)max_blocks_per_seq * kv_bs) return -1;
+    if (n == 0) return 0;
+    double *qh = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *kk = (double *)malloc(sizeof(double) * (size_t)(n * hd));
+    double *vv = (double *)malloc(sizeof(double) * (size_t)(n * hd));
+    double *oh = (double *)malloc(sizeof(double) * (size_t)hd);
+    for (int i = 0; i < hd; ++i) qh[i] = (double)q_row[i];
+    int rc = 0;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t r = orc_row_of(block_table, max_blocks_per_seq, b, t, kv_bs, num_blocks);
+        if (r < 0) { rc = -1; break; }
+        const float *kr = k_f32 + (r * nkv + kh) * hd;
+        const float *vr = v_f32 + (r * nkv + kh) * hd;
+        for (int i = 0; i < hd; ++i) {
+            kk[t * hd + i] = (double)kr[i];
+            vv[t * hd + i] = (double)vr[i];
+        }
+    }
+    if (rc == 0) {
+        orc_attend_dense(qh, kk, vv, n, hd, (double)scale, oh);
+        for (int i = 0; i < hd; ++i) o[i] = (float)oh[i];
+    }
+    free(qh); free(kk); free(vv); free(oh);
+    return rc;
+}
+
+/* Rows rows_bh[r] = b * nq + h of exact decode attention over the fp32
+ * mirror (rows_bh == NULL: every (b, h), r = b * nq + h).  out: [n_rows][hd]. */
+int orc_decode_attn_f32(int batch, int nq, int nkv, int hd, int kv_bs,
+                        const int32_t *block_table, int max_blocks_per_seq,
+                        const int32_t *seq_lens, int num_blocks,
+                        const float *k_f32, const float *v_f32,
+                        const float *q, float scale,
+                        const int64_t *rows_bh, int n_rows, float *out, int nthreads)
+{
+    int status = 0;
+    if (rows_bh == NULL) n_rows = batch * nq;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int r = 0; r < n_rows; ++r) {
+        int64_t bh = rows_bh ? rows_bh[r] : r;
+        int rc = orc_one_row_f32((int)(bh / nq), (int)(bh % nq), nq, nkv, hd, kv_bs,
+                                 block_table, max_blocks_per_seq, seq_lens, num_blocks,
+                                 k_f32, v_f32, q + bh * hd, scale, out + (int64_t)r * hd);
+        if (rc) {
+#pragma omp atomic write
+            status = -1;
+        }
+    }
+    return status;
+}
+
 /* Block partials of every visible token against every query head, over the
  * blocked cache: partials[b][h][t][blk] for t < seq_lens[b]; entries with
  * t >= seq_lens[b] (up to max_seq_len) are 0.  Returns 0, 1 if an int32
