@@ -38,7 +38,8 @@ class _Layer(ctypes.Structure):
     _fields_ = [("nkv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("kv_bs", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_f32", ctypes.c_void_p), ("v_f32", ctypes.c_void_p)]
 
 
 class _Batch(ctypes.Structure):
@@ -65,7 +66,7 @@ def _load():
     lib.q8_decode_attn_auto_parts.restype = I32
     lib.q8_decode_attn_workspace_bytes.argtypes = [LP, BP, I32, I32]
     lib.q8_decode_attn_workspace_bytes.restype = SZ
-    for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge"):
+    for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge", "q8_decode_attn_f32"):
         fn = getattr(lib, name)
         fn.argtypes = [LP, BP, I32, P, F, P, I32, P, SZ, P, P]
         fn.restype = I32
@@ -115,6 +116,7 @@ class KVLayer:
 
     k_codes/v_codes: int8 [num_blocks, kv_bs, nkv_heads * head_dim]
     k_scale/v_scale: fp32 [num_blocks, nkv_heads, kv_bs]
+    k_f32/v_f32:     fp32 [num_blocks, kv_bs, nkv_heads * head_dim] mirror, or None
     """
     k_codes: object
     v_codes: object
@@ -124,10 +126,13 @@ class KVLayer:
     kv_bs: int
     num_blocks: int
     head_dim: int = HEAD_DIM
+    k_f32: object = None
+    v_f32: object = None
 
     def c(self) -> _Layer:
         return _Layer(self.nkv_heads, self.head_dim, self.kv_bs, self.num_blocks,
-                      _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.v_scale))
+                      _ptr(self.k_codes), _ptr(self.v_codes), _ptr(self.k_scale), _ptr(self.v_scale),
+                      _ptr(self.k_f32), _ptr(self.v_f32))
 
 
 @dataclasses.dataclass
@@ -145,14 +150,21 @@ class Batch:
                       _ptr(self.block_table), _ptr(self.seq_lens))
 
 
-def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head_dim: int = HEAD_DIM) -> KVLayer:
-    """Allocate an uninitialised pool with torch (device memory only)."""
+def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head_dim: int = HEAD_DIM,
+                mirror: bool = False) -> KVLayer:
+    """Allocate an uninitialised pool with torch (device memory only); with
+    mirror=True also the fp32 mirror that q8_kv_append fills and
+    q8_decode_attn_f32 reads."""
     import torch
     kc = torch.empty((num_blocks, kv_bs, nkv_heads * head_dim), dtype=torch.int8, device=device)
     vc = torch.empty_like(kc)
     ks = torch.empty((num_blocks, nkv_heads, kv_bs), dtype=torch.float32, device=device)
     vs = torch.empty_like(ks)
-    return KVLayer(kc, vc, ks, vs, nkv_heads, kv_bs, num_blocks, head_dim)
+    kf = vf = None
+    if mirror:
+        kf = torch.empty((num_blocks, kv_bs, nkv_heads * head_dim), dtype=torch.float32, device=device)
+        vf = torch.empty_like(kf)
+    return KVLayer(kc, vc, ks, vs, nkv_heads, kv_bs, num_blocks, head_dim, kf, vf)
 
 
 def make_batch(block_table, seq_lens, max_seq_len: int) -> Batch:
@@ -188,6 +200,11 @@ def _decode(name, layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_
 def decode_attn(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
     """q8_decode_attn: out [batch, nq, 128] fp32 from q [batch, nq, 128] fp32."""
     _decode("q8_decode_attn", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def decode_attn_f32(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
+    """q8_decode_attn_f32: exact attention over the layer's fp32 mirror."""
+    _decode("q8_decode_attn_f32", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
 
 
 def decode_attn_partial(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):

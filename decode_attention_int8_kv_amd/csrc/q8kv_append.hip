@@ -20,6 +20,8 @@ struct AppendParams {
     int8_t *v_codes;
     float *k_scale;
     float *v_scale;
+    float *k_f32;          // fp32 mirror, or null
+    float *v_f32;
     const int32_t *block_table;
     const int32_t *seq_lens;
     const int32_t *tok_seq;
@@ -83,6 +85,10 @@ __global__ __launch_bounds__(64 * kAppendWaves) void q8_append_kernel(AppendPara
     const uint16_t vc = (uint16_t)((kv_code(v.x, vq.recip) & 0xff) | ((kv_code(v.y, vq.recip) & 0xff) << 8));
     *reinterpret_cast<uint16_t *>(p.k_codes + dst) = kc;
     *reinterpret_cast<uint16_t *>(p.v_codes + dst) = vc;
+    if (p.k_f32) {   // the fp32 mirror keeps the row unchanged
+        *reinterpret_cast<float2 *>(p.k_f32 + dst) = k;
+        *reinterpret_cast<float2 *>(p.v_f32 + dst) = v;
+    }
     if (lane == 0) {
         p.k_scale[sdst] = kq.step;
         p.v_scale[sdst] = vq.step;
@@ -98,6 +104,8 @@ hipError_t launch_append(const q8_kv_layer &layer, const q8_batch &batch, int32_
     p.v_codes = layer.v_codes;
     p.k_scale = layer.k_scale;
     p.v_scale = layer.v_scale;
+    p.k_f32 = layer.k_f32;
+    p.v_f32 = layer.v_f32;
     p.block_table = batch.block_table;
     p.seq_lens = batch.seq_lens;
     p.tok_seq = tok_seq;

@@ -24,72 +24,9 @@
 //   * A sequence cut by a range boundary leaves (M, S, acc) partial states
 //     in the workspace; the merge kernel combines them with the same rescale
 //     rule and divides once.  A sequence inside one range is finished in place.
-#include "q8kv_tile.hpp"
-#include "q8kv_internal.hpp"
+#include "q8kv_ranges.hpp"
 
 namespace q8kv {
-
-struct DecodeParams {
-    CacheView cache;
-    const int32_t *block_table;
-    const int32_t *seq_lens;
-    const float *q;
-    float *out;
-    int32_t *ws_prefix;   // [batch + 1] tile prefix over the batch
-    float2 *ws_ms;        // [nparts][2][nq] (M, S) of cut pieces
-    float *ws_acc;        // [nparts][2][nq][128] accumulators of cut pieces
-    int32_t *dev_status;
-    int32_t batch;
-    int32_t nq;
-    int32_t max_blocks_per_seq;
-    int32_t max_seq_len;
-    int32_t nparts;
-    int32_t head_groups;
-    float sc;             // softmax scale * log2(e)
-};
-
-__device__ __forceinline__ int part_start(int i, int total, int nparts)
-{
-    return (int)(((long long)i * total) / nparts);
-}
-
-// The range that holds tile x (0 <= x < total).
-__device__ __forceinline__ int part_of(int x, int total, int nparts)
-{
-    return (int)((((long long)x + 1) * nparts - 1) / total);
-}
-
-// Tile prefix over the batch into LDS: pref[b] = number of tiles of the
-// sequences before b.  A length outside [0, max_seq_len] counts as empty.
-__device__ void build_prefix(const DecodeParams &p, int *pref, bool report)
-{
-    for (int b = threadIdx.x; b < p.batch; b += blockDim.x) {
-        int n = p.seq_lens[b];
-        if (n < 0 || n > p.max_seq_len) {
-            if (report && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
-            n = 0;
-        }
-        pref[b + 1] = (n + kTile - 1) / kTile;
-    }
-    if (threadIdx.x == 0) pref[0] = 0;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int carry = 0;
-        for (int base = 1; base <= p.batch; base += 64) {
-            const int idx = base + lane;
-            int v = (idx <= p.batch) ? pref[idx] : 0;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int u = __shfl_up(v, off, 64);
-                if (lane >= off) v += u;
-            }
-            if (idx <= p.batch) pref[idx] = v + carry;
-            carry += __shfl(v, 63, 64);
-        }
-    }
-    __syncthreads();
-}
 
 // Register tiles per wave.  Two keep the memory system saturated here: a
 // third tile (room for it exists at two query heads per KV head) measured
@@ -312,58 +249,9 @@ template <int G, bool Big>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
     __shared__ int pref[kMaxBatch + 1];
-    const int part = blockIdx.x / p.head_groups;
-    const int hg = blockIdx.x - part * p.head_groups;
-    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int kh = hg * (int)(blockDim.x >> 6) + wave;
-
-    build_prefix(p, pref, blockIdx.x == 0);
-    if (blockIdx.x == 0)
-        for (int b = threadIdx.x; b <= p.batch; b += blockDim.x) p.ws_prefix[b] = pref[b];
-
-    const int total = pref[p.batch];
-    const int start = part_start(part, total, p.nparts);
-    const int end = part_start(part + 1, total, p.nparts);
-
-    if (kh < p.cache.nkv && start < end) {
-        // the sequence holding tile `start`: the largest b with pref[b] <= start
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pref[mid] <= start) lo = mid; else hi = mid - 1;
-        }
-        int b = uniform(lo);
-        int x = start;
-        while (x < end) {
-            while (pref[b + 1] <= x) ++b;
-            b = uniform(b);
-            const int a0 = uniform(pref[b]), e0 = uniform(pref[b + 1]);
-            const int x1 = min(end, e0);
-            const bool whole = (x == a0) && (x1 == e0);
-            const int slot = (x == start) ? 0 : 1;
-            int n = p.seq_lens[b];
-            n = uniform(n);
-            attend_piece<G, Big>(p, b, kh, lane, x - a0, x1 - a0, n, whole, part, slot);
-            x = x1;
-        }
-    }
-
-    // Zero the output rows of empty sequences whose tile position lies in
-    // this range (the last range also takes those at the very end).
-    if (hg == 0) {
-        int lo = 0, hi = p.batch;   // first b with pref[b] >= start
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (pref[mid] < start) lo = mid + 1; else hi = mid;
-        }
-        const bool last = (part == p.nparts - 1);
-        for (int b = lo; b < p.batch && (pref[b] < end || (last && pref[b] <= total)); ++b) {
-            if (pref[b + 1] != pref[b]) continue;
-            float4 *o = reinterpret_cast<float4 *>(p.out + (size_t)b * p.nq * kHeadDim);
-            for (int i = threadIdx.x; i < p.nq * (kHeadDim / 4); i += blockDim.x)
-                o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    walk_ranges(p, pref, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
+        attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
+    });
 }
 
 // ---------------------------------------------------------------- merge ----
@@ -531,9 +419,9 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     return pl;
 }
 
-hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
-                                 const float *q, float scale, float *out, const DecodePlan &plan,
-                                 void *workspace, int32_t *dev_status, hipStream_t stream)
+DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch, int nq, const float *q,
+                                float scale, float *out, const DecodePlan &plan, void *workspace,
+                                int32_t *dev_status)
 {
     DecodeParams p;
     p.cache.k_codes = layer.k_codes;
@@ -543,6 +431,8 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     p.cache.nkv = layer.nkv_heads;
     p.cache.kv_bs_log2 = ilog2(layer.kv_bs);
     p.cache.num_blocks = layer.num_blocks;
+    p.k_f32 = layer.k_f32;
+    p.v_f32 = layer.v_f32;
     p.block_table = batch.block_table;
     p.seq_lens = batch.seq_lens;
     p.q = q;
@@ -559,6 +449,14 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     p.nparts = plan.nparts;
     p.head_groups = plan.head_groups;
     p.sc = (float)((double)scale * 1.4426950408889634);
+    return p;
+}
+
+hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
+                                 const float *q, float scale, float *out, const DecodePlan &plan,
+                                 void *workspace, int32_t *dev_status, hipStream_t stream)
+{
+    DecodeParams p = fill_decode_params(layer, batch, nq, q, scale, out, plan, workspace, dev_status);
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
     const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile);
     void *args[] = {&p};

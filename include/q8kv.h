@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 1
+#define Q8KV_ABI_VERSION 2
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -74,7 +74,12 @@ typedef enum q8_status {
 #define Q8_DEV_BAD_TOKEN    0x4  /* append: tok_seq outside [0, batch) or tok_pos outside [0, seq_lens[seq]) */
 
 /* One layer's physical block pool (pointers to device memory).
- * Alignment: k_codes and v_codes 16 bytes, k_scale and v_scale 4 bytes. */
+ * Alignment: k_codes and v_codes 16 bytes, k_scale and v_scale 4 bytes.
+ * k_f32, v_f32: the optional fp32 mirror ("9-3 q8 KV 精度对照实验" §3,
+ * closing note: the write path also keeps every new K/V row in a float
+ * cache, so quantized and exact attention coexist) -- both NULL, or both
+ * fp32 [num_blocks][kv_bs][nkv_heads * head_dim] (the code layout with fp32
+ * elements), 16-byte aligned. */
 typedef struct q8_kv_layer {
     int32_t nkv_heads;
     int32_t head_dim;
@@ -84,6 +89,8 @@ typedef struct q8_kv_layer {
     int8_t *v_codes;
     float *k_scale;
     float *v_scale;
+    float *k_f32;
+    float *v_f32;
 } q8_kv_layer;
 
 /* Per-step batch metadata, shared by all layers.  batch, max_blocks_per_seq
@@ -105,7 +112,8 @@ typedef struct q8_batch {
  * from zero; writes the codes and d at sequence tok_seq[j], position
  * tok_pos[j] of the cache.  tok_seq, tok_pos: device int32 [n_tokens];
  * k_new, v_new: device fp32 [n_tokens][nkv_heads][head_dim], 16-byte
- * aligned.  n_tokens == 0 is a no-op.  Positions must lie inside
+ * aligned.  When the layer has an fp32 mirror, the rows are also written
+ * there unchanged.  n_tokens == 0 is a no-op.  Positions must lie inside
  * [0, seq_lens[seq]); a decode step appends tok_pos = seq_lens - 1 and then
  * calls q8_decode_attn.  Two tokens with the same (seq, pos) race. */
 q8_status q8_kv_append(const q8_kv_layer *layer, const q8_batch *batch,
@@ -155,6 +163,19 @@ q8_status q8_decode_attn_merge(const q8_kv_layer *layer, const q8_batch *batch, 
                                const float *q, float scale, float *out, int32_t nparts,
                                void *workspace, size_t workspace_bytes,
                                int32_t *dev_status, void *stream);
+
+/* Exact decode attention over the layer's fp32 mirror ("9-3" §1: scores of
+ * the raw fp32 q and K, max-subtracted softmax, weighted raw V), for every
+ * sequence b and query head h:
+ *   out[b][h] = sum_t softmax_t(s) * v_t,  s_t = scale * <q, k_t>,
+ * in fp32 with an online softmax, over t < seq_lens[b].  Same batch, head
+ * map, range cut, merge, workspace (q8_decode_attn_workspace_bytes), length-0
+ * and error behaviour as q8_decode_attn.  Q8_EINVAL if the layer has no
+ * fp32 mirror. */
+q8_status q8_decode_attn_f32(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                             const float *q, float scale, float *out, int32_t nparts,
+                             void *workspace, size_t workspace_bytes,
+                             int32_t *dev_status, void *stream);
 
 /* Test hook: the Q quantizer of the decode kernel ("9-2" §2 segment 1) on
  * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1

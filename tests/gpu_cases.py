@@ -30,13 +30,13 @@ def say(*a):
 class DeviceCache:
     """One layer on the GPU plus its batch metadata."""
 
-    def __init__(self, lens, nkv, kv_bs, seed, spare=2, device="cuda", garbage=True):
+    def __init__(self, lens, nkv, kv_bs, seed, spare=2, device="cuda", garbage=True, mirror=False):
         t = torch()
         m = q8()
         self.lens = np.asarray(lens, np.int32)
         self.nkv, self.kv_bs = nkv, kv_bs
         self.table, self.num_blocks = workloads.block_table(self.lens, kv_bs, seed, spare_blocks=spare)
-        self.layer = m.alloc_layer(self.num_blocks, kv_bs, nkv, device)
+        self.layer = m.alloc_layer(self.num_blocks, kv_bs, nkv, device, mirror=mirror)
         if garbage:
             # rows no token occupies hold junk codes and NaN scales: masking must ignore them
             g = t.Generator(device=device)
@@ -47,6 +47,9 @@ class DeviceCache:
                                                dtype=t.int8))
             self.layer.k_scale.fill_(float("nan"))
             self.layer.v_scale.fill_(float("nan"))
+            if mirror:
+                self.layer.k_f32.fill_(float("nan"))
+                self.layer.v_f32.fill_(float("nan"))
         self.table_t = t.from_numpy(self.table).to(device)
         self.lens_t = t.from_numpy(self.lens).to(device)
         self.max_seq_len = int(max(1, self.lens.max()))
@@ -82,6 +85,24 @@ class DeviceCache:
         vs = np.ascontiguousarray(L.v_scale.cpu().numpy().transpose(0, 2, 1))
         return oracle.Cache(L.k_codes.cpu().numpy(), L.v_codes.cpu().numpy(), ks, vs,
                             self.table, self.lens, self.nkv, 128)
+
+    def host_mirror(self):
+        """The fp32 mirror as an oracle.MirrorCache (copied back)."""
+        L = self.layer
+        return oracle.MirrorCache(L.k_f32.cpu().numpy(), L.v_f32.cpu().numpy(), self.table, self.lens,
+                                  self.nkv, 128)
+
+    def decode_f32(self, q, nq, scale, nparts=0, out=None):
+        t = torch()
+        m = q8()
+        dev = self.layer.k_codes.device
+        qd = q if isinstance(q, t.Tensor) else t.from_numpy(np.ascontiguousarray(q, np.float32)).to(dev)
+        if out is None:
+            out = t.full((self.batch.batch, nq, 128), float("nan"), dtype=t.float32, device=dev)
+        nbytes = m.decode_attn_workspace_bytes(self.layer, self.batch, nq, nparts)
+        ws = t.empty(nbytes, dtype=t.uint8, device=dev)
+        m.decode_attn_f32(self.layer, self.batch, nq, qd, scale, out, ws, nparts=nparts, dev_status=self.status)
+        return out
 
     def decode(self, q, nq, scale, nparts=0, out=None):
         t = torch()

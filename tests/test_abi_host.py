@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 1
+    assert q8.abi_version() == 2
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
@@ -101,6 +101,26 @@ def test_append_argument_validation(q8):
     assert call_append(q8, L, B, n=-1) == -1
     assert call_append(q8, L, B, tok_seq=0) == -1
     assert call_append(q8, L, B, k_new=FAKE + 4) == -1  # 16-byte alignment
+
+
+def call_decode_f32(q8, L, B, nq=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, nparts=4):
+    return q8.lib().q8_decode_attn_f32(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, q, 0.088, out, nparts,
+                                       ws, ws_bytes, None, None)
+
+
+def test_mirror_validation(q8):
+    B = batch(q8)
+    # the fp32 mirror is all or nothing, 16-byte aligned
+    assert call_append(q8, layer(q8, k_f32=FAKE), B) == -1
+    assert call_append(q8, layer(q8, v_f32=FAKE), B) == -1
+    assert call_append(q8, layer(q8, k_f32=FAKE + 4, v_f32=FAKE), B) == -1
+    assert call_decode(q8, layer(q8, k_f32=FAKE, v_f32=FAKE + 8), B) == -1
+    # exact decode needs the mirror; otherwise it validates like q8_decode_attn
+    assert call_decode_f32(q8, layer(q8), B) == -1
+    L = layer(q8, k_f32=FAKE, v_f32=FAKE)
+    assert call_decode_f32(q8, L, B, nq=24) == -2
+    assert call_decode_f32(q8, L, B, ws=0) == -3
+    assert call_decode_f32(q8, L, B, ws_bytes=q8.decode_attn_workspace_bytes(L, B, 16, 4) - 1) == -3
 
 
 def test_decode_argument_validation(q8):
