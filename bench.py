@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("q8", "f32"), default="q8",
+                    help="q8: the q8 cache (default); f32: the fp32 mirror and its exact decode "
+                         "(the append then writes the mirror too)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -54,18 +57,23 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int):
+def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int, path: str = "q8"):
     """Bytes one layer-step must move at least once.
-    attention: K and V codes and scales of every visible token, read once per
-    KV head (n * nkv * (2*128 + 8)); q in and out (B*nq*128*4*2); block-table
-    entries and lengths.  append: fp32 K and V in (T*nkv*128*4*2), codes and
-    scales out (T*nkv*(2*128 + 8)), token indices (T*8)."""
+    q8 attention: K and V codes and scales of every visible token, read once
+    per KV head (n * nkv * (2*128 + 8)); f32 attention: the fp32 mirror rows
+    instead (n * nkv * 2*128*4).  Both: q in and out (B*nq*128*4*2), block-
+    table entries and lengths.  append: fp32 K and V in (T*nkv*128*4*2),
+    codes and scales out (T*nkv*(2*128 + 8)), with the mirror also the fp32
+    rows out (T*nkv*128*4*2), token indices (T*8)."""
     n = lens.astype(np.int64)
-    kv = int(n.sum()) * w.nkv * (2 * w.head_dim + 8)
+    per_tok = 2 * w.head_dim * 4 if path == "f32" else 2 * w.head_dim + 8
+    kv = int(n.sum()) * w.nkv * per_tok
     qo = w.batch * w.nq * w.head_dim * 4 * 2
     meta = int(((n + kv_bs - 1) // kv_bs).sum()) * 4 + w.batch * 4
     t = w.batch * w.append_per_step
     app = t * w.nkv * w.head_dim * 4 * 2 + t * w.nkv * (2 * w.head_dim + 8) + t * 8
+    if path == "f32":
+        app += t * w.nkv * w.head_dim * 4 * 2
     return kv + qo + meta, app
 
 
@@ -139,7 +147,7 @@ SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n405
          "qwen8b_b32_n32k", "qwen8b_b1_n128k", "qwen8b_b128_stress")
 
 
-def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False):
+def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8"):
     """One workload: fill `layers` cache pools, then time whole decode steps
     (graph replay unless eager) and, in an eager pass with HIP events on the
     library's stream, each kernel.  Returns a dict of figures."""
@@ -154,8 +162,9 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False)
     table_t = torch.from_numpy(table).to(dev)
     lens_t = torch.from_numpy(lens).to(dev)
     batch = q8.make_batch(table_t, lens_t, int(max(1, lens.max())))
-    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev) for _ in range(layers)]
+    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev, mirror=(path == "f32")) for _ in range(layers)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    partial = q8.decode_attn_f32_partial if path == "f32" else q8.decode_attn_partial
 
     # history: every position but the last, appended from a source pool drawn
     # with the workload's value distribution
@@ -192,8 +201,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False)
     def step_plain():
         for li in range(layers):
             q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
-            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                   dev_status=status)
+            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
                                  dev_status=status)
 
@@ -230,8 +238,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False)
             if e: e[0].record(stream)
             q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
             if e: e[1].record(stream)
-            q8.decode_attn_partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                   dev_status=status)
+            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             if e: e[2].record(stream)
             q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
                                  dev_status=status)
@@ -242,7 +249,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False)
     t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
     t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
 
-    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs)
+    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs, path)
     ms_per_step = wall * 1e3 / steps
     del pools, outs, qs, new_k, new_v, ws
     return {
@@ -290,7 +297,7 @@ def main():
         return
     w = workloads.WORKLOADS[args.workload]
     layers = args.layers or w.layers
-    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager)
+    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path)
     lens = m["lens"]
     B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
     attn_b, app_b = m["attn_bytes"], m["append_bytes"]
@@ -304,18 +311,19 @@ def main():
     part_us = float(t_partial.mean())
     achieved = attn_b / (part_us * 1e-6) / 1e9
     traffic = None
-    if os.path.exists(args.traffic):
+    if os.path.exists(args.traffic) and args.path == "q8":
         with open(args.traffic) as f:
             tr = json.load(f).get(args.workload)
         if tr and tr.get("kernel_hash") == kernel_hash():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "q8_attn_partial_kernel", "kernel_us": round(part_us, 2),
+                "kernel": "q8_attn_f32_partial_kernel" if args.path == "f32" else "q8_attn_partial_kernel",
+                "kernel_us": round(part_us, 2),
                 "algorithmic_bytes_per_launch": int(attn_b)}
 
     sweep = None
-    if not args.no_sweep:
+    if not args.no_sweep and args.path == "q8":
         sweep = []
         for name in SWEEP:
             if name == args.workload:
@@ -326,16 +334,17 @@ def main():
             print(f"[sweep] {name} done", file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.path == "q8":
         cpu = cpu_baseline(w, lens, m["table"], m["nblocks"], attn_b)
 
     line = {
         "metric": "q8 decode-attn achieved HBM GB/s (% of peak) + us/layer-step, batch x ctx sweep",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8/fp32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp32" if args.path == "f32" else "int8/fp32", "data": "synthetic",
         "config": {
-            "workload": w.name, "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
+            "workload": w.name, "path": args.path,
+            "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "us_per_layer_step": round(ms_per_step * 1e3 / layers, 2),

@@ -66,7 +66,8 @@ def _load():
     lib.q8_decode_attn_auto_parts.restype = I32
     lib.q8_decode_attn_workspace_bytes.argtypes = [LP, BP, I32, I32]
     lib.q8_decode_attn_workspace_bytes.restype = SZ
-    for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge", "q8_decode_attn_f32"):
+    for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge", "q8_decode_attn_f32",
+                 "q8_decode_attn_f32_partial"):
         fn = getattr(lib, name)
         fn.argtypes = [LP, BP, I32, P, F, P, I32, P, SZ, P, P]
         fn.restype = I32
@@ -205,6 +206,12 @@ def decode_attn(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_
 def decode_attn_f32(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
     """q8_decode_attn_f32: exact attention over the layer's fp32 mirror."""
     _decode("q8_decode_attn_f32", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def decode_attn_f32_partial(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None,
+                            stream=None):
+    _decode("q8_decode_attn_f32_partial", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status,
+            stream)
 
 
 def decode_attn_partial(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):

@@ -157,21 +157,30 @@ q8_status q8_decode_attn(const q8_kv_layer *layer, const q8_batch *batch, int32_
                                 workspace_bytes, dev_status, stream);
 }
 
-q8_status q8_decode_attn_f32(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
-                             const float *q, float scale, float *out, int32_t nparts, void *workspace,
-                             size_t workspace_bytes, int32_t *dev_status, void *stream)
+q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                     const float *q, float scale, float *out, int32_t nparts,
+                                     void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                                     void *stream)
 {
     q8kv::DecodePlan plan;
     q8_status s = check_decode(layer, batch, nq_heads, q, out, nparts, workspace, workspace_bytes, &plan);
     if (s != Q8_OK) return s;
     if (!layer->k_f32) return Q8_EINVAL;
     if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = q8kv::launch_decode_partial_f32(*layer, *batch, nq_heads, q, scale, out, plan, workspace,
-                                                   dev_status, st);
-    if (e != hipSuccess) return hip_fail(e, "q8_decode_attn_f32");
-    e = q8kv::launch_decode_merge(*layer, *batch, nq_heads, out, plan, workspace, st);
-    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_attn_f32");
+                                                   dev_status, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_attn_f32_partial");
+}
+
+q8_status q8_decode_attn_f32(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                             const float *q, float scale, float *out, int32_t nparts, void *workspace,
+                             size_t workspace_bytes, int32_t *dev_status, void *stream)
+{
+    q8_status s = q8_decode_attn_f32_partial(layer, batch, nq_heads, q, scale, out, nparts, workspace,
+                                             workspace_bytes, dev_status, stream);
+    if (s != Q8_OK) return s;
+    return q8_decode_attn_merge(layer, batch, nq_heads, q, scale, out, nparts, workspace, workspace_bytes,
+                                dev_status, stream);
 }
 
 q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int8_t *codes, float *qscale,

@@ -177,6 +177,14 @@ q8_status q8_decode_attn_f32(const q8_kv_layer *layer, const q8_batch *batch, in
                              void *workspace, size_t workspace_bytes,
                              int32_t *dev_status, void *stream);
 
+/* The exact decode's cache walk alone: _f32_partial followed by
+ * q8_decode_attn_merge with identical arguments is exactly
+ * q8_decode_attn_f32 (both paths leave the same partial-state records). */
+q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                     const float *q, float scale, float *out, int32_t nparts,
+                                     void *workspace, size_t workspace_bytes,
+                                     int32_t *dev_status, void *stream);
+
 /* Test hook: the Q quantizer of the decode kernel ("9-2" §2 segment 1) on
  * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1
  * when m < 1e-6), qscale = m * fl(1/127), r = 127 / m,

@@ -147,3 +147,20 @@ def test_f32_graph_replays_match_eager():
         t.cuda.synchronize()
         assert t.equal(out, eager), f"replay {i}"
     assert dc.status_word() == 0
+
+
+def test_f32_phase_entry_points_equal_one_call():
+    t = torch()
+    m = q8()
+    say("[mirror] f32 partial + merge == f32 decode")
+    lens = np.array([1000, 70, 3], np.int32)
+    k, v = dense_kv(lens, 8, seed=2006)
+    q = t.from_numpy(np.random.default_rng(2006).standard_normal((3, 16, 128)).astype(np.float32)).cuda()
+    dc = DeviceCache(lens, 8, 32, seed=2006, mirror=True)
+    dc.append_dense(k, v)
+    one = dc.decode_f32(q, 16, SCALE, nparts=9)
+    ws = t.empty(m.decode_attn_workspace_bytes(dc.layer, dc.batch, 16, 9), dtype=t.uint8, device="cuda")
+    out = t.empty_like(one)
+    m.decode_attn_f32_partial(dc.layer, dc.batch, 16, q, SCALE, out, ws, nparts=9)
+    m.decode_attn_merge(dc.layer, dc.batch, 16, q, SCALE, out, ws, nparts=9)
+    assert t.equal(out, one)
