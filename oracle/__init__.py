@@ -68,6 +68,10 @@ def _load():
     lib.orc_single_pass.argtypes = [P, P, P, P, P, P, I64, I, F, P, P]
     lib.orc_decode_attn_f32.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, P, I, P, I]
     lib.orc_decode_attn_f32.restype = I
+    lib.orc_decode_attn_sparse.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, P, P, F, I, P, P, I]
+    lib.orc_decode_attn_sparse.restype = I
+    lib.orc_sparse_scores.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, I, P]
+    lib.orc_sparse_scores.restype = I
     lib.orc_num_threads_available.restype = I
     _lib = lib
     return lib
@@ -318,3 +322,45 @@ def build_mirror(k: np.ndarray, v: np.ndarray, seq_lens, block_table, num_blocks
         kf[blk, row] = k[b, :n].reshape(n, nkv * hd)
         vf[blk, row] = v[b, :n].reshape(n, nkv * hd)
     return MirrorCache(kf, vf, block_table, seq_lens, nkv, hd)
+
+
+SPARSE_BLOCK = 32     # positions per sparse block ("10-1" §2 defaults)
+SPARSE_PROBES = 8     # probe samples per block
+
+
+def decode_attn_sparse(cache: Cache, q: np.ndarray, nq: int, scale: float, topk: int = 32, nthreads: int = 0):
+    """Block-sparse decode ("10-1" §1-§2): per (b, h) the top-k 32-token blocks
+    by probe score, then exact attention over their tokens.  Returns
+    (out [batch, nq, hd] fp32, selected [batch, nq, topk] int32 block indices
+    ascending, -1 after the last)."""
+    if topk < 2:
+        raise ValueError("topk must be at least 2 (two blocks are always kept below the sparse gate)")
+    q = _c(q, np.float32)
+    out = np.empty(q.shape, np.float32)
+    sel = np.empty((cache.batch, nq, topk), np.int32)
+    nthreads = nthreads or threads_available()
+    rc = _load().orc_decode_attn_sparse(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
+                                        _p(cache.block_table), cache.max_blocks_per_seq,
+                                        _p(cache.seq_lens), cache.num_blocks,
+                                        _p(cache.k_codes), _p(cache.v_codes),
+                                        _p(cache.k_step), _p(cache.v_step),
+                                        _p(q), float(np.float32(scale)), int(topk), _p(out), _p(sel), nthreads)
+    if rc:
+        raise ValueError("oracle: bad sequence length or block id")
+    return out, sel
+
+
+def sparse_scores(cache: Cache, q: np.ndarray, nq: int, scale: float) -> np.ndarray:
+    """Probe score of every 32-token block of every (b, h) -> [batch, nq,
+    max blocks] fp32, -inf past a sequence's last block."""
+    q = _c(q, np.float32)
+    max_nb = max(1, (int(cache.seq_lens.max()) + SPARSE_BLOCK - 1) // SPARSE_BLOCK)
+    out = np.empty((cache.batch, nq, max_nb), np.float32)
+    rc = _load().orc_sparse_scores(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
+                                   _p(cache.block_table), cache.max_blocks_per_seq,
+                                   _p(cache.seq_lens), cache.num_blocks,
+                                   _p(cache.k_codes), _p(cache.k_step),
+                                   _p(q), float(np.float32(scale)), max_nb, _p(out))
+    if rc:
+        raise ValueError("oracle: bad sequence length or block id")
+    return out
