@@ -71,6 +71,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = [LP, BP, I32, P, F, P, I32, P, SZ, P, P]
         fn.restype = I32
+    lib.q8_decode_attn_sparse_workspace_bytes.argtypes = [LP, BP, I32, I32]
+    lib.q8_decode_attn_sparse_workspace_bytes.restype = SZ
+    lib.q8_decode_attn_sparse.argtypes = [LP, BP, I32, P, F, P, I32, P, P, SZ, P, P]
+    lib.q8_decode_attn_sparse.restype = I32
     lib.q8_quantize_q.argtypes = [P, I32, I32, P, P, P]
     lib.q8_quantize_q.restype = I32
     lib.q8_qk_block_partials.argtypes = [LP, BP, I32, P, P, P, P]
@@ -220,6 +224,22 @@ def decode_attn_partial(layer, batch, nq_heads, q, scale, out, workspace, nparts
 
 def decode_attn_merge(layer, batch, nq_heads, q, scale, out, workspace, nparts=0, dev_status=None, stream=None):
     _decode("q8_decode_attn_merge", layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream)
+
+
+def decode_attn_sparse_workspace_bytes(layer, batch, nq_heads: int, topk: int = 32) -> int:
+    return int(_load().q8_decode_attn_sparse_workspace_bytes(ctypes.byref(layer.c()), ctypes.byref(batch.c()),
+                                                             nq_heads, topk))
+
+
+def decode_attn_sparse(layer, batch, nq_heads, q, scale, out, workspace, topk=32, selected=None, dev_status=None,
+                       stream=None):
+    """q8_decode_attn_sparse: top-k 32-token blocks per query head by probe,
+    exact q8 attention over them.  selected: optional int32 [batch, nq, topk]."""
+    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    st = _load().q8_decode_attn_sparse(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q),
+                                       float(scale), _ptr(out), int(topk), _ptr(selected), _ptr(workspace),
+                                       ws_bytes, _ptr(dev_status), _stream(stream))
+    _check(st, "q8_decode_attn_sparse")
 
 
 def quantize_q(q, codes, qscale, stream=None):

@@ -183,6 +183,35 @@ q8_status q8_decode_attn_f32(const q8_kv_layer *layer, const q8_batch *batch, in
                                 dev_status, stream);
 }
 
+size_t q8_decode_attn_sparse_workspace_bytes(const q8_kv_layer *layer, const q8_batch *batch,
+                                             int32_t nq_heads, int32_t topk)
+{
+    if (check_layer(layer) != Q8_OK || check_batch(batch, layer) != Q8_OK ||
+        check_heads(layer, nq_heads) != Q8_OK || topk < 2 || topk > 64)
+        return 0;
+    return q8kv::sparse_workspace_bytes(*batch, nq_heads);
+}
+
+q8_status q8_decode_attn_sparse(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                const float *q, float scale, float *out, int32_t topk, int32_t *selected,
+                                void *workspace, size_t workspace_bytes, int32_t *dev_status, void *stream)
+{
+    q8_status s;
+    if ((s = check_layer(layer)) != Q8_OK) return s;
+    if ((s = check_batch(batch, layer)) != Q8_OK) return s;
+    if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
+    if (topk < 2 || topk > 64) return Q8_EINVAL;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return Q8_EINVAL;
+    if (selected && !aligned(selected, 4)) return Q8_EINVAL;
+    if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
+    if ((long long)batch->batch * nq_heads > 0x7fffffffLL) return Q8_EUNSUPPORTED;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < q8kv::sparse_workspace_bytes(*batch, nq_heads))
+        return Q8_EWORKSPACE;
+    hipError_t e = q8kv::launch_sparse(*layer, *batch, nq_heads, q, scale, out, topk, selected, workspace,
+                                       dev_status, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_attn_sparse");
+}
+
 q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int8_t *codes, float *qscale,
                         void *stream)
 {

@@ -41,6 +41,11 @@ hipError_t launch_decode_partial_f32(const q8_kv_layer &layer, const q8_batch &b
                                      const float *q, float scale, float *out, const DecodePlan &plan,
                                      void *workspace, int32_t *dev_status, hipStream_t stream);
 
+size_t sparse_workspace_bytes(const q8_batch &batch, int nq);
+hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq, const float *q, float scale,
+                         float *out, int topk, int32_t *selected, void *workspace, int32_t *dev_status,
+                         hipStream_t stream);
+
 hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,
                                const DecodePlan &plan, void *workspace, hipStream_t stream);
 

@@ -185,6 +185,26 @@ q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *b
                                      void *workspace, size_t workspace_bytes,
                                      int32_t *dev_status, void *stream);
 
+/* Block-sparse decode ("why long context must be sparse" §1-§2): per
+ * sequence b and query head h, the history is cut into 32-token blocks; each
+ * block is probed at its rows 0, 4, ..., 28 and scored by the largest q8
+ * attention score among them (the decode's fp32 score formula); the `topk`
+ * highest-scoring blocks (ties: lower block index) are kept, and out[b][h]
+ * is the exact q8 single-pass attention ("9-2" §2) over the tokens of those
+ * blocks.  A sequence of at most topk blocks keeps every block (the result
+ * is then the full attention of q8_decode_attn up to rounding order).
+ * topk in [2, 64] (the pages' default is 32).  selected: NULL, or device
+ * int32 [batch][nq_heads][topk] receiving the kept block indices in
+ * ascending order, -1 after the last.  workspace: at least
+ * q8_decode_attn_sparse_workspace_bytes() bytes, 256-byte aligned, any
+ * contents.  Errors as q8_decode_attn. */
+size_t q8_decode_attn_sparse_workspace_bytes(const q8_kv_layer *layer, const q8_batch *batch,
+                                             int32_t nq_heads, int32_t topk);
+q8_status q8_decode_attn_sparse(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                const float *q, float scale, float *out, int32_t topk,
+                                int32_t *selected, void *workspace, size_t workspace_bytes,
+                                int32_t *dev_status, void *stream);
+
 /* Test hook: the Q quantizer of the decode kernel ("9-2" §2 segment 1) on
  * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1
  * when m < 1e-6), qscale = m * fl(1/127), r = 127 / m,

@@ -166,3 +166,23 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         m.lib()
+
+
+def call_sparse(q8, L, B, nq=16, topk=32, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, sel=None):
+    return q8.lib().q8_decode_attn_sparse(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, q, 0.088, out, topk, sel,
+                                          ws, ws_bytes, None, None)
+
+
+def test_sparse_validation(q8):
+    L, B = layer(q8), batch(q8)
+    assert call_sparse(q8, L, B, topk=1) == -1
+    assert call_sparse(q8, L, B, topk=65) == -1
+    assert call_sparse(q8, L, B, nq=24) == -2
+    assert call_sparse(q8, L, B, q=FAKE + 4) == -1
+    assert call_sparse(q8, L, B, sel=FAKE + 2) == -1
+    assert call_sparse(q8, L, B, ws=0) == -3
+    need = q8.decode_attn_sparse_workspace_bytes(L, B, 16, 32)
+    # one fp32 score per (sequence, query head, 32-token block)
+    assert need >= 4 * 16 * ((300 + 31) // 32) * 4
+    assert call_sparse(q8, L, B, ws_bytes=need - 1) == -3
+    assert q8.decode_attn_sparse_workspace_bytes(L, B, 16, 1) == 0
