@@ -40,9 +40,11 @@ def parse():
     ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("q8", "f32"), default="q8",
+    ap.add_argument("--path", choices=("q8", "f32", "sparse"), default="q8",
                     help="q8: the q8 cache (default); f32: the fp32 mirror and its exact decode "
-                         "(the append then writes the mirror too)")
+                         "(the append then writes the mirror too); sparse: block-sparse decode (top-k "
+                         "32-token blocks per query head by probe)")
+    ap.add_argument("--topk", type=int, default=32, help="blocks kept per query head (--path sparse)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -57,17 +59,28 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int, path: str = "q8"):
+def algorithmic_bytes(w: workloads.Workload, lens: np.ndarray, kv_bs: int, path: str = "q8", topk: int = 32):
     """Bytes one layer-step must move at least once.
     q8 attention: K and V codes and scales of every visible token, read once
     per KV head (n * nkv * (2*128 + 8)); f32 attention: the fp32 mirror rows
-    instead (n * nkv * 2*128*4).  Both: q in and out (B*nq*128*4*2), block-
+    instead (n * nkv * 2*128*4); sparse attention: the probe rows' K codes
+    and scales per KV head plus the kept blocks' K and V codes and scales per
+    query head (a kept block counted as 32 tokens).  Both: q in and out (B*nq*128*4*2), block-
     table entries and lengths.  append: fp32 K and V in (T*nkv*128*4*2),
     codes and scales out (T*nkv*(2*128 + 8)), with the mirror also the fp32
     rows out (T*nkv*128*4*2), token indices (T*8)."""
     n = lens.astype(np.int64)
     per_tok = 2 * w.head_dim * 4 if path == "f32" else 2 * w.head_dim + 8
     kv = int(n.sum()) * w.nkv * per_tok
+    if path == "sparse":
+        # probe: K codes and scale of rows 0, 4, ..., 28 of every block of a
+        # probed sequence, once per KV head; attention: every token of the kept
+        # blocks, K and V codes and scales, once per query head
+        nb = (n + 31) // 32
+        probed = nb > topk
+        probe_rows = int(np.minimum((n - 32 * (nb - 1) + 3) // 4, 8)[probed].sum() + (8 * (nb[probed] - 1)).sum())
+        kept = np.where(probed, 32 * topk, n)
+        kv = probe_rows * w.nkv * (w.head_dim + 4) + int(kept.sum()) * w.nq * (2 * w.head_dim + 8)
     qo = w.batch * w.nq * w.head_dim * 4 * 2
     meta = int(((n + kv_bs - 1) // kv_bs).sum()) * 4 + w.batch * 4
     t = w.batch * w.append_per_step
@@ -147,7 +160,7 @@ SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n405
          "qwen8b_b32_n32k", "qwen8b_b1_n128k", "qwen8b_b128_stress")
 
 
-def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8"):
+def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8", topk=32):
     """One workload: fill `layers` cache pools, then time whole decode steps
     (graph replay unless eager) and, in an eager pass with HIP events on the
     library's stream, each kernel.  Returns a dict of figures."""
@@ -165,6 +178,14 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev, mirror=(path == "f32")) for _ in range(layers)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     partial = q8.decode_attn_f32_partial if path == "f32" else q8.decode_attn_partial
+    merge = q8.decode_attn_merge
+    if path == "sparse":
+        # the whole sparse decode (probe + attend kernels) in the partial slot; no merge
+        def partial(pool, batch_, nq_, q_, scale_, out_, ws_, nparts=0, dev_status=None):
+            q8.decode_attn_sparse(pool, batch_, nq_, q_, scale_, out_, ws_, topk=topk, dev_status=dev_status)
+
+        def merge(*a, **k):
+            pass
 
     # history: every position but the last, appended from a source pool drawn
     # with the workload's value distribution
@@ -193,7 +214,10 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     qs = torch.randn((layers, B, nq, hd), generator=gen, device=dev)
     outs = torch.empty((layers, B, nq, hd), dtype=torch.float32, device=dev)
     nparts = nparts_arg or q8.decode_attn_auto_parts(pools[0], batch, nq)
-    ws = torch.empty(q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
+    ws_bytes = q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts)
+    if path == "sparse":
+        ws_bytes = max(ws_bytes, q8.decode_attn_sparse_workspace_bytes(pools[0], batch, nq, topk))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set during fill"
     setup_s = time.perf_counter() - t_setup
@@ -202,8 +226,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         for li in range(layers):
             q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
             partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
-            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                 dev_status=status)
+            merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
 
     # ---- timed region 1: whole steps (one HIP graph per step unless eager)
     graph = None
@@ -240,8 +263,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
             if e: e[1].record(stream)
             partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             if e: e[2].record(stream)
-            q8.decode_attn_merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts,
-                                 dev_status=status)
+            merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             if e: e[3].record(stream)
     torch.cuda.synchronize()
     t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
@@ -249,7 +271,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     t_merge = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
     t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
 
-    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs, path)
+    attn_b, app_b = algorithmic_bytes(w, lens, kv_bs, path, topk)
     ms_per_step = wall * 1e3 / steps
     del pools, outs, qs, new_k, new_v, ws
     return {
@@ -297,7 +319,7 @@ def main():
         return
     w = workloads.WORKLOADS[args.workload]
     layers = args.layers or w.layers
-    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path)
+    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk)
     lens = m["lens"]
     B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
     attn_b, app_b = m["attn_bytes"], m["append_bytes"]
@@ -318,7 +340,8 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "q8_attn_f32_partial_kernel" if args.path == "f32" else "q8_attn_partial_kernel",
+                "kernel": {"f32": "q8_attn_f32_partial_kernel", "sparse": "q8_sparse_probe_kernel + q8_sparse_attend_kernel"}.get(
+                    args.path, "q8_attn_partial_kernel"),
                 "kernel_us": round(part_us, 2),
                 "algorithmic_bytes_per_launch": int(attn_b)}
 
@@ -343,7 +366,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32" if args.path == "f32" else "int8/fp32", "data": "synthetic",
         "config": {
-            "workload": w.name, "path": args.path,
+            "workload": w.name, "path": args.path, "topk": args.topk if args.path == "sparse" else None,
             "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
