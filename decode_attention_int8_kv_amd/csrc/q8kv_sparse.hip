@@ -11,18 +11,28 @@
 // with the decode kernel's fp32 score formula; selection per query head,
 // ties to the lower block index, nothing forced in.
 //
-// Kernels:
-//   probe  -- one wave per (sequence, KV head, 16 blocks): lane (slot, c)
-//             reads bytes [16c, 16c + 16) of probe row 4 slot, so one load
-//             covers a block's 8 probes; every query head of the KV head
-//             gets the block's score (max over the 8 probes).
-//   attend -- one 4-wave workgroup per (sequence, query head): top-k by an
-//             8-pass radix select on 64-bit keys (score, then lower index),
-//             the chosen blocks sorted ascending, each wave attends over
-//             every fourth chosen block (the q8 single pass of "9-2
-//             flash_attn_single_q_q8_neon" §2), and the four partial states
-//             are combined in wave order (the same rescale rule) and divided
-//             once.
+// Kernels (one call enqueues them in this order):
+//   probe  -- one wave per (sequence, KV head, 16 blocks), the waves of a
+//             workgroup being the KV heads of the same 16 blocks (whole
+//             cache rows are read together).  The int8 dot products of the
+//             probe rows with up to 4 query heads at once run on the matrix
+//             cores (i8 MFMA, one 32-block per k-group, so every 32-block
+//             partial comes out exact and separate); the fp32 score and the
+//             max over a block's 8 probe rows follow in the lanes.
+//   select -- one wave per (sequence, query head): a lower bound of the
+//             k-th largest score from the 64 lanes' maxima keeps only a few
+//             candidates; the k-th largest of those is found bit by bit
+//             with ballot counts (no atomics); the blocks above it and the
+//             lowest-index ones equal to it are written in ascending order.
+//   attend -- P workgroups of 4 waves per (sequence, query head), P chosen
+//             from batch x heads so that small batches still fill the GPU;
+//             workgroup p takes a contiguous share of the kept blocks, its
+//             waves every fourth of them (the q8 single pass of "9-2
+//             flash_attn_single_q_q8_neon" §2), and their states are
+//             combined in wave order.  With P = 1 the result is written
+//             directly, else as a partial (M, S, acc) record.
+//   merge  -- P > 1 only: the records of each (sequence, query head)
+//             combined in order with the same rescale rule, divided once.
 #include "q8kv_tile.hpp"
 #include "q8kv_internal.hpp"
 
@@ -32,6 +42,10 @@ constexpr int kSparseBlock = 32;        // positions per sparse block
 constexpr int kProbeStride = 4;         // probe rows 0, 4, ..., 28
 constexpr int kProbeBlocksPerWave = 16;
 constexpr int kSparseWaves = 4;
+constexpr int kMaxTopk = 64;
+constexpr int kSelLdsKeys = 8192;       // keys the select wave keeps in LDS (32 KB); more are re-read
+constexpr int kSelSurvivors = 1024;     // keys at or above the select's lower bound kept in LDS (8 KB)
+constexpr int kMaxSparseParts = 8;
 
 struct SparseParams {
     CacheView cache;
@@ -39,10 +53,15 @@ struct SparseParams {
     const int32_t *seq_lens;
     const float *q;
     float *out;
-    float *scores;        // [batch][nq][max_nb] block scores
-    int32_t *selected;    // [batch][nq][topk] chosen blocks, or null
+    float *scores;        // [batch * nq][max_nb] block scores
+    int32_t *sel;         // [batch * nq][kMaxTopk] kept blocks, ascending
+    int32_t *cnt;         // [batch * nq] number kept
+    float2 *rec_ms;       // [batch * nq][parts] (M, S) of partial states (parts > 1)
+    float *rec_acc;       // [batch * nq][parts][128]
+    int32_t *selected;    // user copy [batch][nq][topk], or null
     int32_t *dev_status;
-    int32_t batch, nq, max_blocks_per_seq, max_seq_len, max_nb, topk;
+    int32_t batch, nq, max_blocks_per_seq, max_seq_len, max_nb, topk, parts;
+    int32_t probe_waves, probe_groups;   // probe workgroup: waves = KV heads [g * waves, (g + 1) * waves)
     float sc;             // softmax scale * log2(e)
 };
 
@@ -53,168 +72,311 @@ __device__ __forceinline__ int sparse_len(const SparseParams &p, int b)
 }
 
 // ------------------------------------------------------------------ probe --
-template <int G>
-__global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_probe_kernel(SparseParams p)
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Codes and step of one 32-float block of a query row, in one lane: the
+// decode kernel's query quantizer (step = max|x| * fl(1/127), code =
+// clamp(x * 127 / max|x|) truncated toward zero).
+__device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, uint4 &hi, float &qscale)
 {
+    const float4 *p = reinterpret_cast<const float4 *>(q32);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = p[i];
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));
+    const BlockQuant bq = q_block_params(m);
+    int cd[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cd[i] = q_code(x[i], bq.recip);
+    lo = make_uint4(pack4_i8(cd[0], cd[1], cd[2], cd[3]), pack4_i8(cd[4], cd[5], cd[6], cd[7]),
+                    pack4_i8(cd[8], cd[9], cd[10], cd[11]), pack4_i8(cd[12], cd[13], cd[14], cd[15]));
+    hi = make_uint4(pack4_i8(cd[16], cd[17], cd[18], cd[19]), pack4_i8(cd[20], cd[21], cd[22], cd[23]),
+                    pack4_i8(cd[24], cd[25], cd[26], cd[27]), pack4_i8(cd[28], cd[29], cd[30], cd[31]));
+    qscale = bq.qscale;
+}
+
+// One wave scores 16 blocks (8 pairs) of one KV head for its G query heads
+// with v_mfma_i32_16x16x64_i8 (C = A x B, 16 x 16, k = 64 per step):
+//   B (K rows): column j = lane % 16 is probe row 4 (j % 8) of block
+//     2 q + j / 8 of the pair; lane group lg = lane / 16 holds bytes
+//     [32 lg, 32 lg + 32) of the head's 128, 16 per step;
+//   A (queries): row i = 4 g + beta holds query head g's codes of 32-block
+//     beta, placed in k-group beta only (zeros elsewhere);
+//   so C[4 g + beta][j] is the exact int32 partial of block beta, and lane
+//   (lg, j) ends up holding the 4 partials of head lg for its own row j.
+// The score then follows the decode formula in one lane: x_beta = P_beta *
+// qscale_beta, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc); the block's
+// max over its 8 probe rows is taken across the 8 lanes j % 8 with DPP.
+template <int G>
+__global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_sparse_probe_kernel(SparseParams p)
+{
+    constexpr int kSets = G > 4 ? 2 : 1;   // 4 query heads per MFMA
+    constexpr int kPairs = kProbeBlocksPerWave / 2;
     const int nkv = p.cache.nkv;
-    const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
+    const int b = blockIdx.x / p.probe_groups, hg = blockIdx.x - (blockIdx.x / p.probe_groups) * p.probe_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int slot = lane >> 3, c = lane & 7;
+    const int kh = hg * p.probe_waves + wave;
+    if (kh >= nkv) return;
     const int n = uniform(sparse_len(p, b));
     const int nb = (n + kSparseBlock - 1) / kSparseBlock;
     if (nb <= p.topk) return;   // every block is kept: nothing to probe
-    const int j0 = (blockIdx.y * kSparseWaves + wave) * kProbeBlocksPerWave;
+    const int j0 = blockIdx.y * kProbeBlocksPerWave;
     if (j0 >= nb) return;
+    const int j = lane & 15, lg = lane >> 4;
 
-    uint4 qc[G];
-    float qs[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-        quantize_q_quarter(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim, c, qc[g], qs[g]);
-
+    // Rows at or past n are read at the sequence's last row and a bad block
+    // id as block 0, so every load is in bounds and all are issued before the
+    // first wait; such rows are masked to -inf.
     const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
     const int log2bs = p.cache.kv_bs_log2, mask = (1 << log2bs) - 1;
     const int row_bytes = nkv * kHeadDim;
-    int blk[kProbeBlocksPerWave];
+    auto token = [&](int q) { return (j0 + 2 * q + (j >> 3)) * kSparseBlock + kProbeStride * (j & 7); };
+    int id[kPairs];
 #pragma unroll
-    for (int i = 0; i < kProbeBlocksPerWave; ++i) {
-        const int t = (j0 + i) * kSparseBlock + kProbeStride * slot;
-        blk[i] = (t < n) ? bt[t >> log2bs] : -1;
-    }
-    uint4 kc[kProbeBlocksPerWave];
-    float ks[kProbeBlocksPerWave];
+    for (int q = 0; q < kPairs; ++q) id[q] = bt[min(token(q), n - 1) >> log2bs];
+    uint4 k0[kPairs], k1[kPairs];
+    float ks[kPairs];
+    uint32_t valid = 0;
     bool bad = false;
 #pragma unroll
-    for (int i = 0; i < kProbeBlocksPerWave; ++i) {
-        const int t = (j0 + i) * kSparseBlock + kProbeStride * slot;
-        const bool good = (unsigned)blk[i] < (unsigned)p.cache.num_blocks;
-        bad = bad || (t < n && !good);
-        if (t < n && good) {
-            const size_t row = ((size_t)blk[i] << log2bs) + (t & mask);
-            kc[i] = *reinterpret_cast<const uint4 *>(p.cache.k_codes + row * row_bytes + kh * kHeadDim + 16 * c);
-            ks[i] = p.cache.k_scale[(((size_t)blk[i] * nkv + kh) << log2bs) + (t & mask)];
-        } else {
-            kc[i] = make_uint4(0, 0, 0, 0);
-            ks[i] = 0.0f;
-            blk[i] = -1;
-        }
+    for (int q = 0; q < kPairs; ++q) {
+        const int tr = token(q), t = min(tr, n - 1);
+        const bool good = (unsigned)id[q] < (unsigned)p.cache.num_blocks;
+        bad = bad || (tr < n && !good);
+        valid |= (tr < n && good) ? (1u << q) : 0u;
+        const size_t blk = good ? (size_t)id[q] : 0;
+        const size_t row = (blk << log2bs) + (size_t)(t & mask);
+        const int8_t *src = p.cache.k_codes + row * row_bytes + kh * kHeadDim + 32 * lg;
+        k0[q] = *reinterpret_cast<const uint4 *>(src);
+        k1[q] = *reinterpret_cast<const uint4 *>(src + 16);
+        ks[q] = p.cache.k_scale[((blk * nkv + kh) << log2bs) + (size_t)(t & mask)];
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
 
+    // the queries are read and quantized while the rows are in flight
+    uint4 qa0[kSets], qa1[kSets];
+    float qsc[kSets][4];
 #pragma unroll
-    for (int i = 0; i < kProbeBlocksPerWave; ++i) {
-        const int j = j0 + i;
-        if (j >= nb) break;
+    for (int st = 0; st < kSets; ++st) {
+        const int gi = 4 * st + (j >> 2), beta = j & 3;
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+        float step = 0.0f;
+        if (gi < G) quantize_q_block(p.q + ((size_t)b * p.nq + kh * G + gi) * kHeadDim + 32 * beta, lo, hi, step);
+        const bool mine = lg == beta;
+        qa0[st] = mine ? lo : make_uint4(0, 0, 0, 0);
+        qa1[st] = mine ? hi : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            // the decode kernel's score, step for step: per 32-block
-            // x = P * qscale, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc)
-            float x = (float)block_partial(kc[i], qc[g]) * qs[g];
-            x += dpp_f<kDppQuadXor2>(x);
-            x += dpp_f<kDppHalfMirror>(x);
-            const float f = ks[i] * p.sc;
-            const float s = blk[i] >= 0 ? x * f : -INFINITY;
-            const float m = max_over_slots(s);
-            if (lane == 0) p.scores[((size_t)b * p.nq + kh * G + g) * p.max_nb + j] = m;
+        for (int r = 0; r < 4; ++r) qsc[st][r] = __shfl(step, 4 * lg + r, 64);   // head 4 st + lg, block r
+    }
+
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+        const float f = ks[q] * p.sc;
+        const bool ok = (valid >> q) & 1u;
+        const int jb = j0 + 2 * q + (j >> 3);
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) {
+            v4i c = {0, 0, 0, 0};
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, qa0[st]), __builtin_bit_cast(v4i, k0[q]),
+                                                      c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, qa1[st]), __builtin_bit_cast(v4i, k1[q]),
+                                                      c, 0, 0, 0);
+            const float x0 = __fmul_rn((float)c[0], qsc[st][0]), x1 = __fmul_rn((float)c[1], qsc[st][1]);
+            const float x2 = __fmul_rn((float)c[2], qsc[st][2]), x3 = __fmul_rn((float)c[3], qsc[st][3]);
+            const float y = __fadd_rn(__fadd_rn(x0, x1), __fadd_rn(x3, x2));
+            float sv = ok ? __fmul_rn(y, f) : -INFINITY;
+            sv = fmaxf(sv, dpp_f<kDppQuadXor1>(sv));
+            sv = fmaxf(sv, dpp_f<kDppQuadXor2>(sv));
+            sv = fmaxf(sv, dpp_f<kDppHalfMirror>(sv));   // max over the block's 8 probe rows
+            const int g = 4 * st + lg;
+            if (g < G && (j & 7) == 0 && jb < nb) p.scores[((size_t)b * p.nq + kh * G + g) * p.max_nb + jb] = sv;
         }
     }
 }
 
-// ----------------------------------------------------------------- attend --
-__device__ __forceinline__ uint64_t block_key(float s, int j)
+// ----------------------------------------------------------------- select --
+__device__ __forceinline__ uint32_t score_ord(float s)
 {
-    const uint32_t u = __float_as_uint(s);
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // order-preserving
-    return ((uint64_t)ord << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);   // ties: lower index first
+    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);   // -0 ties with +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // unsigned order = float order
 }
 
-template <bool Big>
-__global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_attend_kernel(SparseParams p)
-{
-    __shared__ uint32_t hist[256];
-    __shared__ uint64_t s_prefix;
-    __shared__ int s_need, s_cnt;
-    __shared__ int sel[64];
-    __shared__ float sh_m[kSparseWaves], sh_s[kSparseWaves];
-    __shared__ float sh_acc[kSparseWaves][kHeadDim];
+__device__ __forceinline__ int count_true(bool pred) { return __builtin_popcountll(__builtin_amdgcn_ballot_w64(pred)); }
 
-    const int b = blockIdx.x / p.nq, h = blockIdx.x - (blockIdx.x / p.nq) * p.nq;
-    const int G = p.nq / p.cache.nkv, kh = h / G;
-    const int tid = threadIdx.x;
-    const int wave = uniform(tid >> 6), lane = tid & 63, tslot = lane >> 3, c = lane & 7;
+__device__ __forceinline__ int lanes_before(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// The largest T with at least k of the list's keys >= T (the k-th largest
+// key), found bit by bit; a list item is key(i), i < len.
+template <class Key>
+__device__ __forceinline__ uint32_t kth_largest(int len, int k, int lane, Key key)
+{
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int c = 0;
+        for (int i0 = 0; i0 < len && c < k; i0 += 64) c += count_true(i0 + lane < len && key(i0 + lane) >= cand);
+        if (c >= k) T = cand;
+    }
+    return T;
+}
+
+// One wave per (sequence, query head).
+//  1. Each lane takes the maximum of the keys j = lane mod 64.  The k-th
+//     largest of these 64 maxima, L, is at most the k-th largest key T (the
+//     k lanes with the largest maxima each hold a key >= L).
+//  2. The keys >= L (few, except when many scores are equal) are compacted
+//     in index order; T is the k-th largest of them.
+//  3. Kept: every key > T, then the lowest-index keys equal to T up to k,
+//     written in ascending block order.
+// If more than kSelSurvivors keys are >= L, steps 2-3 run over all keys.
+__global__ __launch_bounds__(64) void q8_sparse_select_kernel(SparseParams p)
+{
+    extern __shared__ uint32_t keys[];   // min(max_nb, kSelLdsKeys) score keys when blocks are probed
+    __shared__ uint32_t surv_key[kSelSurvivors];
+    __shared__ int32_t surv_idx[kSelSurvivors];
+    const int bh = blockIdx.x, b = bh / p.nq, h = bh - (bh / p.nq) * p.nq;
+    const int lane = threadIdx.x;
     int n = p.seq_lens[b];
     if (n < 0 || n > p.max_seq_len) {
-        if (h == 0 && tid == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
+        if (h == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
         n = 0;
     }
     n = uniform(n);
-    float *o = p.out + ((size_t)b * p.nq + h) * kHeadDim;
     const int nb = (n + kSparseBlock - 1) / kSparseBlock;
-
-    // ---- which blocks
-    if (nb <= p.topk) {
-        if (tid < 64) sel[tid] = tid;
-        if (tid == 0) s_cnt = nb;
+    int32_t *sel = p.sel + (size_t)bh * kMaxTopk;
+    int32_t *user = p.selected ? p.selected + (size_t)bh * p.topk : nullptr;
+    const int k = p.topk;
+    int count;
+    if (nb <= k) {
+        for (int i = lane; i < nb; i += 64) {
+            sel[i] = i;
+            if (user) user[i] = i;
+        }
+        count = nb;
     } else {
-        const float *sc = p.scores + ((size_t)b * p.nq + h) * p.max_nb;
-        if (tid == 0) {
-            s_prefix = 0;
-            s_need = p.topk;
-        }
-        uint64_t mask = 0;
-        for (int pass = 0; pass < 8; ++pass) {
-            const int shift = 56 - 8 * pass;
-            hist[tid] = 0;
-            __syncthreads();
-            const uint64_t prefix = s_prefix;
-            for (int j = tid; j < nb; j += 64 * kSparseWaves) {
-                const uint64_t key = block_key(sc[j], j);
-                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xff], 1u);
+        const float *sc = p.scores + (size_t)bh * p.max_nb;
+        const bool in_lds = nb <= kSelLdsKeys;
+        uint32_t lmax = 0;
+        for (int j0 = 0; j0 < nb; j0 += 16 * 64) {   // 16 loads in flight per lane
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int jj = j0 + 64 * u + lane;
+                v[u] = jj < nb ? sc[jj] : 0.0f;
             }
-            __syncthreads();
-            if (tid == 0) {
-                // the digit of the need-th largest key among those matching the prefix
-                int need = s_need, d = 255;
-                for (; d > 0; --d) {
-                    const int hcount = (int)hist[d];
-                    if (hcount >= need) break;
-                    need -= hcount;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int jj = j0 + 64 * u + lane;
+                const uint32_t kj = score_ord(v[u]);
+                if (jj < nb) {
+                    if (in_lds) keys[jj] = kj;
+                    lmax = kj > lmax ? kj : lmax;
                 }
-                s_need = need;
-                s_prefix = prefix | ((uint64_t)d << shift);
             }
-            mask |= (uint64_t)0xff << shift;
-            __syncthreads();
         }
-        // keys are distinct, so exactly topk keys are >= the topk-th largest
-        const uint64_t kth = s_prefix;
-        if (tid == 0) s_cnt = 0;
         __syncthreads();
-        for (int j = tid; j < nb; j += 64 * kSparseWaves)
-            if (block_key(sc[j], j) >= kth) sel[atomicAdd(&s_cnt, 1)] = j;
-        __syncthreads();
-        if (tid < 64) {
-            // ascending block order: bitonic sort over the 64 lanes of wave 0
-            int v = tid < s_cnt ? sel[tid] : 0x7fffffff;
-            for (int k = 2; k <= 64; k <<= 1)
-                for (int jj = k >> 1; jj > 0; jj >>= 1) {
-                    const int u = __shfl_xor(v, jj, 64);
-                    const bool up = ((tid & k) == 0);
-                    const bool lower = (tid & jj) == 0;
-                    v = (lower == up) ? min(v, u) : max(v, u);
+        auto key = [&](int j) { return in_lds ? keys[j] : score_ord(sc[j]); };
+        // 1. the lower bound L
+        uint32_t L = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = L | (1u << bit);
+            if (count_true(lmax >= cand) >= k) L = cand;
+        }
+        // 2. survivors in index order
+        int ns = 0;
+        for (int j0 = 0; j0 < nb; j0 += 4 * 64) {   // 4 reads in flight per lane
+            uint32_t kv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int jj = j0 + 64 * u + lane;
+                kv[u] = jj < nb ? key(jj) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int jj = j0 + 64 * u + lane;
+                const bool keep = jj < nb && kv[u] >= L;
+                const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+                const int at = ns + lanes_before(bal);
+                if (keep && at < kSelSurvivors) {
+                    surv_key[at] = kv[u];
+                    surv_idx[at] = jj;
                 }
-            sel[tid] = v;
+                ns += __builtin_popcountll(bal);
+            }
         }
+        __syncthreads();
+        const bool few = ns <= kSelSurvivors;
+        const int len = few ? ns : nb;
+        auto item_key = [&](int i) { return few ? surv_key[i] : key(i); };
+        auto item_idx = [&](int i) { return few ? surv_idx[i] : i; };
+        uint32_t T;
+        if (len <= 64) {   // one candidate per lane: the search runs on ballots of a register
+            const uint32_t kr = lane < len ? item_key(lane) : 0u;
+            T = kth_largest(len, k, lane, [&](int) { return kr; });
+        } else {
+            T = kth_largest(len, k, lane, item_key);
+        }
+        // 3. the kept blocks in ascending order
+        int above = 0;
+        for (int i0 = 0; i0 < len; i0 += 64) above += count_true(i0 + lane < len && item_key(i0 + lane) > T);
+        int ties = k - above;   // items equal to T still to take, lowest index first
+        int base = 0;
+        for (int i0 = 0; i0 < len && base < k; i0 += 64) {
+            const int i = i0 + lane;
+            const uint32_t ki = i < len ? item_key(i) : 0u;
+            const uint64_t eqb = __builtin_amdgcn_ballot_w64(i < len && ki == T);
+            const bool take = i < len && (ki > T || (ki == T && lanes_before(eqb) < ties));
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
+            if (take) {
+                const int at = base + lanes_before(bal);
+                const int j = item_idx(i);
+                sel[at] = j;
+                if (user) user[at] = j;
+            }
+            base += __builtin_popcountll(bal);
+            const int eq_n = __builtin_popcountll(eqb);
+            ties -= eq_n < ties ? eq_n : ties;
+        }
+        count = k;
     }
-    __syncthreads();
-    const int cnt = s_cnt;
-    if (p.selected && tid < p.topk)
-        p.selected[((size_t)b * p.nq + h) * p.topk + tid] = tid < cnt ? sel[tid] : -1;
+    if (lane == 0) p.cnt[bh] = count;
+    if (user)
+        for (int i = count + lane; i < k; i += 64) user[i] = -1;
+}
 
-    // ---- exact attention over the chosen blocks: wave w takes every fourth
+// ----------------------------------------------------------------- attend --
+template <bool Big>
+__global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_attend_kernel(SparseParams p)
+{
+    __shared__ int sel[kMaxTopk];
+    __shared__ float sh_m[kSparseWaves], sh_s[kSparseWaves];
+    __shared__ float sh_acc[kSparseWaves][kHeadDim];
+
+    const int bh = blockIdx.x / p.parts, part = blockIdx.x - (blockIdx.x / p.parts) * p.parts;
+    const int b = bh / p.nq, h = bh - (bh / p.nq) * p.nq;
+    const int G = p.nq / p.cache.nkv, kh = h / G;
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6), lane = tid & 63, tslot = lane >> 3, c = lane & 7;
+    const int n = uniform(sparse_len(p, b));
+    const int cnt = uniform(p.cnt[bh]);
+    if (tid < kMaxTopk) sel[tid] = tid < cnt ? p.sel[(size_t)bh * kMaxTopk + tid] : 0;
+    __syncthreads();
+    const int k0 = (int)(((long long)part * cnt) / p.parts), k1 = (int)(((long long)(part + 1) * cnt) / p.parts);
+
     uint4 qc;
     float qs;
-    quantize_q_quarter(p.q + ((size_t)b * p.nq + h) * kHeadDim, c, qc, qs);
+    quantize_q_quarter(p.q + (size_t)bh * kHeadDim, c, qc, qs);
     const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
     const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
     const int log2bs = p.cache.kv_bs_log2;
@@ -259,14 +421,15 @@ __global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_attend_kernel(Spa
         }
     };
 
-    // this wave's blocks: sel[wave], sel[wave + 4], ...; tile i of the wave is
-    // block sel[wave + 4 i]; a tile past the list loads nothing
-    const int mine = cnt > wave ? (cnt - wave + kSparseWaves - 1) / kSparseWaves : 0;
-    auto tile_t0 = [&](int i) { return i < mine ? sel[wave + kSparseWaves * i] * kSparseBlock : 0; };
+    // this wave's blocks: kept positions k0 + wave, k0 + wave + 4, ... < k1;
+    // a tile past the list loads nothing
+    const int span = k1 - k0;
+    const int mine = span > wave ? (span - wave + kSparseWaves - 1) / kSparseWaves : 0;
+    auto tile_t0 = [&](int i) { return i < mine ? sel[k0 + wave + kSparseWaves * i] * kSparseBlock : 0; };
     auto tile_n = [&](int i) { return i < mine ? n : 0; };
-    Tile ta, tb;
-    TileBlocks ba, bb;
     if (mine > 0) {
+        Tile ta, tb;
+        TileBlocks ba, bb;
         fetch_blocks(bt, log2bs, tile_t0(0), tile_n(0), ba);
         load_tile<true, Big>(p.cache, ba, lo, lane, tile_t0(0), tile_n(0), p.dev_status, ta);
         fetch_blocks(bt, log2bs, tile_t0(1), tile_n(1), bb);
@@ -286,7 +449,7 @@ __global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_attend_kernel(Spa
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = sum_over_slots(acc[j]);
 
-    // ---- combine the waves in wave order, divide once
+    // combine the waves in wave order
     if (lane == 0) {
         sh_m[wave] = M;
         sh_s[wave] = S;
@@ -308,20 +471,82 @@ __global__ __launch_bounds__(64 * kSparseWaves) void q8_sparse_attend_kernel(Spa
             a1 = fmaf(sh_acc[w][2 * lane + 1], f, a1);
         }
     }
-    reinterpret_cast<float2 *>(o)[lane] = st > 0.0f ? make_float2(a0 / st, a1 / st) : make_float2(0.0f, 0.0f);
+    if (p.parts == 1) {
+        float2 *o = reinterpret_cast<float2 *>(p.out + (size_t)bh * kHeadDim);
+        o[lane] = st > 0.0f ? make_float2(a0 / st, a1 / st) : make_float2(0.0f, 0.0f);
+    } else {
+        const size_t r = (size_t)bh * p.parts + part;
+        reinterpret_cast<float2 *>(p.rec_acc + r * kHeadDim)[lane] = make_float2(a0, a1);
+        if (lane == 0) p.rec_ms[r] = make_float2(mx, st);
+    }
+}
+
+// ------------------------------------------------------------------ merge --
+__global__ __launch_bounds__(64) void q8_sparse_merge_kernel(SparseParams p)
+{
+    const size_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    float mx = -INFINITY;
+    for (int i = 0; i < p.parts; ++i) mx = fmaxf(mx, p.rec_ms[bh * p.parts + i].x);
+    float st = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    if (mx != -INFINITY) {
+        for (int i = 0; i < p.parts; ++i) {
+            const float2 ms = p.rec_ms[bh * p.parts + i];
+            const float f = __builtin_amdgcn_exp2f(ms.x - mx);   // 0 for a part with no tokens
+            const float2 a = reinterpret_cast<const float2 *>(p.rec_acc + (bh * p.parts + i) * kHeadDim)[lane];
+            st = fmaf(ms.y, f, st);
+            a0 = fmaf(a.x, f, a0);
+            a1 = fmaf(a.y, f, a1);
+        }
+    }
+    reinterpret_cast<float2 *>(p.out + bh * kHeadDim)[lane] =
+        st > 0.0f ? make_float2(a0 / st, a1 / st) : make_float2(0.0f, 0.0f);
 }
 
 // ------------------------------------------------------------------- host --
-size_t sparse_workspace_bytes(const q8_batch &batch, int nq)
+// Workgroups per (sequence, query head): enough that a small batch still
+// spreads over ~512 workgroups; a function of the shape only, so the
+// workspace size and the result do not depend on the device.
+static int sparse_parts(const q8_batch &batch, int nq)
 {
-    const size_t max_nb = (size_t)((batch.max_seq_len + kSparseBlock - 1) / kSparseBlock);
-    return ((size_t)batch.batch * nq * (max_nb > 0 ? max_nb : 1) * sizeof(float) + 255) / 256 * 256;
+    const long long rows = (long long)batch.batch * nq;
+    long long parts = 512 / (rows > 0 ? rows : 1);
+    if (parts < 1) parts = 1;
+    if (parts > kMaxSparseParts) parts = kMaxSparseParts;
+    return (int)parts;
 }
+
+struct SparseLayout {
+    size_t scores, sel, cnt, ms, acc, bytes;
+    int max_nb, parts;
+};
+
+static SparseLayout sparse_layout(const q8_batch &batch, int nq)
+{
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    SparseLayout l;
+    l.max_nb = (batch.max_seq_len + kSparseBlock - 1) / kSparseBlock;
+    if (l.max_nb < 1) l.max_nb = 1;
+    l.parts = sparse_parts(batch, nq);
+    const size_t rows = (size_t)batch.batch * nq;
+    l.scores = 0;
+    l.sel = up(rows * l.max_nb * sizeof(float));
+    l.cnt = l.sel + up(rows * kMaxTopk * sizeof(int32_t));
+    l.ms = l.cnt + up(rows * sizeof(int32_t));
+    const size_t recs = l.parts > 1 ? rows * l.parts : 0;
+    l.acc = l.ms + up(recs * sizeof(float2));
+    l.bytes = l.acc + up(recs * kHeadDim * sizeof(float));
+    return l;
+}
+
+size_t sparse_workspace_bytes(const q8_batch &batch, int nq) { return sparse_layout(batch, nq).bytes; }
 
 hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq, const float *q, float scale,
                          float *out, int topk, int32_t *selected, void *workspace, int32_t *dev_status,
                          hipStream_t stream)
 {
+    const SparseLayout l = sparse_layout(batch, nq);
+    char *ws = static_cast<char *>(workspace);
     SparseParams p;
     p.cache.k_codes = layer.k_codes;
     p.cache.v_codes = layer.v_codes;
@@ -334,21 +559,30 @@ hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq
     p.seq_lens = batch.seq_lens;
     p.q = q;
     p.out = out;
-    p.scores = static_cast<float *>(workspace);
+    p.scores = reinterpret_cast<float *>(ws + l.scores);
+    p.sel = reinterpret_cast<int32_t *>(ws + l.sel);
+    p.cnt = reinterpret_cast<int32_t *>(ws + l.cnt);
+    p.rec_ms = reinterpret_cast<float2 *>(ws + l.ms);
+    p.rec_acc = reinterpret_cast<float *>(ws + l.acc);
     p.selected = selected;
     p.dev_status = dev_status;
     p.batch = batch.batch;
     p.nq = nq;
     p.max_blocks_per_seq = batch.max_blocks_per_seq;
     p.max_seq_len = batch.max_seq_len;
-    p.max_nb = (batch.max_seq_len + kSparseBlock - 1) / kSparseBlock;
-    if (p.max_nb < 1) p.max_nb = 1;
+    p.max_nb = l.max_nb;
     p.topk = topk;
+    p.parts = l.parts;
     p.sc = (float)((double)scale * 1.4426950408889634);
+    p.probe_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    p.probe_waves = (layer.nkv_heads + p.probe_groups - 1) / p.probe_groups;
+    const bool big = layer.kv_bs >= kTile;
+    void *args[] = {&p};
+    hipError_t e;
 
-    if (p.max_nb > topk) {
-        const dim3 grid(batch.batch * layer.nkv_heads,
-                        (p.max_nb + kSparseWaves * kProbeBlocksPerWave - 1) / (kSparseWaves * kProbeBlocksPerWave));
+    const bool probing = l.max_nb > topk;
+    if (probing) {
+        const dim3 grid(batch.batch * p.probe_groups, (l.max_nb + kProbeBlocksPerWave - 1) / kProbeBlocksPerWave);
         const void *fn;
         switch (nq / layer.nkv_heads) {
         case 1: fn = reinterpret_cast<const void *>(&q8_sparse_probe_kernel<1>); break;
@@ -356,15 +590,22 @@ hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq
         case 4: fn = reinterpret_cast<const void *>(&q8_sparse_probe_kernel<4>); break;
         default: fn = reinterpret_cast<const void *>(&q8_sparse_probe_kernel<8>); break;
         }
-        void *args[] = {&p};
-        const hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * kSparseWaves), args, 0, stream);
-        if (e != hipSuccess) return e;
+        if ((e = hipLaunchKernel(fn, grid, dim3(64 * p.probe_waves), args, 0, stream)) != hipSuccess) return e;
     }
-    const void *fa = layer.kv_bs >= kTile ? reinterpret_cast<const void *>(&q8_sparse_attend_kernel<true>)
-                                          : reinterpret_cast<const void *>(&q8_sparse_attend_kernel<false>);
-    void *args[] = {&p};
-    const hipError_t e = hipLaunchKernel(fa, dim3(batch.batch * nq), dim3(64 * kSparseWaves), args, 0, stream);
-    return e != hipSuccess ? e : hipGetLastError();
+    const size_t lds = probing ? (size_t)(l.max_nb < kSelLdsKeys ? l.max_nb : kSelLdsKeys) * sizeof(uint32_t) : 0;
+    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(&q8_sparse_select_kernel), dim3(batch.batch * nq),
+                             dim3(64), args, lds, stream)) != hipSuccess)
+        return e;
+    const void *fa = big ? reinterpret_cast<const void *>(&q8_sparse_attend_kernel<true>)
+                         : reinterpret_cast<const void *>(&q8_sparse_attend_kernel<false>);
+    if ((e = hipLaunchKernel(fa, dim3(batch.batch * nq * l.parts), dim3(64 * kSparseWaves), args, 0, stream)) !=
+        hipSuccess)
+        return e;
+    if (l.parts > 1 &&
+        (e = hipLaunchKernel(reinterpret_cast<const void *>(&q8_sparse_merge_kernel), dim3(batch.batch * nq),
+                             dim3(64), args, 0, stream)) != hipSuccess)
+        return e;
+    return hipGetLastError();
 }
 
 }  // namespace q8kv
