@@ -396,12 +396,18 @@ def copy_probe(torch, dev, mib, reps):
     print(json.dumps({"copy_probe_bytes": mib * 2 ** 20, "reps": reps}), flush=True)
 
 
+# the sources the q8 decode partial kernel and its launch are built from
+KERNEL_SOURCES = ("q8kv_api.hip", "q8kv_decode.hip", "q8kv_device.hpp", "q8kv_internal.hpp", "q8kv_ranges.hpp",
+                  "q8kv_tile.hpp")
+
+
 def kernel_hash() -> str:
-    """Hash of the kernel sources: counter figures taken on other sources are stale."""
+    """Hash of the q8 decode kernel's sources: counter figures taken on other
+    sources are stale."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_int8_kv_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

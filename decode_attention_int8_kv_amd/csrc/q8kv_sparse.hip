@@ -7,14 +7,14 @@
 // at most k blocks (which includes every sequence of at most two blocks, the
 // page's gate, since k >= 2) keep every block.  Readings where the page
 // defers to another: probe rows 0, 4, ..., 28 of a block; a block's
-// importance is the largest q8 attention score of its probe rows, computed
-// with the decode kernel's fp32 score formula; selection per query head,
-// ties to the lower block index, nothing forced in.
+// importance is the largest q8 attention score of its probe rows, in fp32
+// with every product and sum rounded on its own (x_b = P_b * qscale_b,
+// y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc)); selection per query
+// head, ties to the lower block index, nothing forced in.
 //
 // Kernels (one call enqueues them in this order):
 //   probe  -- one wave per (sequence, KV head, 16 blocks), the waves of a
-//             workgroup being the KV heads of the same 16 blocks (whole
-//             cache rows are read together).  The int8 dot products of the
+//             workgroup being up to 4 KV heads of the same 16 blocks.  The int8 dot products of the
 //             probe rows with up to 4 query heads at once run on the matrix
 //             cores (i8 MFMA, one 32-block per k-group, so every 32-block
 //             partial comes out exact and separate); the fp32 score and the
@@ -41,6 +41,7 @@ namespace q8kv {
 constexpr int kSparseBlock = 32;        // positions per sparse block
 constexpr int kProbeStride = 4;         // probe rows 0, 4, ..., 28
 constexpr int kProbeBlocksPerWave = 16;
+constexpr int kProbeWaves = 4;         // KV heads per probe workgroup
 constexpr int kSparseWaves = 4;
 constexpr int kMaxTopk = 64;
 constexpr int kSelLdsKeys = 8192;       // keys the select wave keeps in LDS (32 KB); more are re-read
@@ -116,7 +117,7 @@ __device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, ui
 // qscale_beta, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc); the block's
 // max over its 8 probe rows is taken across the 8 lanes j % 8 with DPP.
 template <int G>
-__global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_sparse_probe_kernel(SparseParams p)
+__global__ __launch_bounds__(64 * kProbeWaves) void q8_sparse_probe_kernel(SparseParams p)
 {
     constexpr int kSets = G > 4 ? 2 : 1;   // 4 query heads per MFMA
     constexpr int kPairs = kProbeBlocksPerWave / 2;
@@ -189,10 +190,17 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_sparse_probe_kernel(Sp
                                                       c, 0, 0, 0);
             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, qa1[st]), __builtin_bit_cast(v4i, k1[q]),
                                                       c, 0, 0, 0);
-            const float x0 = __fmul_rn((float)c[0], qsc[st][0]), x1 = __fmul_rn((float)c[1], qsc[st][1]);
-            const float x2 = __fmul_rn((float)c[2], qsc[st][2]), x3 = __fmul_rn((float)c[3], qsc[st][3]);
-            const float y = __fadd_rn(__fadd_rn(x0, x1), __fadd_rn(x3, x2));
-            float sv = ok ? __fmul_rn(y, f) : -INFINITY;
+            float sv;
+            {
+                // every product and sum rounded on its own: the score decides
+                // which blocks are kept, so it must be the formula's exact fp32
+                // value (no fused multiply-add)
+#pragma clang fp contract(off)
+                const float x0 = (float)c[0] * qsc[st][0], x1 = (float)c[1] * qsc[st][1];
+                const float x2 = (float)c[2] * qsc[st][2], x3 = (float)c[3] * qsc[st][3];
+                const float y = (x0 + x1) + (x3 + x2);
+                sv = ok ? y * f : -INFINITY;
+            }
             sv = fmaxf(sv, dpp_f<kDppQuadXor1>(sv));
             sv = fmaxf(sv, dpp_f<kDppQuadXor2>(sv));
             sv = fmaxf(sv, dpp_f<kDppHalfMirror>(sv));   // max over the block's 8 probe rows
@@ -574,7 +582,7 @@ hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq
     p.topk = topk;
     p.parts = l.parts;
     p.sc = (float)((double)scale * 1.4426950408889634);
-    p.probe_groups = (layer.nkv_heads + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
+    p.probe_groups = (layer.nkv_heads + kProbeWaves - 1) / kProbeWaves;
     p.probe_waves = (layer.nkv_heads + p.probe_groups - 1) / p.probe_groups;
     const bool big = layer.kv_bs >= kTile;
     void *args[] = {&p};

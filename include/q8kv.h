@@ -188,7 +188,9 @@ q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *b
 /* Block-sparse decode ("why long context must be sparse" §1-§2): per
  * sequence b and query head h, the history is cut into 32-token blocks; each
  * block is probed at its rows 0, 4, ..., 28 and scored by the largest q8
- * attention score among them (the decode's fp32 score formula); the `topk`
+ * attention score among them (fp32, each product and sum rounded on its
+ * own: x_b = P_b * qscale_b, y = (x0 + x1) + (x3 + x2), s = y * (kscale *
+ * scale * log2 e)); the `topk`
  * highest-scoring blocks (ties: lower block index) are kept, and out[b][h]
  * is the exact q8 single-pass attention ("9-2" §2) over the tokens of those
  * blocks.  A sequence of at most topk blocks keeps every block (the result

@@ -112,3 +112,38 @@ def test_sparse_graph_replays_match_eager():
         t.cuda.synchronize()
         assert t.equal(out, eager), f"replay {i}"
     assert dc.status_word() == 0
+
+
+@pytest.mark.parametrize("group,kv_bs", [(1, 32), (2, 8), (4, 32), (8, 16)])
+def test_sparse_probe_scores_bitwise(group, kv_bs):
+    # White-box: the probe's block scores sit at the start of the workspace,
+    # [batch * nq][max_nb] fp32 (max_nb = ceil(max_seq_len / 32)).  Wherever a
+    # sequence has more than k blocks they must equal the oracle's probe
+    # scores bit for bit (the matrix-core dot products are exact integers and
+    # the fp32 steps follow the same order).
+    say(f"[sparse] probe scores group={group} kv_bs={kv_bs}")
+    t, m = torch(), q8()
+    nkv, nq, topk = 2, 2 * group, 4
+    lens = np.array([1500, 97, 5, 4096, 700], np.int32)
+    k, v = dense_kv(lens, nkv, seed=600 + group, dist="student3x3")
+    q = np.random.default_rng([600 + group, 7]).standard_normal((len(lens), nq, 128)).astype(np.float32)
+    dc = DeviceCache(lens, nkv, kv_bs, seed=600 + group)
+    dc.append_dense(k, v)
+    want = oracle.sparse_scores(oracle.build_cache(k, v, lens, dc.table, dc.num_blocks, kv_bs), q, nq, SCALE)
+    out = t.empty((len(lens), nq, 128), dtype=t.float32, device="cuda")
+    ws = t.empty(m.decode_attn_sparse_workspace_bytes(dc.layer, dc.batch, nq, topk), dtype=t.uint8, device="cuda")
+    ws.fill_(0xCD)
+    m.decode_attn_sparse(dc.layer, dc.batch, nq, t.from_numpy(q).cuda(), SCALE, out, ws, topk=topk,
+                         dev_status=dc.status)
+    assert dc.status_word() == 0
+    max_nb = want.shape[-1]
+    got = ws[:len(lens) * nq * max_nb * 4].cpu().numpy().view(np.float32).reshape(len(lens), nq, max_nb)
+    checked = 0
+    for b, n in enumerate(lens):
+        nb = (int(n) + 31) // 32
+        if nb <= topk:
+            continue
+        np.testing.assert_array_equal(got[b, :, :nb].view(np.uint32), want[b, :, :nb].view(np.uint32),
+                                      err_msg=f"sequence {b}")
+        checked += nq * nb
+    assert checked > 0
