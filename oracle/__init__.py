@@ -12,7 +12,10 @@ Pages the oracle follows (cited by title and section):
     online softmax), §2 segment 3 (final division), §3 (single pass is
     functionally the same as storing every score first), §4 (observables).
   * 9-3 "q8 KV 精度对照实验": §1 (the reference attention), §2 (per-(token,
-    head) K/V quantizer), §3 (printed fp32-KV vs q8-KV gap).
+    head) K/V quantizer), §3 (printed fp32-KV vs q8-KV gap, and the fp32
+    mirror cache of its closing note).
+  * 10-1 "why long context must be sparse": §1-§2 (block-sparse decode; the
+    batched prefill over the cache).
 
 Every oracle function is pinned by a CPU test against facts fixed by the
 pages or by mathematics (closed forms, invariants, brute force); none is
@@ -72,6 +75,8 @@ def _load():
     lib.orc_decode_attn_sparse.restype = I
     lib.orc_sparse_scores.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, I, P]
     lib.orc_sparse_scores.restype = I
+    lib.orc_prefill_attn.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, P, P, I, P, F, P, I]
+    lib.orc_prefill_attn.restype = I
     lib.orc_num_threads_available.restype = I
     _lib = lib
     return lib
@@ -348,6 +353,29 @@ def decode_attn_sparse(cache: Cache, q: np.ndarray, nq: int, scale: float, topk:
     if rc:
         raise ValueError("oracle: bad sequence length or block id")
     return out, sel
+
+
+def prefill_attn(cache: Cache, q: np.ndarray, q_start, nq: int, scale: float, nthreads: int = 0) -> np.ndarray:
+    """Batched prefill attention ("10-1" §1-§2, readings in the C source):
+    the q_start[b + 1] - q_start[b] new tokens of sequence b are the last
+    positions of its cache; query row r sits at position seq_lens[b] - nb +
+    (r - q_start[b]) and attends causally to positions 0..p.  q: [total_q,
+    nq, hd] fp32 -> the same shape."""
+    q = _c(q, np.float32)
+    qs = _c(np.asarray(q_start), np.int32)
+    if qs.shape != (cache.batch + 1,) or q.shape[0] != int(qs[-1]):
+        raise ValueError("q_start must be [batch + 1] with q_start[batch] = number of query rows")
+    out = np.zeros(q.shape, np.float32)
+    nthreads = nthreads or threads_available()
+    rc = _load().orc_prefill_attn(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
+                                  _p(cache.block_table), cache.max_blocks_per_seq,
+                                  _p(cache.seq_lens), cache.num_blocks,
+                                  _p(cache.k_codes), _p(cache.v_codes),
+                                  _p(cache.k_step), _p(cache.v_step),
+                                  _p(qs), int(q.shape[0]), _p(q), float(np.float32(scale)), _p(out), nthreads)
+    if rc:
+        raise ValueError("oracle: bad q_start, sequence length or block id")
+    return out
 
 
 def sparse_scores(cache: Cache, q: np.ndarray, nq: int, scale: float) -> np.ndarray:

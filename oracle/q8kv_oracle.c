@@ -181,15 +181,13 @@ static int64_t orc_row_of(const int32_t *block_table, int max_blocks_per_seq, in
  * row of KV head h / (nq/nkv) exactly (code times its scale, in double), then
  * run the three-pass attention.  Writes hd fp32 values to o (zeros when the
  * length is 0).  Returns 0, or -1 on a bad length or block id (o = zeros). */
-static int orc_one_row(int b, int h, int nq, int nkv, int hd, int kv_bs,
-                       const int32_t *block_table, int max_blocks_per_seq,
-                       const int32_t *seq_lens, int num_blocks,
-                       const int8_t *k_codes, const int8_t *v_codes,
-                       const float *k_step, const float *v_step,
-                       const float *q_row, float scale, float *o)
+static int orc_one_row_n(int b, int h, int nq, int nkv, int hd, int kv_bs,
+                         const int32_t *block_table, int max_blocks_per_seq, int64_t n, int num_blocks,
+                         const int8_t *k_codes, const int8_t *v_codes,
+                         const float *k_step, const float *v_step,
+                         const float *q_row, float scale, float *o)
 {
     int kh = h / (nq / nkv);
-    int64_t n = seq_lens[b];
     for (int i = 0; i < hd; ++i) o[i] = 0.0f;
     if (n < 0 || n > (int64_t)max_blocks_per_seq * kv_bs) return -1;
     if (n == 0) return 0;
@@ -220,6 +218,18 @@ static int orc_one_row(int b, int h, int nq, int nkv, int hd, int kv_bs,
     }
     free(cq); free(qsc); free(qh); free(kk); free(vv); free(oh);
     return rc;
+}
+
+/* The same over the sequence's whole visible history (n = seq_lens[b]). */
+static int orc_one_row(int b, int h, int nq, int nkv, int hd, int kv_bs,
+                       const int32_t *block_table, int max_blocks_per_seq,
+                       const int32_t *seq_lens, int num_blocks,
+                       const int8_t *k_codes, const int8_t *v_codes,
+                       const float *k_step, const float *v_step,
+                       const float *q_row, float scale, float *o)
+{
+    return orc_one_row_n(b, h, nq, nkv, hd, kv_bs, block_table, max_blocks_per_seq, seq_lens[b], num_blocks,
+                         k_codes, v_codes, k_step, v_step, q_row, scale, o);
 }
 
 /* Every (b, h) of a batch.  q, out: [batch][nq][hd] fp32.  Returns 0, or -1
@@ -609,6 +619,63 @@ int orc_decode_attn_sparse(int batch, int nq, int nkv, int hd, int kv_bs,
         if (rc < 0) {
 #pragma omp atomic write
             status = -1;
+        }
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------ O12 ------- */
+/* Batched prefill attention over the q8 cache ([10-1] §1: a prefill batch of
+ * nb new tokens scores against the whole history, O(nb x n); §2: the exact
+ * batched path beside the block-sparse one).  The pages do not spell out the
+ * masking inside the batch or the query quantization for many rows; the
+ * readings taken here:
+ *   - the nb_b = q_start[b + 1] - q_start[b] new tokens of sequence b are the
+ *     last nb_b positions of its cache (appended before the call), so query
+ *     row r (q_start[b] <= r < q_start[b + 1]) sits at position
+ *     p = seq_lens[b] - nb_b + (r - q_start[b]);
+ *   - causal: that row attends to positions 0..p (the history and the batch's
+ *     earlier tokens and itself);
+ *   - each query row is quantized on its own exactly like the decode query
+ *     (O2), and its attention is the decode attention (O4-O8) over the first
+ *     p + 1 positions.
+ * q, out: [total_q][nq][hd] fp32, total_q = q_start[batch].  Returns 0, or -1
+ * on a bad q_start, length or block id (rows of such a sequence are zeros;
+ * nothing is written for a q_start range outside [0, total_q]). */
+int orc_prefill_attn(int batch, int nq, int nkv, int hd, int kv_bs,
+                     const int32_t *block_table, int max_blocks_per_seq,
+                     const int32_t *seq_lens, int num_blocks,
+                     const int8_t *k_codes, const int8_t *v_codes,
+                     const float *k_step, const float *v_step,
+                     const int32_t *q_start, int total_q,
+                     const float *q, float scale, float *out, int nthreads)
+{
+    int status = 0;
+    if (nthreads < 1) nthreads = 1;
+    for (int b = 0; b < batch; ++b) {
+        int32_t r0 = q_start[b], r1 = q_start[b + 1];
+        int64_t n = seq_lens[b];
+        if (r0 < 0 || r1 < r0 || r1 > total_q) { status = -1; continue; }
+        int64_t nb = (int64_t)r1 - r0;
+        int bad = n < nb || n > (int64_t)max_blocks_per_seq * kv_bs;
+        if (bad) {
+            status = -1;
+            for (int64_t i = (int64_t)r0 * nq * hd; i < (int64_t)r1 * nq * hd; ++i) out[i] = 0.0f;
+            continue;
+        }
+        int64_t rows = nb * nq;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+        for (int64_t rh = 0; rh < rows; ++rh) {
+            int64_t r = r0 + rh / nq;
+            int h = (int)(rh % nq);
+            int64_t pos = n - nb + (r - r0);
+            int rc = orc_one_row_n(b, h, nq, nkv, hd, kv_bs, block_table, max_blocks_per_seq, pos + 1,
+                                   num_blocks, k_codes, v_codes, k_step, v_step,
+                                   q + (r * nq + h) * hd, scale, out + (r * nq + h) * hd);
+            if (rc) {
+#pragma omp atomic write
+                status = -1;
+            }
         }
     }
     return status;
