@@ -75,6 +75,8 @@ def _load():
     lib.q8_decode_attn_sparse_workspace_bytes.restype = SZ
     lib.q8_decode_attn_sparse.argtypes = [LP, BP, I32, P, F, P, I32, P, P, SZ, P, P]
     lib.q8_decode_attn_sparse.restype = I32
+    lib.q8_prefill_attn.argtypes = [LP, BP, I32, P, I32, I32, P, F, P, P, P]
+    lib.q8_prefill_attn.restype = I32
     lib.q8_quantize_q.argtypes = [P, I32, I32, P, P, P]
     lib.q8_quantize_q.restype = I32
     lib.q8_qk_block_partials.argtypes = [LP, BP, I32, P, P, P, P]
@@ -240,6 +242,17 @@ def decode_attn_sparse(layer, batch, nq_heads, q, scale, out, workspace, topk=32
                                        float(scale), _ptr(out), int(topk), _ptr(selected), _ptr(workspace),
                                        ws_bytes, _ptr(dev_status), _stream(stream))
     _check(st, "q8_decode_attn_sparse")
+
+
+def prefill_attn(layer, batch, nq_heads, q_start, max_new, q, scale, out, dev_status=None, stream=None):
+    """q8_prefill_attn: causal attention of the new tokens' queries (the last
+    q_start[b + 1] - q_start[b] positions of each sequence's cache) over the
+    q8 cache.  q_start: device int32 [batch + 1]; q, out: [total_q, nq, 128]."""
+    total_q = int(q.shape[0])
+    st = _load().q8_prefill_attn(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q_start),
+                                 total_q, int(max_new), _ptr(q), float(scale), _ptr(out), _ptr(dev_status),
+                                 _stream(stream))
+    _check(st, "q8_prefill_attn")
 
 
 def quantize_q(q, codes, qscale, stream=None):

@@ -212,6 +212,27 @@ q8_status q8_decode_attn_sparse(const q8_kv_layer *layer, const q8_batch *batch,
     return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_attn_sparse");
 }
 
+q8_status q8_prefill_attn(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                          const int32_t *q_start, int32_t total_q, int32_t max_new, const float *q, float scale,
+                          float *out, int32_t *dev_status, void *stream)
+{
+    q8_status s;
+    if ((s = check_layer(layer)) != Q8_OK) return s;
+    if ((s = check_batch(batch, layer)) != Q8_OK) return s;
+    if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
+    if (total_q < 0 || max_new < 0 || max_new > batch->max_seq_len) return Q8_EINVAL;
+    if (!q_start || !aligned(q_start, 4)) return Q8_EINVAL;
+    if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
+    if (total_q == 0 || max_new == 0) return Q8_OK;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return Q8_EINVAL;
+    if ((long long)total_q * nq_heads * q8kv::kHeadDim > (1LL << 40)) return Q8_EUNSUPPORTED;
+    // launch rows: max_new * G per (sequence, KV head), 64 per workgroup, grid y <= 65535
+    if (((long long)max_new * (nq_heads / layer->nkv_heads) + 63) / 64 > 65535) return Q8_EUNSUPPORTED;
+    hipError_t e = q8kv::launch_prefill(*layer, *batch, nq_heads, q_start, total_q, max_new, q, scale, out,
+                                        dev_status, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_prefill_attn");
+}
+
 q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int8_t *codes, float *qscale,
                         void *stream)
 {

@@ -46,6 +46,10 @@ hipError_t launch_sparse(const q8_kv_layer &layer, const q8_batch &batch, int nq
                          float *out, int topk, int32_t *selected, void *workspace, int32_t *dev_status,
                          hipStream_t stream);
 
+hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int nq, const int32_t *q_start,
+                          int total_q, int max_new, const float *q, float scale, float *out, int32_t *dev_status,
+                          hipStream_t stream);
+
 hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,
                                const DecodePlan &plan, void *workspace, hipStream_t stream);
 

@@ -1,0 +1,330 @@
+// q8kv_prefill.hip -- batched prefill attention over the q8 cache on the
+// matrix cores.
+//
+// Method ("why long context must be sparse" §1-§2: the exact batched prefill
+// path; a batch of nb new tokens scores against the whole history): the new
+// tokens of sequence b are the last nb_b positions of its cache (appended
+// before the call); query row r at position p attends to positions 0..p.
+// Each query row is quantized like the decode query (per 32-block step
+// m * fl(1/127), codes truncated), and its attention is the decode's:
+// s_t = ((sum_beta float(P_beta) * qs_beta) * ks_t) * scale with exact int32
+// block partials P_beta, softmax over t <= p, weights times V codes and V
+// steps, one division at the end ("9-2 flash_attn_single_q_q8_neon" §2).
+//
+// A wave owns 16 query rows of one KV head: row rho = position * G + head of
+// the flattened (position, query head) list.  It walks the keys 0..p_max of
+// its rows in tiles of 16 tokens:
+//   scores  S^T = K Q^T with v_mfma_i32_16x16x32_i8, one instruction per
+//           32-block beta (A: token j's bytes 32 beta + [8 lg, 8 lg + 8) in
+//           lane (lg, j); B: the query codes in the same places), so lane
+//           (lg, j) receives the exact partials of query j with tokens
+//           4 lg .. 4 lg + 3 and forms their fp32 scores in place;
+//   softmax online per query (log2 domain): the tile max across the 4 lane
+//           groups with v_permlane16/32_swap, one rescale of S and the
+//           accumulators per tile;
+//   values  O^T += V^T P^T with v_mfma_f32_16x16x16_bf16.  P^T arrives in
+//           exactly the B layout (query j, tokens 4 lg + e); each weight
+//           w = p * vs is split exactly into three bf16 terms
+//           (w = hi + mid + lo by truncation; the "bf16x3" form of an fp32
+//           product), and V codes (|code| <= 127) are exact in bf16, so the
+//           products are exact and only the fp32 accumulation order differs
+//           from a scalar loop.  V^T is staged per tile through LDS: each
+//           lane loads 4 bytes of 8 token rows, transposes them with v_perm
+//           and writes one dword (4 tokens of one dim) per dim.
+#include "q8kv_tile.hpp"
+#include "q8kv_internal.hpp"
+
+namespace q8kv {
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPrefillWaves = 4;   // 16-row query tiles per workgroup
+constexpr int kPrefillRows = 16;   // query rows per wave
+constexpr int kKeyTile = 16;       // tokens per step
+constexpr int kVtStride = 5;       // dwords per dim row of the staged V^T tile (4 token quads + 1 pad)
+
+struct PrefillParams {
+    CacheView cache;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    const int32_t *q_start;
+    const float *q;
+    float *out;
+    int32_t *dev_status;
+    int32_t nq, max_blocks_per_seq, max_seq_len, max_new, total_q, log2g;
+    float sc;   // softmax scale * log2(e)
+};
+
+// 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
+__device__ __forceinline__ v4s_t codes_to_bf16(uint32_t w)
+{
+    const uint32_t f0 = __float_as_uint((float)(int)(int8_t)(w & 0xff));
+    const uint32_t f1 = __float_as_uint((float)(int)(int8_t)((w >> 8) & 0xff));
+    const uint32_t f2 = __float_as_uint((float)(int)(int8_t)((w >> 16) & 0xff));
+    const uint32_t f3 = __float_as_uint((float)(int)(int8_t)(w >> 24));
+    const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);   // upper halves of f0, f1
+    const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    return __builtin_bit_cast(v4s_t, make_uint2(lo, hi));
+}
+
+// Exact split of 4 fp32 weights into three bf16 terms each (truncation: the
+// first term keeps the top 8 significant bits, the second the next 8, the
+// third the rest; both subtractions are exact).
+__device__ __forceinline__ void split_bf16x3(const float (&w)[4], v4s_t &hi, v4s_t &mid, v4s_t &lo)
+{
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h[e] = __float_as_uint(w[e]) & 0xffff0000u;
+        const float r1 = w[e] - __uint_as_float(h[e]);
+        m[e] = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(m[e]);
+        l[e] = __float_as_uint(r2);
+    }
+    hi = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(h[1], h[0], 0x07060302u),
+                                              __builtin_amdgcn_perm(h[3], h[2], 0x07060302u)));
+    mid = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(m[1], m[0], 0x07060302u),
+                                               __builtin_amdgcn_perm(m[3], m[2], 0x07060302u)));
+    lo = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(l[1], l[0], 0x07060302u),
+                                              __builtin_amdgcn_perm(l[3], l[2], 0x07060302u)));
+}
+
+__global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillParams p)
+{
+    __shared__ uint32_t vt_all[kPrefillWaves][kHeadDim * kVtStride];
+    const int nkv = p.cache.nkv;
+    const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
+    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    uint32_t *vt = vt_all[wave];
+    const int tile = blockIdx.y * kPrefillWaves + wave;
+    const int G = 1 << p.log2g;
+    const int j = lane & 15, lg = lane >> 4;
+
+    const int r0 = uniform(p.q_start[b]), r1 = uniform(p.q_start[b + 1]);
+    const int n = uniform(p.seq_lens[b]);
+    const bool range_ok = 0 <= r0 && r0 <= r1 && r1 <= p.total_q;
+    const int nn = r1 - r0;
+    if (!range_ok || n < nn || n > p.max_seq_len || nn > p.max_new) {
+        // a bad sequence: reported; its rows that this wave covers are zeros
+        if (kh == 0 && tile == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
+        if (range_ok) {
+            const int rho = tile * kPrefillRows + j;
+            if (rho < (nn << p.log2g)) {
+                const int i = rho >> p.log2g, g = rho & (G - 1);
+                float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        return;
+    }
+    const int rows = nn << p.log2g;
+    if (tile * kPrefillRows >= rows) return;
+
+    // this lane's query row (clamped to a real row; lanes past the end are
+    // computed and discarded) and its position
+    const int rho = tile * kPrefillRows + j;
+    const bool live = rho < rows;
+    const int rr = live ? rho : rows - 1;
+    const int qi = rr >> p.log2g, qg = rr & (G - 1);
+    const int pos = n - nn + qi;
+    const size_t qrow = ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
+    const int p_hi = n - nn + (min(tile * kPrefillRows + kPrefillRows - 1, rows - 1) >> p.log2g);
+    const int nkt = p_hi / kKeyTile + 1;
+
+    // query codes, the B operand of the score MFMAs: bytes 32 beta + [8 lg, 8 lg + 8)
+    long qb[4];
+    float qs[4];
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+        const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
+        const float4 a = src[0], c = src[1];
+        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+        m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
+        const BlockQuant bq = q_block_params(m);
+        int cd[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cd[e] = q_code(x[e], bq.recip);
+        const uint32_t w0 = pack4_i8(cd[0], cd[1], cd[2], cd[3]), w1 = pack4_i8(cd[4], cd[5], cd[6], cd[7]);
+        qb[beta] = (long)(((uint64_t)w1 << 32) | w0);
+        qs[beta] = bq.qscale;
+    }
+
+    const const_i32 *sbt = (const const_i32 *)(p.block_table + (size_t)b * p.max_blocks_per_seq);
+    const int log2bs = p.cache.kv_bs_log2, bmask = (1 << log2bs) - 1;
+    const int row_bytes = nkv * kHeadDim;
+    const int8_t *kbase = p.cache.k_codes + (size_t)kh * kHeadDim;
+    const int8_t *vbase = p.cache.v_codes + (size_t)kh * kHeadDim;
+    const int vh = lane >> 5, vd = lane & 31;   // V staging: tokens 8 vh + u, dims 4 vd .. 4 vd + 3
+
+    float M = -INFINITY, S = 0.0f;
+    v4f_t acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    bool bad = false;
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int t0 = kt * kKeyTile;
+        // Block ids of the tile's two 8-token halves (kv_bs >= 8 keeps each
+        // half in one block).  Tokens are clamped to n - 1 >= t0, so every
+        // address is inside the sequence's blocks; a bad id reads block 0 and
+        // its tokens are masked.
+        int id0 = sbt[min(t0, n - 1) >> log2bs];
+        int id1 = sbt[min(t0 + 8, n - 1) >> log2bs];
+        const bool good0 = (unsigned)id0 < (unsigned)p.cache.num_blocks;
+        const bool good1 = (unsigned)id1 < (unsigned)p.cache.num_blocks;
+        bad = bad || !good0 || (t0 + 8 <= p_hi && !good1);
+        id0 = good0 ? id0 : 0;
+        id1 = good1 ? id1 : 0;
+        auto row_of = [&](int t) {   // t in [t0, t0 + 16), already clamped to n - 1
+            const int id = ((t - t0) >> 3) ? id1 : id0;
+            return ((size_t)id << log2bs) + (size_t)(t & bmask);
+        };
+        auto good_of = [&](int t) { return ((t - t0) >> 3) ? good1 : good0; };
+
+        // K rows (A operand): token t0 + j, bytes 32 beta + 8 lg
+        const int8_t *krow = kbase + row_of(min(t0 + j, n - 1)) * row_bytes + 8 * lg;
+        long ka[4];
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) ka[beta] = *reinterpret_cast<const long *>(krow + 32 * beta);
+        // steps of tokens t0 + 4 lg + e
+        float ks[4], vs[4];
+        bool tok_ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 4 * lg + e, tc = min(t, n - 1);
+            const size_t row = row_of(tc);
+            const size_t sidx = ((((row >> log2bs) * nkv + kh)) << log2bs) + (row & bmask);
+            ks[e] = p.cache.k_scale[sidx];
+            vs[e] = p.cache.v_scale[sidx];
+            tok_ok[e] = t <= pos && good_of(tc);
+        }
+        // V rows for the transpose: 4 bytes (dims 4 vd ..) of tokens t0 + 8 vh + u
+        uint32_t vw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t row = row_of(min(t0 + 8 * vh + u, n - 1));
+            vw[u] = *reinterpret_cast<const uint32_t *>(vbase + row * row_bytes + 4 * vd);
+        }
+
+        // scores of query j with tokens t0 + 4 lg + e
+        v4i_t c[4];
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta)
+            c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[beta], qb[beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
+        float s[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = (float)c[0][e] * qs[0], x1 = (float)c[1][e] * qs[1];
+            const float x2 = (float)c[2][e] * qs[2], x3 = (float)c[3][e] * qs[3];
+            const float y = (x0 + x1) + (x3 + x2);
+            // branch-free mask (a select here becomes a divergent branch)
+            const uint32_t keep = tok_ok[e] ? 0xffffffffu : 0u;
+            s[e] = __uint_as_float(bitsel(keep, __float_as_uint(y * (ks[e] * p.sc)), 0xff800000u));
+        }
+        float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        m = max_rows32(max_rows16(m));   // the tile max of query j (token 0 keeps M finite from tile 0)
+        const float Mn = fmaxf(M, m);
+        // 0 on the first tile with a finite max; 1 while every token so far is masked
+        const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+        M = Mn;
+        float w[4], psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // a masked score is -inf: exp2(-inf - M) = 0 for finite M; while M
+            // is still -inf every score is masked and the weight must be 0
+            const float pw = __uint_as_float(bitsel(tok_ok[e] ? 0xffffffffu : 0u,
+                                                    __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M)), 0u));
+            psum += pw;
+            w[e] = pw * vs[e];
+        }
+        S = S * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+        v4s_t whi, wmid, wlo;
+        split_bf16x3(w, whi, wmid, wlo);
+
+        // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim
+        uint32_t tq[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t a0 = vw[4 * half], a1 = vw[4 * half + 1], a2 = vw[4 * half + 2], a3 = vw[4 * half + 3];
+            const uint32_t x01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.b0 a1.b0 a0.b1 a1.b1
+            const uint32_t x01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.b2 a1.b2 a0.b3 a1.b3
+            const uint32_t x23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+            const uint32_t x23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+            tq[4 * half + 0] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);  // byte 0 of a0..a3
+            tq[4 * half + 1] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);  // byte 1
+            tq[4 * half + 2] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);  // byte 2
+            tq[4 * half + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);  // byte 3
+        }
+        asm volatile("" ::: "memory");   // the previous tile's V^T reads come first
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+            vt[(4 * vd + dd) * kVtStride + 2 * vh] = tq[dd];
+            vt[(4 * vd + dd) * kVtStride + 2 * vh + 1] = tq[4 + dd];
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const v4s_t va = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, whi, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, wmid, acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, wlo, acc[dt], 0, 0, 0);
+        }
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
+
+    S = sum_rows32(sum_rows16(S));   // the four lane groups hold different tokens
+    if (!live) return;
+    float *o = p.out + ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        // one division at the end, per element
+        const v4f_t a = acc[dt];
+        reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] =
+            S > 0.0f ? make_float4(a[0] / S, a[1] / S, a[2] / S, a[3] / S) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int nq, const int32_t *q_start,
+                          int total_q, int max_new, const float *q, float scale, float *out, int32_t *dev_status,
+                          hipStream_t stream)
+{
+    PrefillParams p;
+    p.cache.k_codes = layer.k_codes;
+    p.cache.v_codes = layer.v_codes;
+    p.cache.k_scale = layer.k_scale;
+    p.cache.v_scale = layer.v_scale;
+    p.cache.nkv = layer.nkv_heads;
+    p.cache.kv_bs_log2 = ilog2(layer.kv_bs);
+    p.cache.num_blocks = layer.num_blocks;
+    p.block_table = batch.block_table;
+    p.seq_lens = batch.seq_lens;
+    p.q_start = q_start;
+    p.q = q;
+    p.out = out;
+    p.dev_status = dev_status;
+    p.nq = nq;
+    p.max_blocks_per_seq = batch.max_blocks_per_seq;
+    p.max_seq_len = batch.max_seq_len;
+    p.max_new = max_new;
+    p.total_q = total_q;
+    p.log2g = ilog2(nq / layer.nkv_heads);
+    p.sc = (float)((double)scale * 1.4426950408889634);
+    const long long rows = (long long)max_new * (nq / layer.nkv_heads);
+    const dim3 grid(batch.batch * layer.nkv_heads,
+                    (unsigned)((rows + kPrefillRows * kPrefillWaves - 1) / (kPrefillRows * kPrefillWaves)));
+    void *args[] = {&p};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&q8_prefill_kernel), grid,
+                                         dim3(64 * kPrefillWaves), args, 0, stream);
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace q8kv

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 2
+#define Q8KV_ABI_VERSION 3
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -206,6 +206,33 @@ q8_status q8_decode_attn_sparse(const q8_kv_layer *layer, const q8_batch *batch,
                                 const float *q, float scale, float *out, int32_t topk,
                                 int32_t *selected, void *workspace, size_t workspace_bytes,
                                 int32_t *dev_status, void *stream);
+
+/* Batched prefill attention over the q8 cache ("why long context must be
+ * sparse" §1-§2: the exact batched path; a batch of new tokens scores against
+ * the whole history).  For each sequence b, its nb_b = q_start[b + 1] -
+ * q_start[b] new tokens are the last nb_b positions of its cache (appended
+ * with q8_kv_append before this call, so seq_lens[b] counts them).  Query row
+ * r, q_start[b] <= r < q_start[b + 1], sits at position
+ *     p = seq_lens[b] - nb_b + (r - q_start[b])
+ * and attends causally to positions 0..p: for every query head h,
+ *     out[r][h] = the q8 single-pass attention ("9-2" §2) of q[r][h] over
+ *                 tokens 0..p of KV head h / (nq_heads / nkv_heads),
+ * with the decode's Q quantizer, scores, softmax and one final division
+ * (products on the matrix cores; the value products are exact, only the fp32
+ * summation order differs from q8_decode_attn over the same tokens).
+ *   q_start : device int32 [batch + 1], q_start[0] = 0, nondecreasing,
+ *             q_start[batch] = total_q;
+ *   q, out  : device fp32 [total_q][nq_heads][head_dim], 16-byte aligned;
+ *   max_new : host bound on every nb_b (sizes the launch), in [0, max_seq_len].
+ * Device-detected: a sequence with q_start out of order or outside
+ * [0, total_q], nb_b > seq_lens[b], nb_b > max_new, or seq_lens[b] outside
+ * [0, max_seq_len] sets Q8_DEV_BAD_SEQ_LEN and its rows (when its q_start
+ * range is inside [0, total_q], up to max_new of them) are zeros; a bad block
+ * id sets Q8_DEV_BAD_BLOCK_ID and its tokens are left out.  No workspace;
+ * nothing allocated; total_q == 0 or max_new == 0 enqueues nothing. */
+q8_status q8_prefill_attn(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                          const int32_t *q_start, int32_t total_q, int32_t max_new,
+                          const float *q, float scale, float *out, int32_t *dev_status, void *stream);
 
 /* Test hook: the Q quantizer of the decode kernel ("9-2" §2 segment 1) on
  * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("q8_kv_append", "q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge",
                  "q8_decode_attn_workspace_bytes", "q8_decode_attn_auto_parts", "q8_quantize_q",
-                 "q8_qk_block_partials", "q8_status_string", "q8_last_error", "q8_abi_version"):
+                 "q8_qk_block_partials", "q8_status_string", "q8_last_error", "q8_abi_version",
+                 "q8_decode_attn_f32", "q8_decode_attn_sparse", "q8_prefill_attn"):
         assert want in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 2
+    assert q8.abi_version() == 3
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
@@ -186,3 +187,24 @@ def test_sparse_validation(q8):
     assert need >= 4 * 16 * ((300 + 31) // 32) * 4
     assert call_sparse(q8, L, B, ws_bytes=need - 1) == -3
     assert q8.decode_attn_sparse_workspace_bytes(L, B, 16, 1) == 0
+
+
+def call_prefill(q8, L, B, nq=16, q_start=FAKE, total_q=64, max_new=32, q=FAKE, out=FAKE):
+    return q8.lib().q8_prefill_attn(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, q_start, total_q, max_new, q,
+                                    0.088, out, None, None)
+
+
+def test_prefill_validation(q8):
+    L, B = layer(q8), batch(q8)
+    assert call_prefill(q8, L, B, nq=24) == -2
+    assert call_prefill(q8, L, B, nq=0) == -1
+    assert call_prefill(q8, L, B, q_start=0) == -1
+    assert call_prefill(q8, L, B, q_start=FAKE + 2) == -1
+    assert call_prefill(q8, L, B, total_q=-1) == -1
+    assert call_prefill(q8, L, B, max_new=-1) == -1
+    assert call_prefill(q8, L, B, max_new=301) == -1     # above max_seq_len
+    assert call_prefill(q8, L, B, q=FAKE + 8) == -1
+    assert call_prefill(q8, L, B, out=0) == -1
+    assert call_prefill(q8, L, B, total_q=0) == 0        # nothing to do, nothing enqueued
+    assert call_prefill(q8, L, B, max_new=0) == 0
+    assert call_prefill(q8, layer(q8, kv_bs=24), B) == -2
