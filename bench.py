@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak, vendor figure (no sparsity)
 POOL_TOKENS = 65536            # N(0,1) source rows the history is appended from
 FILL_CHUNK = 32768
 
@@ -40,10 +41,11 @@ def parse():
     ap.add_argument("--nparts", type=int, default=0, help="decode partitions (0 = automatic)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("q8", "f32", "sparse"), default="q8",
+    ap.add_argument("--path", choices=("q8", "f32", "sparse", "prefill"), default="q8",
                     help="q8: the q8 cache (default); f32: the fp32 mirror and its exact decode "
                          "(the append then writes the mirror too); sparse: block-sparse decode (top-k "
-                         "32-token blocks per query head by probe)")
+                         "32-token blocks per query head by probe); prefill: batched causal prefill of "
+                         "the workload's new tokens (a qwen2b_prefill_* workload)")
     ap.add_argument("--topk", type=int, default=32, help="blocks kept per query head (--path sparse)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
@@ -282,6 +284,172 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     }
 
 
+def prefill_flops(w: workloads.Workload, lens: np.ndarray) -> int:
+    """Algorithmic flops of one layer's prefill attention: for every query row
+    at position p and query head, p + 1 keys, each 128 multiply-adds for the
+    score and 128 for the weighted V (2 flops per multiply-add)."""
+    nb = w.append_per_step
+    n = lens.astype(np.int64)
+    keys = nb * (n - nb) + nb * (nb + 1) // 2   # sum over the new rows of (p + 1)
+    return int(keys.sum()) * w.nq * 4 * w.head_dim
+
+
+def measure_prefill(torch, q8, dev, w, layers, steps, warmup, eager=False):
+    """A prefill step: per layer, append the workload's new tokens (the last
+    append_per_step positions of every sequence) and run q8_prefill_attn over
+    them.  Same structure as measure(): whole steps as one HIP graph, then an
+    eager pass with HIP events around each kernel."""
+    lens = workloads.seq_lens(w)
+    nb = w.append_per_step
+    assert nb > 1 and np.all(lens >= nb), "not a prefill workload"
+    kv_bs = w.kv_bs
+    B, nq, nkv, hd = w.batch, w.nq, w.nkv, w.head_dim
+    scale = float(workloads.softmax_scale(hd))
+    t_setup = time.perf_counter()
+    table, nblocks = workloads.block_table(lens, kv_bs, w.seed)
+    table_t = torch.from_numpy(table).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    batch = q8.make_batch(table_t, lens_t, int(lens.max()))
+    pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev) for _ in range(layers)]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    # history (positions below n_b - nb) from a source pool, as in measure()
+    hist = [(b, n - nb) for b, n in enumerate(lens) if n > nb]
+    if hist:
+        src_k = workloads.kv_pool_torch(w, POOL_TOKENS + FILL_CHUNK, gen, dev)
+        src_v = workloads.kv_pool_torch(w, POOL_TOKENS + FILL_CHUNK, gen, dev)
+        hist_seq = torch.from_numpy(np.concatenate([np.full(h, b, np.int32) for b, h in hist])).to(dev)
+        hist_pos = torch.from_numpy(np.concatenate([np.arange(h, dtype=np.int32) for _, h in hist])).to(dev)
+        rng = np.random.default_rng(w.seed)
+        for pool in pools:
+            for c0 in range(0, hist_seq.numel(), FILL_CHUNK):
+                c1 = min(hist_seq.numel(), c0 + FILL_CHUNK)
+                off = int(rng.integers(0, POOL_TOKENS))
+                q8.kv_append(pool, batch, hist_seq[c0:c1], hist_pos[c0:c1], src_k[off:off + c1 - c0],
+                             src_v[off:off + c1 - c0], dev_status=status)
+        del src_k, src_v
+    T = B * nb
+    new_seq = torch.from_numpy(np.repeat(np.arange(B, dtype=np.int32), nb)).to(dev)
+    new_pos = torch.from_numpy(np.concatenate([np.arange(n - nb, n, dtype=np.int32) for n in lens])).to(dev)
+    q_start = torch.from_numpy((np.arange(B + 1) * nb).astype(np.int32)).to(dev)
+    new_k = torch.randn((layers, T, nkv, hd), generator=gen, device=dev)
+    new_v = torch.randn((layers, T, nkv, hd), generator=gen, device=dev)
+    qs = torch.randn((layers, T, nq, hd), generator=gen, device=dev)
+    outs = torch.empty((layers, T, nq, hd), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status set during fill"
+    setup_s = time.perf_counter() - t_setup
+
+    def step_plain():
+        for li in range(layers):
+            q8.kv_append(pools[li], batch, new_seq, new_pos, new_k[li], new_v[li], dev_status=status)
+            q8.prefill_attn(pools[li], batch, nq, q_start, nb, qs[li], scale, outs[li], dev_status=status)
+
+    graph = None
+    if not eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_plain()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_plain()
+    run = graph.replay if graph is not None else step_plain
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0, "device status set during timing"
+
+    stream = torch.cuda.current_stream()
+    ev_steps = max(2, min(steps, 5))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_steps * layers)]
+    for s_ in range(ev_steps + 1):
+        for li in range(layers):
+            e = ev[(s_ - 1) * layers + li] if s_ > 0 else None
+            if e: e[0].record(stream)
+            q8.kv_append(pools[li], batch, new_seq, new_pos, new_k[li], new_v[li], dev_status=status)
+            if e: e[1].record(stream)
+            q8.prefill_attn(pools[li], batch, nq, q_start, nb, qs[li], scale, outs[li], dev_status=status)
+            if e: e[2].record(stream)
+    torch.cuda.synchronize()
+    t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    t_prefill = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    del pools, outs, qs, new_k, new_v
+    return {"lens": lens, "table": table, "nblocks": nblocks, "layers": layers, "ms_per_step": wall * 1e3 / steps,
+            "t_append": t_append, "t_prefill": t_prefill, "graph": graph is not None, "setup_s": setup_s}
+
+
+def prefill_cpu_baseline(w, lens):
+    """The oracle's prefill on a bounded sample: the first sequence's first
+    rows (positions from n - nb on) of one layer, all query heads, repeated
+    for ~10 s; in algorithmic TFLOP/s."""
+    import oracle
+    nb = w.append_per_step
+    n = int(lens[0])
+    rows = min(nb, 256)
+    sample_len = n - nb + rows   # a cache holding the history and the sampled rows
+    rng = np.random.default_rng(w.seed)
+    k = rng.standard_normal((1, sample_len, w.nkv, w.head_dim), dtype=np.float32)
+    v = rng.standard_normal((1, sample_len, w.nkv, w.head_dim), dtype=np.float32)
+    q = rng.standard_normal((rows, w.nq, w.head_dim), dtype=np.float32)
+    tab, nbl = workloads.block_table(np.array([sample_len], np.int32), w.kv_bs, w.seed)
+    cache = oracle.build_cache(k, v, np.array([sample_len], np.int32), tab, nbl, w.kv_bs)
+    threads = min(oracle.threads_available(), 16)
+    keys = rows * (sample_len - rows) + rows * (rows + 1) // 2
+    flops = keys * w.nq * 4 * w.head_dim
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill_attn(cache, q, [0, rows], w.nq, float(workloads.softmax_scale(w.head_dim)), nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} query rows at positions {n - nb}..{n - nb + rows - 1} of one sequence, all "
+                      f"{w.nq} query heads, one layer, oracle prefill_attn repeated {reps}x in {dt:.1f} s"}
+
+
+def prefill_main(args, torch, q8, dev):
+    w = workloads.WORKLOADS[args.workload]
+    layers = args.layers or w.layers
+    m = measure_prefill(torch, q8, dev, w, layers, args.steps, args.warmup, args.eager)
+    lens = m["lens"]
+    flops = prefill_flops(w, lens)
+    ms = m["ms_per_step"]
+    value = layers * flops / (ms * 1e-3) / 1e12
+    pre_us = float(m["t_prefill"].mean())
+    achieved = flops / (pre_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "q8_prefill_kernel", "kernel_us": round(pre_us, 2), "algorithmic_flops_per_launch": flops}
+    cpu = None if args.no_cpu_baseline else prefill_cpu_baseline(w, lens)
+    line = {
+        "metric": "q8 prefill-attn achieved TFLOP/s (algorithmic: 4 * 128 flops per query head and visible key)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8/bf16x3/fp32", "data": "synthetic",
+        "config": {
+            "workload": w.name, "path": "prefill", "batch": w.batch, "nq_heads": w.nq, "nkv_heads": w.nkv,
+            "head_dim": w.head_dim, "kv_bs": w.kv_bs, "layers": layers, "ctx": list(w.lens),
+            "new_tokens_per_seq": w.append_per_step,
+            "us_per_layer_step": round(ms * 1e3 / layers, 2),
+            "us_append": round(float(np.median(m["t_append"])), 2),
+            "us_prefill": round(float(np.median(m["t_prefill"])), 2),
+            "flops_per_layer": flops, "graph": m["graph"], "setup_s": round(m["setup_s"], 1),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def sweep_entry(w, m):
     step_bytes = m["layers"] * (m["attn_bytes"] + m["append_bytes"])
     gbs = step_bytes / (m["ms_per_step"] * 1e-3) / 1e9
@@ -318,6 +486,13 @@ def main():
         copy_probe(torch, dev, args.copy_probe, args.steps)
         return
     w = workloads.WORKLOADS[args.workload]
+    if args.path == "prefill":
+        if w.append_per_step <= 1:
+            raise SystemExit("--path prefill needs a prefill workload (qwen2b_prefill_*)")
+        prefill_main(args, torch, q8, dev)
+        return
+    if w.append_per_step > 1:
+        raise SystemExit(f"{w.name} is a prefill workload: use --path prefill")
     layers = args.layers or w.layers
     m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk)
     lens = m["lens"]

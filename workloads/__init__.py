@@ -51,6 +51,13 @@ WORKLOADS = {
     "qwen8b_b128_stress": Workload("qwen8b_b128_stress", 32, 8, 128, 36,
                                    ("uniform_forced", 1, 4096, (1, 2, 31, 32, 33, 63, 64, 65)),
                                    "student3x3", 1006),
+    # batched prefill: append_per_step new tokens per sequence are the queries
+    # (the last positions of each sequence).  The pages' prefill table runs
+    # whole prompts of 506 / 2046 / 4059 tokens on the 2B model.
+    "qwen2b_prefill_n4059": Workload("qwen2b_prefill_n4059", 16, 8, 1, 28, ("fixed", 4059), "normal", 1007,
+                                     append_per_step=4059),
+    "qwen2b_prefill_b8_c512": Workload("qwen2b_prefill_b8_c512", 16, 8, 8, 28, ("fixed", 4096), "normal", 1008,
+                                       append_per_step=512),
 }
 
 
