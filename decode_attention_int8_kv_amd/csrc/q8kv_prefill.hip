@@ -91,6 +91,75 @@ __device__ __forceinline__ void split_bf16x3(const float (&w)[4], v4s_t &hi, v4s
                                               __builtin_amdgcn_perm(l[3], l[2], 0x07060302u)));
 }
 
+// Loads of one 16-token key tile: K bytes for the score MFMAs, the K and V
+// steps of tokens t0 + 4 lg + e, and 4 bytes of 8 V rows for the transpose.
+struct KeyTile {
+    long ka[4];
+    float ks[4], vs[4];
+    uint32_t vw[8];
+    bool good_lo, good_hi;   // block ids of tokens t0 .. t0 + 7 and t0 + 8 .. t0 + 15 are valid
+};
+
+// Big (kv_bs >= 16): the tile lies in one physical block, which holds only
+// this sequence's rows; the bases are scalar, the lane offsets fixed, and
+// rows past the sequence end inside the block are read (they may hold any
+// bytes) and masked by the caller.  Otherwise (kv_bs = 8) the tile spans
+// two blocks and tokens are clamped to n - 1.
+template <bool Big>
+__device__ __forceinline__ void load_key_tile(const PrefillParams &p, const const_i32 *sbt, int kh, int t0, int n,
+                                              int j, int lg, int vh, int vd, KeyTile &kt)
+{
+    const int nkv = p.cache.nkv, row_bytes = nkv * kHeadDim;
+    const int log2bs = p.cache.kv_bs_log2, bmask = (1 << log2bs) - 1;
+    if (Big) {
+        const int id = sbt[t0 >> log2bs];   // t0 <= n - 1
+        const bool good = (unsigned)id < (unsigned)p.cache.num_blocks;
+        kt.good_lo = kt.good_hi = good;
+        const size_t row0 = ((size_t)(good ? id : 0) << log2bs) + (size_t)(t0 & bmask);
+        const int8_t *kb = p.cache.k_codes + row0 * row_bytes + kh * kHeadDim;
+        const int8_t *vb = p.cache.v_codes + row0 * row_bytes + kh * kHeadDim;
+        const size_t s0 = (((size_t)(good ? id : 0) * nkv + kh) << log2bs) + (size_t)(t0 & bmask);
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta)
+            kt.ka[beta] = *reinterpret_cast<const long *>(kb + j * row_bytes + 32 * beta + 8 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kt.ks[e] = p.cache.k_scale[s0 + 4 * lg + e];
+            kt.vs[e] = p.cache.v_scale[s0 + 4 * lg + e];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            kt.vw[u] = *reinterpret_cast<const uint32_t *>(vb + (8 * vh + u) * row_bytes + 4 * vd);
+    } else {
+        int id0 = sbt[min(t0, n - 1) >> log2bs];
+        int id1 = sbt[min(t0 + 8, n - 1) >> log2bs];
+        kt.good_lo = (unsigned)id0 < (unsigned)p.cache.num_blocks;
+        kt.good_hi = (unsigned)id1 < (unsigned)p.cache.num_blocks;
+        id0 = kt.good_lo ? id0 : 0;
+        id1 = kt.good_hi ? id1 : 0;
+        auto row_of = [&](int t) {   // t in [t0, t0 + 16), clamped to n - 1
+            const int id = ((t - t0) >> 3) ? id1 : id0;
+            return ((size_t)id << log2bs) + (size_t)(t & bmask);
+        };
+        const int8_t *krow = p.cache.k_codes + row_of(min(t0 + j, n - 1)) * row_bytes + kh * kHeadDim + 8 * lg;
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) kt.ka[beta] = *reinterpret_cast<const long *>(krow + 32 * beta);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t row = row_of(min(t0 + 4 * lg + e, n - 1));
+            const size_t sidx = (((row >> log2bs) * nkv + kh) << log2bs) + (row & bmask);
+            kt.ks[e] = p.cache.k_scale[sidx];
+            kt.vs[e] = p.cache.v_scale[sidx];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t row = row_of(min(t0 + 8 * vh + u, n - 1));
+            kt.vw[u] = *reinterpret_cast<const uint32_t *>(p.cache.v_codes + row * row_bytes + kh * kHeadDim + 4 * vd);
+        }
+    }
+}
+
+template <bool Big>
 __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillParams p)
 {
     __shared__ uint32_t vt_all[kPrefillWaves][kHeadDim * kVtStride];
@@ -157,12 +226,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     }
 
     const const_i32 *sbt = (const const_i32 *)(p.block_table + (size_t)b * p.max_blocks_per_seq);
-    const int log2bs = p.cache.kv_bs_log2, bmask = (1 << log2bs) - 1;
-    const int row_bytes = nkv * kHeadDim;
-    const int8_t *kbase = p.cache.k_codes + (size_t)kh * kHeadDim;
-    const int8_t *vbase = p.cache.v_codes + (size_t)kh * kHeadDim;
     const int vh = lane >> 5, vd = lane & 31;   // V staging: tokens 8 vh + u, dims 4 vd .. 4 vd + 3
 
+    // M is a reference max per query: the weights exp2(s - M) may exceed 1 by
+    // up to 2^kLazyRescale, and S and the accumulators are rescaled only when
+    // some query's tile max rises above its M by more than that (the result
+    // is the same quantity; only rounding differs)
+    constexpr float kLazyRescale = 8.0f;
     float M = -INFINITY, S = 0.0f;
     v4f_t acc[8];
 #pragma unroll
@@ -171,82 +241,48 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
 
     for (int kt = 0; kt < nkt; ++kt) {
         const int t0 = kt * kKeyTile;
-        // Block ids of the tile's two 8-token halves (kv_bs >= 8 keeps each
-        // half in one block).  Tokens are clamped to n - 1 >= t0, so every
-        // address is inside the sequence's blocks; a bad id reads block 0 and
-        // its tokens are masked.
-        int id0 = sbt[min(t0, n - 1) >> log2bs];
-        int id1 = sbt[min(t0 + 8, n - 1) >> log2bs];
-        const bool good0 = (unsigned)id0 < (unsigned)p.cache.num_blocks;
-        const bool good1 = (unsigned)id1 < (unsigned)p.cache.num_blocks;
-        bad = bad || !good0 || (t0 + 8 <= p_hi && !good1);
-        id0 = good0 ? id0 : 0;
-        id1 = good1 ? id1 : 0;
-        auto row_of = [&](int t) {   // t in [t0, t0 + 16), already clamped to n - 1
-            const int id = ((t - t0) >> 3) ? id1 : id0;
-            return ((size_t)id << log2bs) + (size_t)(t & bmask);
-        };
-        auto good_of = [&](int t) { return ((t - t0) >> 3) ? good1 : good0; };
-
-        // K rows (A operand): token t0 + j, bytes 32 beta + 8 lg
-        const int8_t *krow = kbase + row_of(min(t0 + j, n - 1)) * row_bytes + 8 * lg;
-        long ka[4];
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) ka[beta] = *reinterpret_cast<const long *>(krow + 32 * beta);
-        // steps of tokens t0 + 4 lg + e
-        float ks[4], vs[4];
-        bool tok_ok[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * lg + e, tc = min(t, n - 1);
-            const size_t row = row_of(tc);
-            const size_t sidx = ((((row >> log2bs) * nkv + kh)) << log2bs) + (row & bmask);
-            ks[e] = p.cache.k_scale[sidx];
-            vs[e] = p.cache.v_scale[sidx];
-            tok_ok[e] = t <= pos && good_of(tc);
-        }
-        // V rows for the transpose: 4 bytes (dims 4 vd ..) of tokens t0 + 8 vh + u
-        uint32_t vw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const size_t row = row_of(min(t0 + 8 * vh + u, n - 1));
-            vw[u] = *reinterpret_cast<const uint32_t *>(vbase + row * row_bytes + 4 * vd);
-        }
+        KeyTile tl;
+        load_key_tile<Big>(p, sbt, kh, t0, n, j, lg, vh, vd, tl);
+        bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
 
         // scores of query j with tokens t0 + 4 lg + e
         v4i_t c[4];
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta)
-            c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka[beta], qb[beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
+            c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(tl.ka[beta], qb[beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
         float s[4];
+        uint32_t keep[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 4 * lg + e;
+            keep[e] = (t <= pos && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
             const float x0 = (float)c[0][e] * qs[0], x1 = (float)c[1][e] * qs[1];
             const float x2 = (float)c[2][e] * qs[2], x3 = (float)c[3][e] * qs[3];
             const float y = (x0 + x1) + (x3 + x2);
-            // branch-free mask (a select here becomes a divergent branch)
-            const uint32_t keep = tok_ok[e] ? 0xffffffffu : 0u;
-            s[e] = __uint_as_float(bitsel(keep, __float_as_uint(y * (ks[e] * p.sc)), 0xff800000u));
+            // branch-free mask (a select here becomes a divergent branch); a
+            // masked token's step may be any bits, even NaN
+            s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(y * (tl.ks[e] * p.sc)), 0xff800000u));
         }
         float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        m = max_rows32(max_rows16(m));   // the tile max of query j (token 0 keeps M finite from tile 0)
-        const float Mn = fmaxf(M, m);
-        // 0 on the first tile with a finite max; 1 while every token so far is masked
-        const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-        M = Mn;
+        m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
+        const bool grow = m > M + kLazyRescale;   // also true on the first tile with a finite max
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float Mn = grow ? m : M;
+            const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+            M = Mn;
+            S *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+        }
         float w[4], psum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // a masked score is -inf: exp2(-inf - M) = 0 for finite M; while M
-            // is still -inf every score is masked and the weight must be 0
-            const float pw = __uint_as_float(bitsel(tok_ok[e] ? 0xffffffffu : 0u,
-                                                    __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M)), 0u));
+            // masked: weight 0 (M may still be -inf, and the step may be NaN)
+            const float pw = __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M)), 0u));
             psum += pw;
-            w[e] = pw * vs[e];
+            w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
         }
-        S = S * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+        S += psum;
         v4s_t whi, wmid, wlo;
         split_bf16x3(w, whi, wmid, wlo);
 
@@ -254,7 +290,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         uint32_t tq[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const uint32_t a0 = vw[4 * half], a1 = vw[4 * half + 1], a2 = vw[4 * half + 2], a3 = vw[4 * half + 3];
+            const uint32_t a0 = tl.vw[4 * half], a1 = tl.vw[4 * half + 1], a2 = tl.vw[4 * half + 2],
+                           a3 = tl.vw[4 * half + 3];
             const uint32_t x01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.b0 a1.b0 a0.b1 a1.b1
             const uint32_t x01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.b2 a1.b2 a0.b3 a1.b3
             const uint32_t x23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
@@ -322,7 +359,9 @@ hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int n
     const dim3 grid(batch.batch * layer.nkv_heads,
                     (unsigned)((rows + kPrefillRows * kPrefillWaves - 1) / (kPrefillRows * kPrefillWaves)));
     void *args[] = {&p};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&q8_prefill_kernel), grid,
+    const void *fn = layer.kv_bs >= kKeyTile ? reinterpret_cast<const void *>(&q8_prefill_kernel<true>)
+                                             : reinterpret_cast<const void *>(&q8_prefill_kernel<false>);
+    const hipError_t e = hipLaunchKernel(fn, grid,
                                          dim3(64 * kPrefillWaves), args, 0, stream);
     return e != hipSuccess ? e : hipGetLastError();
 }
