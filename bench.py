@@ -571,9 +571,8 @@ def copy_probe(torch, dev, mib, reps):
     print(json.dumps({"copy_probe_bytes": mib * 2 ** 20, "reps": reps}), flush=True)
 
 
-# the sources the q8 decode partial kernel and its launch are built from
-KERNEL_SOURCES = ("q8kv_api.hip", "q8kv_decode.hip", "q8kv_device.hpp", "q8kv_internal.hpp", "q8kv_ranges.hpp",
-                  "q8kv_tile.hpp")
+# the sources that define the q8 decode partial kernel and its launch plan
+KERNEL_SOURCES = ("q8kv_decode.hip", "q8kv_device.hpp", "q8kv_plan.hpp", "q8kv_ranges.hpp", "q8kv_tile.hpp")
 
 
 def kernel_hash() -> str:

@@ -19,12 +19,20 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The prefill kernel keeps its matrix-core accumulators
+# in VGPRs (the MFMAs read and write them there), so the rare rescale of the
+# accumulators does not make the compiler copy them between register files
+# on every key tile.
+FILE_FLAGS = {
+    "q8kv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-o", OUT + ".tmp", *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,6 +43,24 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source to an object (in parallel, with its own flags),
+    then link the shared library."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="q8kv_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(f) + ".o") for f in srcs]
+        compile_flags = [f for f in FLAGS if f != "-shared"]
+        cmds = [[HIPCC, *compile_flags, *FILE_FLAGS.get(os.path.basename(f), []), *extra, "-c", "-o", o, f]
+                for f, o in zip(srcs, objs)]
+        with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+            for fut in [ex.submit(_run, c, verbose) for c in cmds]:
+                fut.result()
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp", *objs], verbose)
     os.replace(OUT + ".tmp", OUT)
     return OUT
 

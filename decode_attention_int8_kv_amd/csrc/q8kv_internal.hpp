@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "q8kv.h"
+#include "q8kv_plan.hpp"
 
 namespace q8kv {
 
@@ -16,18 +17,6 @@ inline int ilog2(int v)
     while ((1 << (r + 1)) <= v) ++r;
     return r;
 }
-
-// Resolved launch plan of one decode call.
-struct DecodePlan {
-    int nparts;          // equal ranges of the batch's tile sequence
-    int head_groups;     // workgroups per range (8 KV heads each)
-    int waves;           // waves per decode workgroup
-    int merge_waves;     // waves per merge workgroup
-    size_t off_prefix, off_ms, off_acc, bytes;
-};
-
-DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);
-int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq);
 
 hipError_t launch_append(const q8_kv_layer &layer, const q8_batch &batch, int32_t n_tokens,
                          const int32_t *tok_seq, const int32_t *tok_pos, const float *k_new,

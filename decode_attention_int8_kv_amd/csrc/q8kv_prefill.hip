@@ -11,9 +11,10 @@
 // block partials P_beta, softmax over t <= p, weights times V codes and V
 // steps, one division at the end ("9-2 flash_attn_single_q_q8_neon" §2).
 //
-// A wave owns 16 query rows of one KV head: row rho = position * G + head of
-// the flattened (position, query head) list.  It walks the keys 0..p_max of
-// its rows in tiles of 16 tokens:
+// A wave owns 32 query rows of one KV head (two sets of 16): row rho =
+// position * G + head of the flattened (position, query head) list.  It
+// walks the keys 0..p_max of its rows in tiles of 16 tokens; each tile's
+// loads, V transpose and V operands serve both sets:
 //   scores  S^T = K Q^T with v_mfma_i32_16x16x32_i8, one instruction per
 //           32-block beta (A: token j's bytes 32 beta + [8 lg, 8 lg + 8) in
 //           lane (lg, j); B: the query codes in the same places), so lane
@@ -40,8 +41,9 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPrefillWaves = 4;   // 16-row query tiles per workgroup
-constexpr int kPrefillRows = 16;   // query rows per wave
+constexpr int kPrefillWaves = 4;   // query tiles per workgroup
+constexpr int kSets = 2;           // 16-row query sets per wave (share each key tile's loads and V operands)
+constexpr int kPrefillRows = 16 * kSets;   // query rows per wave
 constexpr int kKeyTile = 16;       // tokens per step
 constexpr int kVtStride = 5;       // dwords per dim row of the staged V^T tile (4 token quads + 1 pad)
 
@@ -179,13 +181,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         // a bad sequence: reported; its rows that this wave covers are zeros
         if (kh == 0 && tile == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
         if (range_ok) {
-            const int rho = tile * kPrefillRows + j;
-            if (rho < (nn << p.log2g)) {
-                const int i = rho >> p.log2g, g = rho & (G - 1);
-                float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int st = 0; st < kSets; ++st) {
+                const int rho = tile * kPrefillRows + 16 * st + j;
+                if (rho < (nn << p.log2g)) {
+                    const int i = rho >> p.log2g, g = rho & (G - 1);
+                    float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt)
+                        reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
         }
         return;
@@ -193,36 +198,45 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     const int rows = nn << p.log2g;
     if (tile * kPrefillRows >= rows) return;
 
-    // this lane's query row (clamped to a real row; lanes past the end are
-    // computed and discarded) and its position
-    const int rho = tile * kPrefillRows + j;
-    const bool live = rho < rows;
-    const int rr = live ? rho : rows - 1;
-    const int qi = rr >> p.log2g, qg = rr & (G - 1);
-    const int pos = n - nn + qi;
-    const size_t qrow = ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
+    // this lane's query row in each set (clamped to a real row; lanes past the
+    // end are computed and discarded) and its position
+    bool live[kSets];
+    int qi[kSets], qg[kSets], pos[kSets];
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        const int rho = tile * kPrefillRows + 16 * st + j;
+        live[st] = rho < rows;
+        const int rr = live[st] ? rho : rows - 1;
+        qi[st] = rr >> p.log2g;
+        qg[st] = rr & (G - 1);
+        pos[st] = n - nn + qi[st];
+    }
     const int p_hi = n - nn + (min(tile * kPrefillRows + kPrefillRows - 1, rows - 1) >> p.log2g);
     const int nkt = p_hi / kKeyTile + 1;
 
-    // query codes, the B operand of the score MFMAs: bytes 32 beta + [8 lg, 8 lg + 8)
-    long qb[4];
-    float qs[4];
+    // query codes, the B operands of the score MFMAs: bytes 32 beta + [8 lg, 8 lg + 8)
+    long qb[kSets][4];
+    float qs[kSets][4];
 #pragma unroll
-    for (int beta = 0; beta < 4; ++beta) {
-        const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
-        const float4 a = src[0], c = src[1];
-        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        float m = 0.0f;
+    for (int st = 0; st < kSets; ++st) {
+        const size_t qrow = ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-        m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
-        const BlockQuant bq = q_block_params(m);
-        int cd[8];
+        for (int beta = 0; beta < 4; ++beta) {
+            const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
+            const float4 a = src[0], c = src[1];
+            const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            float m = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cd[e] = q_code(x[e], bq.recip);
-        const uint32_t w0 = pack4_i8(cd[0], cd[1], cd[2], cd[3]), w1 = pack4_i8(cd[4], cd[5], cd[6], cd[7]);
-        qb[beta] = (long)(((uint64_t)w1 << 32) | w0);
-        qs[beta] = bq.qscale;
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+            m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
+            const BlockQuant bq = q_block_params(m);
+            int cd[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cd[e] = q_code(x[e], bq.recip);
+            const uint32_t w0 = pack4_i8(cd[0], cd[1], cd[2], cd[3]), w1 = pack4_i8(cd[4], cd[5], cd[6], cd[7]);
+            qb[st][beta] = (long)(((uint64_t)w1 << 32) | w0);
+            qs[st][beta] = bq.qscale;
+        }
     }
 
     const const_i32 *sbt = (const const_i32 *)(p.block_table + (size_t)b * p.max_blocks_per_seq);
@@ -233,10 +247,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     // some query's tile max rises above its M by more than that (the result
     // is the same quantity; only rounding differs)
     constexpr float kLazyRescale = 8.0f;
-    float M = -INFINITY, S = 0.0f;
-    v4f_t acc[8];
+    float M[kSets], S[kSets];
+    v4f_t acc[kSets][8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < kSets; ++st) {
+        M[st] = -INFINITY;
+        S[st] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[st][dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    }
     bool bad = false;
 
     for (int kt = 0; kt < nkt; ++kt) {
@@ -245,48 +264,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         load_key_tile<Big>(p, sbt, kh, t0, n, j, lg, vh, vd, tl);
         bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
 
-        // scores of query j with tokens t0 + 4 lg + e
-        v4i_t c[4];
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta)
-            c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(tl.ka[beta], qb[beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
-        float s[4];
-        uint32_t keep[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 4 * lg + e;
-            keep[e] = (t <= pos && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
-            const float x0 = (float)c[0][e] * qs[0], x1 = (float)c[1][e] * qs[1];
-            const float x2 = (float)c[2][e] * qs[2], x3 = (float)c[3][e] * qs[3];
-            const float y = (x0 + x1) + (x3 + x2);
-            // branch-free mask (a select here becomes a divergent branch); a
-            // masked token's step may be any bits, even NaN
-            s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(y * (tl.ks[e] * p.sc)), 0xff800000u));
-        }
-        float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
-        const bool grow = m > M + kLazyRescale;   // also true on the first tile with a finite max
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float Mn = grow ? m : M;
-            const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-            M = Mn;
-            S *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-        }
-        float w[4], psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // masked: weight 0 (M may still be -inf, and the step may be NaN)
-            const float pw = __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M)), 0u));
-            psum += pw;
-            w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
-        }
-        S += psum;
-        v4s_t whi, wmid, wlo;
-        split_bf16x3(w, whi, wmid, wlo);
-
-        // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim
+        // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim;
+        // the bf16 A operands are formed once and serve both query sets
         uint32_t tq[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -308,25 +287,79 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
             vt[(4 * vd + dd) * kVtStride + 2 * vh + 1] = tq[4 + dd];
         }
         asm volatile("" ::: "memory");
+        v4s_t va[8];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const v4s_t va = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, whi, acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, wmid, acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, wlo, acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < 8; ++dt) va[dt] = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
+
+#pragma unroll
+        for (int st = 0; st < kSets; ++st) {
+            // scores of query j of this set with tokens t0 + 4 lg + e
+            v4i_t c[4];
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta)
+                c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(tl.ka[beta], qb[st][beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
+            float s[4];
+            uint32_t keep[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = t0 + 4 * lg + e;
+                keep[e] = (t <= pos[st] && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
+                const float x0 = (float)c[0][e] * qs[st][0], x1 = (float)c[1][e] * qs[st][1];
+                const float x2 = (float)c[2][e] * qs[st][2], x3 = (float)c[3][e] * qs[st][3];
+                const float y = (x0 + x1) + (x3 + x2);
+                // branch-free mask (a select here becomes a divergent branch); a
+                // masked token's step may be any bits, even NaN
+                s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(y * (tl.ks[e] * p.sc)), 0xff800000u));
+            }
+            float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
+            const bool grow = m > M[st] + kLazyRescale;   // also true on the first tile with a finite max
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float Mn = grow ? m : M[st];
+                const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
+                M[st] = Mn;
+                S[st] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= alpha;
+            }
+            float w[4], psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // masked: weight 0 (M may still be -inf, and the step may be NaN)
+                const float pw =
+                    __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M[st])), 0u));
+                psum += pw;
+                w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
+            }
+            S[st] += psum;
+            v4s_t whi, wmid, wlo;
+            split_bf16x3(w, whi, wmid, wlo);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], whi, acc[st][dt], 0, 0, 0);
+                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], wmid, acc[st][dt], 0, 0, 0);
+                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], wlo, acc[st][dt], 0, 0, 0);
+            }
         }
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
 
-    S = sum_rows32(sum_rows16(S));   // the four lane groups hold different tokens
-    if (!live) return;
-    float *o = p.out + ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
+    float Ssum[kSets];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        // one division at the end, per element
-        const v4f_t a = acc[dt];
-        reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] =
-            S > 0.0f ? make_float4(a[0] / S, a[1] / S, a[2] / S, a[3] / S) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int st = 0; st < kSets; ++st) Ssum[st] = sum_rows32(sum_rows16(S[st]));   // lane groups hold different tokens
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        const float Sst = Ssum[st];
+        if (!live[st]) continue;
+        float *o = p.out + ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            // one division at the end, per element
+            const v4f_t a = acc[st][dt];
+            reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] =
+                Sst > 0.0f ? make_float4(a[0] / Sst, a[1] / Sst, a[2] / Sst, a[3] / Sst)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
 }
 
