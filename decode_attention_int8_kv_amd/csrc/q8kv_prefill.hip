@@ -169,7 +169,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     uint32_t *vt = vt_all[wave];
-    const int tile = blockIdx.y * kPrefillWaves + wave;
+    // the last query tiles (the longest key ranges under the causal mask) are
+    // dispatched first, so the short ones fill in behind them
+    const int tile = (gridDim.y - 1 - blockIdx.y) * kPrefillWaves + wave;
     const int G = 1 << p.log2g;
     const int j = lane & 15, lg = lane >> 4;
 
