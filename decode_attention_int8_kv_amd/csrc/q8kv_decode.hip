@@ -266,7 +266,7 @@ struct MergeParams {
 };
 
 constexpr int kMaxMergeWaves = 16;
-constexpr int kMergeBatch = 8;   // pieces whose loads a wave has in flight together
+constexpr int kMergeBatch = 16;  // pieces whose loads a wave has in flight together
 
 // One workgroup per (sequence, query head) whose tiles span several ranges:
 // combines the pieces' (M, S, acc) with the online-softmax rescale rule
@@ -286,6 +286,9 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
     const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    // a range can be empty (and write no record) only when there are more
+    // ranges than tiles; otherwise skip the two 64-bit divisions per record
+    const bool may_be_empty = p.nparts > total;
 
     float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
     for (int j0 = wave; j0 < np; j0 += kMergeBatch * waves) {
@@ -293,8 +296,8 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             const int j = j0 + u * waves, i = i0 + j;
-            // an empty range (more ranges than tiles) wrote no record
-            const bool have = j < np && part_start(i, total, p.nparts) != part_start(i + 1, total, p.nparts);
+            const bool have = j < np && (!may_be_empty || part_start(i, total, p.nparts) !=
+                                                              part_start(i + 1, total, p.nparts));
             if (have) {
                 const size_t r = ((size_t)i * 2 + (j == 0 ? slot0 : 0)) * p.nq + h;
                 ms[u] = p.ws_ms[r];
@@ -407,10 +410,12 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     DecodePlan pl;
     pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
     choose_width(layer.nkv_heads, nq / layer.nkv_heads, pl.waves, pl.head_groups);
-    // merge waves: about the number of pieces a sequence is cut into
-    long long per_seq = (long long)pl.nparts / (batch.batch > 0 ? batch.batch : 1) + 2;
+    // merge waves: enough that a sequence cut into about twice the average
+    // number of pieces is read in one round (kMergeBatch pieces per wave);
+    // more pieces take more rounds
+    const long long per_seq = 2LL * pl.nparts / (batch.batch > 0 ? batch.batch : 1) + 2;
     int mw = 1;
-    while (mw < kMaxMergeWaves && mw < per_seq) mw <<= 1;
+    while (mw < kMaxMergeWaves && (long long)mw * kMergeBatch < per_seq) mw <<= 1;
     pl.merge_waves = mw;
     pl.off_prefix = 0;
     pl.off_ms = align_up(sizeof(int32_t) * ((size_t)batch.batch + 1), 256);
