@@ -260,10 +260,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     }
     bool bad = false;
 
+    // tile kt + 1 (block id, K, steps, V rows) is in flight while tile kt is
+    // computed; past the end the last tile is reloaded, unused.  (Loading the
+    // V rows at the start of their own tile, or two tiles used in turn
+    // without the copy, both measured slower.)
+    KeyTile nxt;
+    load_key_tile<Big>(p, sbt, kh, 0, n, j, lg, vh, vd, nxt);
     for (int kt = 0; kt < nkt; ++kt) {
         const int t0 = kt * kKeyTile;
-        KeyTile tl;
-        load_key_tile<Big>(p, sbt, kh, t0, n, j, lg, vh, vd, tl);
+        const KeyTile tl = nxt;
+        load_key_tile<Big>(p, sbt, kh, min(kt + 1, nkt - 1) * kKeyTile, n, j, lg, vh, vd, nxt);
         bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
 
         // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim;
