@@ -214,6 +214,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         pos[st] = n - nn + qi[st];
     }
     const int p_hi = n - nn + (min(tile * kPrefillRows + kPrefillRows - 1, rows - 1) >> p.log2g);
+    const int pos_lo = n - nn + ((tile * kPrefillRows) >> p.log2g);   // the wave's smallest position
     const int nkt = p_hi / kKeyTile + 1;
 
     // query codes, the B operands of the score MFMAs: bytes 32 beta + [8 lg, 8 lg + 8)
@@ -271,6 +272,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         const KeyTile tl = nxt;
         load_key_tile<Big>(p, sbt, kh, min(kt + 1, nkt - 1) * kKeyTile, n, j, lg, vh, vd, nxt);
         bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
+        // every row of the wave sees all 16 tokens of the tile: no masks
+        const bool full = t0 + kKeyTile - 1 <= pos_lo && tl.good_lo && tl.good_hi;
 
         // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim;
         // the bf16 A operands are formed once and serve both query sets
@@ -310,14 +313,20 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
             uint32_t keep[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 4 * lg + e;
-                keep[e] = (t <= pos[st] && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
                 const float x0 = (float)c[0][e] * qs[st][0], x1 = (float)c[1][e] * qs[st][1];
                 const float x2 = (float)c[2][e] * qs[st][2], x3 = (float)c[3][e] * qs[st][3];
                 const float y = (x0 + x1) + (x3 + x2);
-                // branch-free mask (a select here becomes a divergent branch); a
-                // masked token's step may be any bits, even NaN
-                s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(y * (tl.ks[e] * p.sc)), 0xff800000u));
+                s[e] = y * (tl.ks[e] * p.sc);
+            }
+            if (!full) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = t0 + 4 * lg + e;
+                    keep[e] = (t <= pos[st] && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
+                    // branch-free mask (a select here becomes a divergent
+                    // branch); a masked token's step may be any bits, even NaN
+                    s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(s[e]), 0xff800000u));
+                }
             }
             float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
             m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
@@ -331,13 +340,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
                 for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= alpha;
             }
             float w[4], psum = 0.0f;
+            if (full) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // masked: weight 0 (M may still be -inf, and the step may be NaN)
-                const float pw =
-                    __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M[st])), 0u));
-                psum += pw;
-                w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
+                for (int e = 0; e < 4; ++e) {
+                    const float pw = __builtin_amdgcn_exp2f(s[e] - M[st]);
+                    psum += pw;
+                    w[e] = pw * tl.vs[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // masked: weight 0 (M may still be -inf, and the step may be NaN)
+                    const float pw =
+                        __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M[st])), 0u));
+                    psum += pw;
+                    w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
+                }
             }
             S[st] += psum;
             v4s_t whi, wmid, wlo;
