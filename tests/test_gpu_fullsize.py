@@ -1,0 +1,96 @@
+"""GPU parity at the full sizes of the batched workloads, in the launch
+configuration bench.py times (automatic partition count), on sampled rows.
+
+The caches are filled through q8_kv_append from GPU-drawn K/V with each
+workload's value distribution; the oracle then reads the codes and steps back
+and computes the sampled (sequence, query head) rows one by one.  Rows must
+satisfy max |gpu - oracle| <= 2e-5 * max |oracle| + 1e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_cases import DeviceCache, assert_rows_close, q8, say, torch
+
+pytestmark = pytest.mark.gpu
+SCALE = float(workloads.softmax_scale(128))
+CHUNK = 1 << 16   # tokens appended per call
+
+
+def _filled(w, seed, mirror=False):
+    """One layer of workload w on the GPU, every position appended."""
+    t, m = torch(), q8()
+    lens = workloads.seq_lens(w)
+    dc = DeviceCache(lens, w.nkv, w.kv_bs, seed=seed, garbage=False, mirror=mirror)
+    seqs = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(lens)])
+    poss = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(seed)
+    for c0 in range(0, seqs.size, CHUNK):
+        c1 = min(seqs.size, c0 + CHUNK)
+        k = workloads.kv_pool_torch(w, c1 - c0, gen, "cuda")
+        v = workloads.kv_pool_torch(w, c1 - c0, gen, "cuda")
+        m.kv_append(dc.layer, dc.batch, t.from_numpy(seqs[c0:c1]).cuda(), t.from_numpy(poss[c0:c1]).cuda(), k, v,
+                    dev_status=dc.status)
+    q = t.randn((w.batch, w.nq, 128), generator=gen, device="cuda")
+    assert dc.status_word() == 0
+    return dc, lens, q
+
+
+def _sample_seqs(lens, k, seed):
+    order = np.argsort(lens)
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(k, lens.size):
+        pick.add(int(rng.integers(0, lens.size)))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name,nseq", [("qwen2b_b64_ragged", 6), ("qwen8b_b32_n32k", 3), ("qwen8b_b1_n128k", 1),
+                                       ("qwen8b_b128_stress", 10)])
+def test_decode_full_size_sampled(name, nseq):
+    w = workloads.WORKLOADS[name]
+    say(f"[full size] {name}: batch {w.batch}, {w.nq}/{w.nkv} heads, {w.lens}")
+    dc, lens, q = _filled(w, seed=900 + len(name))
+    out = dc.decode(q, w.nq, SCALE, nparts=0).cpu().numpy()   # automatic partitions, as bench.py
+    assert dc.status_word() == 0
+    seqs = _sample_seqs(lens, nseq, 901)
+    if name == "qwen8b_b128_stress":
+        # also the forced short lengths
+        seqs = sorted(set(seqs) | {int(b) for b in np.nonzero(lens <= 65)[0][:8]})
+    rows = np.array([b * w.nq + h for b in seqs for h in range(w.nq)], np.int64)
+    want = oracle.decode_attn_rows(dc.host(), q.cpu().numpy(), w.nq, SCALE, rows)
+    worst = assert_rows_close(out.reshape(-1, 128)[rows], want, name)
+    say(f"  {rows.size} rows of sequences {seqs} (lengths {lens[seqs].tolist()}), worst err/tol {worst:.3f}")
+
+
+def test_sparse_full_size_ragged():
+    # every (sequence, query head) of the ragged 2B batch: kept blocks exact,
+    # outputs within tolerance
+    w = workloads.WORKLOADS["qwen2b_b64_ragged"]
+    say("[full size] block-sparse decode, qwen2b_b64_ragged, k = 32")
+    t, m = torch(), q8()
+    dc, lens, q = _filled(w, seed=910)
+    out = t.empty((w.batch, w.nq, 128), dtype=t.float32, device="cuda")
+    sel = t.empty((w.batch, w.nq, 32), dtype=t.int32, device="cuda")
+    ws = t.empty(m.decode_attn_sparse_workspace_bytes(dc.layer, dc.batch, w.nq, 32), dtype=t.uint8, device="cuda")
+    m.decode_attn_sparse(dc.layer, dc.batch, w.nq, q, SCALE, out, ws, topk=32, selected=sel, dev_status=dc.status)
+    assert dc.status_word() == 0
+    want, want_sel = oracle.decode_attn_sparse(dc.host(), q.cpu().numpy(), w.nq, SCALE, 32)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+    worst = assert_rows_close(out.cpu().numpy(), want, "sparse full size")
+    say(f"  {w.batch * w.nq} rows, worst err/tol {worst:.3f}")
+
+
+def test_f32_mirror_full_size_ragged():
+    w = workloads.WORKLOADS["qwen2b_b64_ragged"]
+    say("[full size] exact fp32 decode over the mirror, qwen2b_b64_ragged")
+    dc, lens, q = _filled(w, seed=920, mirror=True)
+    out = dc.decode_f32(q, w.nq, SCALE, nparts=0).cpu().numpy()
+    assert dc.status_word() == 0
+    seqs = _sample_seqs(lens, 6, 921)
+    rows = np.array([b * w.nq + h for b in seqs for h in range(w.nq)], np.int64)
+    want = oracle.decode_attn_f32(dc.host_mirror(), q.cpu().numpy(), w.nq, SCALE, rows_bh=rows)
+    worst = assert_rows_close(out.reshape(-1, 128)[rows], want, "f32 full size")
+    say(f"  {rows.size} rows, worst err/tol {worst:.3f}")
