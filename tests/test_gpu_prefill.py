@@ -113,3 +113,52 @@ def test_prefill_2b_prompt_4059_sampled():
     want = oracle.decode_attn(view, q[pos], nq, SCALE)
     w = assert_rows_close(got[pos], want, "sampled prefill rows")
     say(f"  {pos.size} positions, worst err/tol {w:.3f}")
+
+
+def test_prefill_graph_replays_match_eager():
+    # append of the new tokens + prefill captured in one HIP graph; every
+    # replay (with eager work and synchronizations between them) must equal
+    # the eager result bit for bit
+    say("[prefill] graph capture / replay")
+    t, m = torch(), q8()
+    lens = np.array([600, 97, 1200], np.int32)
+    nbs = np.array([600, 33, 100], np.int32)
+    k, v = dense_kv(lens, 8, seed=870)
+    dc = DeviceCache(lens, 8, 32, seed=870)
+    dc.append_dense(k, v)   # history and the new tokens' first values
+    qs = t.from_numpy(np.concatenate([[0], np.cumsum(nbs)]).astype(np.int32)).cuda()
+    total = int(nbs.sum())
+    seq = t.from_numpy(np.repeat(np.arange(3, dtype=np.int32), nbs)).cuda()
+    pos = t.from_numpy(np.concatenate([np.arange(n - c, n, dtype=np.int32) for n, c in zip(lens, nbs)])).cuda()
+    g_ = t.Generator(device="cuda")
+    g_.manual_seed(871)
+    kn = t.randn((total, 8, 128), generator=g_, device="cuda")
+    vn = t.randn((total, 8, 128), generator=g_, device="cuda")
+    q = t.randn((total, 16, 128), generator=g_, device="cuda")
+    out = t.empty((total, 16, 128), dtype=t.float32, device="cuda")
+
+    def body():
+        m.kv_append(dc.layer, dc.batch, seq, pos, kn, vn, dev_status=dc.status)
+        m.prefill_attn(dc.layer, dc.batch, 16, qs, int(nbs.max()), q, SCALE, out, dev_status=dc.status)
+
+    body()
+    t.cuda.synchronize()
+    eager = out.clone()
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        body()
+    t.cuda.current_stream().wait_stream(side)
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        body()
+    for i in range(4):
+        out.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(out, eager), f"replay {i}"
+    assert dc.status_word() == 0
+    # and the result is the oracle's
+    want = oracle.prefill_attn(dc.host(), q.cpu().numpy(), qs.cpu().numpy(), 16, SCALE)
+    assert_rows_close(eager.cpu().numpy(), want, "prefill after graph replays")
