@@ -245,12 +245,207 @@ piece_done:
     }
 }
 
+// Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores.
+// v_mfma_i32_16x16x64_i8 with A = the four heads' query codes (row 4 g + beta
+// holds head g's codes of 32-block beta, in k-group beta only) and B = K rows
+// (column j = token, lane (lg, j) holding bytes [32 lg, 32 lg + 32)) leaves
+// in lane (lg, j) the exact int32 partials of head lg with token j, four
+// blocks in four registers, two instructions per 16 tokens.  The score is
+// then formed once per (head, token) instead of in eight lanes: x_b = P_b *
+// qscale_b, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc).  The per-head
+// tile max is a row-of-16 reduction; each V lane (slot, c) receives its
+// head's (c % 4) weights with ds_bpermute and the value path is the 4x4x1
+// matrix-core outer product of attend_piece.
+typedef int v4i_dec __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    return fmaxf(v, dpp_f<kDppRor8>(v));
+}
+
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f<kDppQuadXor1>(v);
+    v += dpp_f<kDppQuadXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    return v + dpp_f<kDppRor8>(v);
+}
+
+__device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, int kh, int lane, int lt0, int lt1,
+                                                int n, bool whole, int part, int slot)
+{
+    constexpr int G = 4;
+    const int c = lane & 7, tslot = lane >> 3;
+    const int j = lane & 15, lg = lane >> 4;
+    const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
+
+    // A operands: head g = j / 4's codes of block beta = j % 4 in k-group
+    // beta (this lane's group lg), 16 bytes per MFMA; qs[r] = head lg's step
+    // of block r
+    v4i_dec qa[2];
+    float qs[4];
+    {
+        const int g = j >> 2, beta = j & 3;
+        uint4 lo, hi;
+        float step;
+        quantize_q_block(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim + 32 * beta, lo, hi, step);
+        const bool mine = lg == beta;
+        qa[0] = __builtin_bit_cast(v4i_dec, mine ? lo : make_uint4(0, 0, 0, 0));
+        qa[1] = __builtin_bit_cast(v4i_dec, mine ? hi : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qs[r] = __shfl(step, 4 * lg + r, 64);
+    }
+
+    float M[G], Sl = 0.0f;   // M per head (uniform); Sl: this lane's share of head lg's sum
+    v4f accm[16];
+#pragma unroll
+    for (int g = 0; g < G; ++g) M[g] = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) accm[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
+    const int log2bs = p.cache.kv_bs_log2;
+    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
+    // ds_bpermute byte addresses of the score lanes holding head c % 4's
+    // weight of token slot (+ 8)
+    const int src_lo = (16 * (c & 3) + tslot) * 4, src_hi = src_lo + 32;
+
+    auto process = [&](const Tile &t) {
+        float ks[4], vs[4];
+        tile_scales<0>(t, c, ks[0], vs[0]);
+        tile_scales<1>(t, c, ks[1], vs[1]);
+        tile_scales<2>(t, c, ks[2], vs[2]);
+        tile_scales<3>(t, c, ks[3], vs[3]);
+        float s[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            v4i_dec acc_i = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], __builtin_bit_cast(v4i_dec, t.k[2 * m]),
+                                                                  v4i_dec{0, 0, 0, 0}, 0, 0, 0);
+            acc_i = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], __builtin_bit_cast(v4i_dec, t.k[2 * m + 1]), acc_i,
+                                                          0, 0, 0);
+            const float x0 = (float)acc_i[0] * qs[0], x1 = (float)acc_i[1] * qs[1];
+            const float x2 = (float)acc_i[2] * qs[2], x3 = (float)acc_i[3] * qs[3];
+            const float y = (x0 + x1) + (x3 + x2);
+            const uint32_t keep = ((t.svalid >> m) & 1u) ? 0xffffffffu : 0u;
+            // a masked token's scale may be any bit pattern
+            s[m] = __uint_as_float(bitsel(keep, __float_as_uint(y * (t.ksm[m] * p.sc)), 0xff800000u));
+        }
+        // tile max per head: lanes 16 g .. 16 g + 15 hold head g
+        const float mrow = row16_max(fmaxf(s[0], s[1]));
+        float mg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mg[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrow), 16 * g));
+        float alpha[G];
+        bool rise = false;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            alpha[g] = 1.0f;
+            if (mg[g] > M[g]) {
+                alpha[g] = __builtin_amdgcn_exp2f(M[g] - mg[g]);
+                M[g] = mg[g];
+                rise = true;
+            }
+        }
+        if (rise) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) accm[jj][g] *= alpha[g];
+        }
+        // this lane's head: alpha, reference max
+        const float a_l = lg == 0 ? alpha[0] : lg == 1 ? alpha[1] : lg == 2 ? alpha[2] : alpha[3];
+        const float M_l = lg == 0 ? M[0] : lg == 1 ? M[1] : lg == 2 ? M[2] : M[3];
+        const float Mf = M_l == -INFINITY ? 0.0f : M_l;   // then every weight of the head is 0
+        const float p0 = __builtin_amdgcn_exp2f(s[0] - Mf), p1 = __builtin_amdgcn_exp2f(s[1] - Mf);
+        Sl = Sl * a_l + (p0 + p1);
+        // weights to the V lanes: token slot + 8 kk of head c % 4 sits in
+        // lane 16 (c % 4) + (slot + 8 kk) % 16, register kk / 2
+        float pw[4];
+        pw[0] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_lo, __float_as_int(p0)));
+        pw[1] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_hi, __float_as_int(p0)));
+        pw[2] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_lo, __float_as_int(p1)));
+        pw[3] = __int_as_float(__builtin_amdgcn_ds_bpermute(src_hi, __float_as_int(p1)));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t okm = ((t.valid >> kk) & 1u) ? 0xffffffffu : 0u;
+            const float wa = __uint_as_float(__float_as_uint(pw[kk] * vs[kk]) & okm);
+            const uint32_t words[4] = {t.v[kk].x, t.v[kk].y, t.v[kk].z, t.v[kk].w};
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) accm[jj] = mfma_outer4(wa, byte_f(words[jj >> 2], jj & 3), accm[jj]);
+        }
+        (void)m1;
+        (void)m2;
+    };
+
+    constexpr int D = 2;
+    const int ne = min(n, lt1 * kTile);
+    Tile t[D];
+    TileBlocks bl[D];
+    fetch_blocks(bt, log2bs, lt0 * kTile, ne, bl[0]);
+    load_tile_mf(p.cache, bl[0], lo, lane, lt0 * kTile, ne, p.dev_status, t[0]);
+    fetch_blocks(bt, log2bs, (lt0 + 1) * kTile, ne, bl[1]);
+    int lt = lt0;
+    while (true) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int nxt = (d + D - 1) % D;
+            load_tile_mf(p.cache, bl[nxt], lo, lane, (lt + D - 1) * kTile, ne, p.dev_status, t[nxt]);
+            fetch_blocks(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
+            process(t[d]);
+            if (++lt >= lt1) goto piece_done;
+        }
+    }
+piece_done:
+
+    float S[G], acc[G][16];
+    const float srow = row16_sum(Sl);
+#pragma unroll
+    for (int g = 0; g < G; ++g) S[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srow), 16 * g));
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[g][jj] = sum_over_slots(accm[jj][g]);
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (tslot != g) continue;
+        const int h = kh * G + g;
+        if (whole) {
+            // one division at the end ("9-2" §2 segment 3)
+            const float sg = S[g];
+            float4 *o = reinterpret_cast<float4 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 r;
+                r.x = sg > 0.0f ? acc[g][4 * q4 + 0] / sg : 0.0f;
+                r.y = sg > 0.0f ? acc[g][4 * q4 + 1] / sg : 0.0f;
+                r.z = sg > 0.0f ? acc[g][4 * q4 + 2] / sg : 0.0f;
+                r.w = sg > 0.0f ? acc[g][4 * q4 + 3] / sg : 0.0f;
+                o[q4] = r;
+            }
+        } else {
+            const size_t idx = ((size_t)part * 2 + slot) * p.nq + h;
+            float4 *a = reinterpret_cast<float4 *>(p.ws_acc + idx * kHeadDim + 16 * c);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                a[q4] = make_float4(acc[g][4 * q4], acc[g][4 * q4 + 1], acc[g][4 * q4 + 2], acc[g][4 * q4 + 3]);
+            if (c == 0) p.ws_ms[idx] = make_float2(M[g], S[g]);
+        }
+    }
+}
+
 template <int G, bool Big>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
     __shared__ int pref[kMaxBatch + 1];
     walk_ranges(p, pref, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
-        attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
+        if constexpr (G == 4 && Big)
+            attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
+        else
+            attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
     });
 }
 

@@ -214,6 +214,35 @@ __device__ __forceinline__ void quantize_q_quarter(const float *__restrict__ qro
     qscale = bq.qscale;
 }
 
+// Codes and step of one 32-float block of a query row, in one lane: the
+// decode kernel's query quantizer (step = max|x| * fl(1/127), code =
+// clamp(x * 127 / max|x|) truncated toward zero).
+__device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, uint4 &hi, float &qscale)
+{
+    const float4 *p = reinterpret_cast<const float4 *>(q32);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = p[i];
+        x[4 * i] = v.x;
+        x[4 * i + 1] = v.y;
+        x[4 * i + 2] = v.z;
+        x[4 * i + 3] = v.w;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));
+    const BlockQuant bq = q_block_params(m);
+    int cd[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cd[i] = q_code(x[i], bq.recip);
+    lo = make_uint4(pack4_i8(cd[0], cd[1], cd[2], cd[3]), pack4_i8(cd[4], cd[5], cd[6], cd[7]),
+                    pack4_i8(cd[8], cd[9], cd[10], cd[11]), pack4_i8(cd[12], cd[13], cd[14], cd[15]));
+    hi = make_uint4(pack4_i8(cd[16], cd[17], cd[18], cd[19]), pack4_i8(cd[20], cd[21], cd[22], cd[23]),
+                    pack4_i8(cd[24], cd[25], cd[26], cd[27]), pack4_i8(cd[28], cd[29], cd[30], cd[31]));
+    qscale = bq.qscale;
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 }  // namespace q8kv

@@ -61,6 +61,10 @@ struct Tile {
     uint4 v[4];
     float sk, sv;     // this lane's scale: K (c < 4, sv = 0) or V (c >= 4, sk = 0) of token t0 + 8 (c % 4) + slot
     uint32_t valid;   // bit k: token t0 + 8 k + slot is inside the sequence (and its block id is good)
+    // matrix-core score layout only (load_tile_mf): K scales of tokens
+    // t0 + j and t0 + 16 + j, and their validity in bits 0 and 1
+    float ksm[2];
+    uint32_t svalid;
 };
 
 // Physical block ids of the 4 sub-tiles of tile [t0, t0 + 32), read with
@@ -88,6 +92,8 @@ struct LaneOffsets {
     int scale_v;  // same for V
     int scale_sub;// byte offset of this lane's scale inside an 8-row sub-tile
     int kh;       // the wave's KV head
+    int kmf;      // matrix-core score layout: bytes [32 lg, 32 lg + 32) of token row j (lane = 16 lg + j)
+    int ksmf;     // and that row's scale
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh, int lane)
@@ -101,6 +107,8 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const CacheView &cv, int kh,
     o.scale_v = (c < 4) ? kOutOfRange : in_tile;
     o.scale_sub = slot * 4;
     o.kh = uniform(kh);   // wave-uniform: the scale resources live in SGPRs
+    o.kmf = (lane & 15) * row_bytes + kh * kHeadDim + 32 * (lane >> 4);
+    o.ksmf = (lane & 15) * 4;
     return o;
 }
 
@@ -181,6 +189,47 @@ __device__ __forceinline__ void load_tile(const CacheView &cv, const TileBlocks 
             t.sv = sv;
         }
     }
+}
+
+// load_tile for the matrix-core score path (kv_bs >= 32, so a tile lies in
+// one block): V, the spread scales and `valid` as load_tile, but K in the
+// layout of v_mfma_i32_16x16x64_i8's B operand -- lane (lg, j) holds bytes
+// [32 lg, 32 lg + 32) of token t0 + j in k[0], k[1] and of token t0 + 16 + j
+// in k[2], k[3] -- plus those two tokens' K scales.
+__device__ __forceinline__ void load_tile_mf(const CacheView &cv, const TileBlocks &tb, const LaneOffsets &lo,
+                                             int lane, int t0, int n, int32_t *status, Tile &t)
+{
+    const int slot = lane >> 3, j = lane & 15;
+    const int bs_mask = (1 << cv.kv_bs_log2) - 1;
+    const int row_bytes = cv.nkv * kHeadDim;
+    const bool want = t0 < n;
+    const bool good = (unsigned)tb.id[0] < (unsigned)cv.num_blocks;
+    const bool tok = want && good;
+    if (want && !good && lane == 0 && status) atomicOr(status, kDevBadBlockId);
+    t.valid = 0;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t.valid |= (tok && t0 + kSub * kk + slot < n) ? (1u << kk) : 0u;
+    t.svalid = ((tok && t0 + j < n) ? 1u : 0u) | ((tok && t0 + 16 + j < n) ? 2u : 0u);
+    const size_t row0 = ((size_t)(tok ? tb.id[0] : 0) << cv.kv_bs_log2) + (size_t)(t0 & bs_mask);
+    const int bytes = tok ? kTile * row_bytes : 0;
+    const size_t s0 =
+        ((((size_t)(tok ? tb.id[0] : 0) * cv.nkv + lo.kh) << cv.kv_bs_log2) + (size_t)(t0 & bs_mask));
+    const int sbytes = tok ? kTile * 4 : 0;
+    const auto sk = make_rsrc(cv.k_scale + s0, sbytes);
+    const auto sv = make_rsrc(cv.v_scale + s0, sbytes);
+    t.sk = buf_load4(sk, lo.scale_k, 0);
+    t.sv = buf_load4(sv, lo.scale_v, 0);
+    t.ksm[0] = buf_load4(sk, lo.ksmf, 0);
+    t.ksm[1] = buf_load4(sk, lo.ksmf, 16 * 4);
+    const auto rk = make_rsrc(cv.k_codes + row0 * row_bytes, bytes);
+    const auto rv = make_rsrc(cv.v_codes + row0 * row_bytes, bytes);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        t.k[2 * m] = buf_load16(rk, lo.kmf, 16 * m * row_bytes);
+        t.k[2 * m + 1] = buf_load16(rk, lo.kmf + 16, 16 * m * row_bytes);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t.v[kk] = buf_load16(rv, lo.code, kk * kSub * row_bytes);
 }
 
 // K and V scales of this lane's token in sub-tile kk, from the lanes of the
