@@ -1,8 +1,10 @@
 """Benchmark: q8 decode-attention decode steps on one MI355X.
 
 One step = for every layer of the workload: append one new token per sequence
-through q8_kv_append, then q8_decode_attn over every sequence's whole history
-(partial kernel + merge kernel).  Inputs (cache history, the step's q and new
+and run the decode attention over every sequence's whole history.  By default
+(--append fused) that is q8_decode_step: the append inside the decode's
+partial kernel, then the merge kernel; --append separate runs q8_kv_append,
+then q8_decode_attn (partial + merge).  Inputs (cache history, the step's q and new
 K/V, block tables) are resident in HBM before timing starts.
 
 Prints ONE JSON line (rank 0): achieved algorithmic HBM GB/s of the whole step
@@ -47,6 +49,9 @@ def parse():
                          "32-token blocks per query head by probe); prefill: batched causal prefill of "
                          "the workload's new tokens (a qwen2b_prefill_* workload)")
     ap.add_argument("--topk", type=int, default=32, help="blocks kept per query head (--path sparse)")
+    ap.add_argument("--append", choices=("fused", "separate"), default="fused",
+                    help="--path q8: the new tokens appended inside the decode's partial kernel "
+                         "(q8_decode_step) or by q8_kv_append before it")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -162,7 +167,8 @@ SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n405
          "qwen8b_b32_n32k", "qwen8b_b1_n128k", "qwen8b_b128_stress")
 
 
-def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8", topk=32):
+def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8", topk=32,
+            fused=True):
     """One workload: fill `layers` cache pools, then time whole decode steps
     (graph replay unless eager) and, in an eager pass with HIP events on the
     library's stream, each kernel.  Returns a dict of figures."""
@@ -181,6 +187,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     partial = q8.decode_attn_f32_partial if path == "f32" else q8.decode_attn_partial
     merge = q8.decode_attn_merge
+    fused = fused and path == "q8"
     if path == "sparse":
         # the whole sparse decode (probe + attend kernels) in the partial slot; no merge
         def partial(pool, batch_, nq_, q_, scale_, out_, ws_, nparts=0, dev_status=None):
@@ -224,10 +231,21 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     assert int(status.item()) == 0, "device status set during fill"
     setup_s = time.perf_counter() - t_setup
 
+    def append(li):
+        if not fused:
+            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+
+    def attend(li):
+        if fused:
+            q8.decode_step_partial(pools[li], batch, nq, new_k[li], new_v[li], qs[li], scale, outs[li], ws,
+                                   nparts=nparts, dev_status=status)
+        else:
+            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+
     def step_plain():
         for li in range(layers):
-            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
-            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            append(li)
+            attend(li)
             merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
 
     # ---- timed region 1: whole steps (one HIP graph per step unless eager)
@@ -261,9 +279,9 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         for li in range(layers):
             e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
             if e: e[0].record(stream)
-            q8.kv_append(pools[li], batch, step_seq, step_pos, new_k[li], new_v[li], dev_status=status)
+            append(li)
             if e: e[1].record(stream)
-            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            attend(li)
             if e: e[2].record(stream)
             merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             if e: e[3].record(stream)
@@ -280,7 +298,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         "lens": lens, "table": table, "nblocks": nblocks, "nparts": nparts, "layers": layers,
         "ms_per_step": ms_per_step, "attn_bytes": attn_b, "append_bytes": app_b,
         "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
-        "graph": graph is not None, "setup_s": setup_s,
+        "graph": graph is not None, "setup_s": setup_s, "fused": fused,
     }
 
 
@@ -454,15 +472,16 @@ def sweep_entry(w, m):
     step_bytes = m["layers"] * (m["attn_bytes"] + m["append_bytes"])
     gbs = step_bytes / (m["ms_per_step"] * 1e-3) / 1e9
     part_us = float(m["t_partial"].mean())
+    part_b = m["attn_bytes"] + (m["append_bytes"] if m["fused"] else 0)
     return {
         "workload": w.name, "batch": w.batch, "nq_heads": w.nq, "nkv_heads": w.nkv, "ctx": list(w.lens),
         "layers": m["layers"], "nparts": m["nparts"],
         "us_per_layer_step": round(m["ms_per_step"] * 1e3 / m["layers"], 2),
         "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_decode_partial": round(float(np.median(m["t_partial"])), 2),
-        "partial_GBps": round(m["attn_bytes"] / (part_us * 1e-6) / 1e9, 1),
+        "partial_GBps": round(part_b / (part_us * 1e-6) / 1e9, 1),
         "us_decode_merge": round(float(np.median(m["t_merge"])), 2),
-        "us_append": round(float(np.median(m["t_append"])), 2),
+        "us_append": None if m["fused"] else round(float(np.median(m["t_append"])), 2),
     }
 
 
@@ -494,7 +513,9 @@ def main():
     if w.append_per_step > 1:
         raise SystemExit(f"{w.name} is a prefill workload: use --path prefill")
     layers = args.layers or w.layers
-    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk)
+    fused = args.append == "fused" and args.path == "q8"
+    m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk,
+                fused)
     lens = m["lens"]
     B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
     attn_b, app_b = m["attn_bytes"], m["append_bytes"]
@@ -504,9 +525,11 @@ def main():
     t_partial, t_merge, t_append, t_layer = m["t_partial"], m["t_merge"], m["t_append"], m["t_layer"]
 
     # dominant kernel: the decode partial kernel; its algorithmic bytes are the
-    # attention bytes (the merge traffic is overhead and not counted)
+    # attention bytes, plus the append's when it appends too (the merge traffic
+    # is overhead and not counted)
     part_us = float(t_partial.mean())
-    achieved = attn_b / (part_us * 1e-6) / 1e9
+    part_b = attn_b + (app_b if fused else 0)
+    achieved = part_b / (part_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(args.traffic) and args.path == "q8":
         with open(args.traffic) as f:
@@ -518,7 +541,7 @@ def main():
                 "kernel": {"f32": "q8_attn_f32_partial_kernel", "sparse": "q8_sparse_probe_kernel + q8_sparse_attend_kernel"}.get(
                     args.path, "q8_attn_partial_kernel"),
                 "kernel_us": round(part_us, 2),
-                "algorithmic_bytes_per_launch": int(attn_b)}
+                "algorithmic_bytes_per_launch": int(part_b)}
 
     sweep = None
     if not args.no_sweep and args.path == "q8":
@@ -527,7 +550,8 @@ def main():
             if name == args.workload:
                 continue
             ws_ = workloads.WORKLOADS[name]
-            sweep.append(sweep_entry(ws_, measure(torch, q8, dev, ws_, ws_.layers, 10, 2, 0, args.eager)))
+            sweep.append(sweep_entry(ws_, measure(torch, q8, dev, ws_, ws_.layers, 10, 2, 0, args.eager,
+                                                  fused=fused)))
             torch.cuda.empty_cache()
             print(f"[sweep] {name} done", file=sys.stderr, flush=True)
 
@@ -542,12 +566,13 @@ def main():
         "vs_baseline": None, "dtype": "fp32" if args.path == "f32" else "int8/fp32", "data": "synthetic",
         "config": {
             "workload": w.name, "path": args.path, "topk": args.topk if args.path == "sparse" else None,
+            "append": "fused" if fused else "separate",
             "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "us_per_layer_step": round(ms_per_step * 1e3 / layers, 2),
             "us_per_layer_step_eager_p10_p50_p90": [round(float(np.percentile(t_layer, q)), 2) for q in (10, 50, 90)],
-            "us_append": round(float(np.median(t_append)), 2),
+            "us_append": None if fused else round(float(np.median(t_append)), 2),
             "us_decode_partial": round(float(np.median(t_partial)), 2),
             "us_decode_merge": round(float(np.median(t_merge)), 2),
             "graph": m["graph"],

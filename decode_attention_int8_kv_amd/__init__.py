@@ -75,6 +75,9 @@ def _load():
     lib.q8_decode_attn_sparse_workspace_bytes.restype = SZ
     lib.q8_decode_attn_sparse.argtypes = [LP, BP, I32, P, F, P, I32, P, P, SZ, P, P]
     lib.q8_decode_attn_sparse.restype = I32
+    for fn in (lib.q8_decode_step, lib.q8_decode_step_partial):
+        fn.argtypes = [LP, BP, I32, P, P, P, F, P, I32, P, SZ, P, P]
+        fn.restype = I32
     lib.q8_prefill_attn.argtypes = [LP, BP, I32, P, I32, I32, P, F, P, P, P]
     lib.q8_prefill_attn.restype = I32
     lib.q8_quantize_q.argtypes = [P, I32, I32, P, P, P]
@@ -242,6 +245,30 @@ def decode_attn_sparse(layer, batch, nq_heads, q, scale, out, workspace, topk=32
                                        float(scale), _ptr(out), int(topk), _ptr(selected), _ptr(workspace),
                                        ws_bytes, _ptr(dev_status), _stream(stream))
     _check(st, "q8_decode_attn_sparse")
+
+
+def _step(name, layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts, dev_status, stream):
+    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    st = getattr(_load(), name)(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(k_new),
+                                _ptr(v_new), _ptr(q), float(scale), _ptr(out), int(nparts), _ptr(workspace),
+                                ws_bytes, _ptr(dev_status), _stream(stream))
+    _check(st, name)
+
+
+def decode_step(layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts=0, dev_status=None,
+                stream=None):
+    """q8_decode_step: append the token at position seq_lens[b] - 1 of every
+    sequence (k_new, v_new [batch, nkv, 128] fp32) and decode, in one call."""
+    _step("q8_decode_step", layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts, dev_status,
+          stream)
+
+
+def decode_step_partial(layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts=0,
+                        dev_status=None, stream=None):
+    """q8_decode_step_partial: the step's append + cache walk; decode_attn_merge
+    with the same arguments completes it."""
+    _step("q8_decode_step_partial", layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts,
+          dev_status, stream)
 
 
 def prefill_attn(layer, batch, nq_heads, q_start, max_new, q, scale, out, dev_status=None, stream=None):

@@ -157,6 +157,32 @@ q8_status q8_decode_attn(const q8_kv_layer *layer, const q8_batch *batch, int32_
                                 workspace_bytes, dev_status, stream);
 }
 
+q8_status q8_decode_step_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                 const float *k_new, const float *v_new, const float *q, float scale,
+                                 float *out, int32_t nparts, void *workspace, size_t workspace_bytes,
+                                 int32_t *dev_status, void *stream)
+{
+    q8kv::DecodePlan plan;
+    q8_status s = check_decode(layer, batch, nq_heads, q, out, nparts, workspace, workspace_bytes, &plan);
+    if (s != Q8_OK) return s;
+    if (!k_new || !v_new || !aligned(k_new, 8) || !aligned(v_new, 8)) return Q8_EINVAL;
+    if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
+    hipError_t e = q8kv::launch_decode_partial(*layer, *batch, nq_heads, q, scale, out, plan, workspace, dev_status,
+                                               static_cast<hipStream_t>(stream), k_new, v_new);
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_step_partial");
+}
+
+q8_status q8_decode_step(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, const float *k_new,
+                         const float *v_new, const float *q, float scale, float *out, int32_t nparts,
+                         void *workspace, size_t workspace_bytes, int32_t *dev_status, void *stream)
+{
+    q8_status s = q8_decode_step_partial(layer, batch, nq_heads, k_new, v_new, q, scale, out, nparts, workspace,
+                                         workspace_bytes, dev_status, stream);
+    if (s != Q8_OK) return s;
+    return q8_decode_attn_merge(layer, batch, nq_heads, q, scale, out, nparts, workspace, workspace_bytes,
+                                dev_status, stream);
+}
+
 q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
                                      const float *q, float scale, float *out, int32_t nparts,
                                      void *workspace, size_t workspace_bytes, int32_t *dev_status,

@@ -68,31 +68,9 @@ __global__ __launch_bounds__(64 * kAppendWaves) void q8_append_kernel(AppendPara
         return;
     }
 
-    const size_t src = (size_t)row * kHeadDim + 2 * lane;
-    const float2 k = *reinterpret_cast<const float2 *>(p.k_new + src);
-    const float2 v = *reinterpret_cast<const float2 *>(p.v_new + src);
-    const float ka = wave_max(fmaxf(fabsf(k.x), fabsf(k.y)));
-    const float va = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
-    const RowQuant kq = kv_row_params(ka);
-    const RowQuant vq = kv_row_params(va);
-
-    const int row_in_blk = pos & ((1 << p.kv_bs_log2) - 1);
-    const size_t cache_row = ((size_t)blk << p.kv_bs_log2) + row_in_blk;
-    const size_t dst = (cache_row * p.nkv + kh) * kHeadDim + 2 * lane;
-    // scales: [block][kv head][row], a head's rows of a block side by side
-    const size_t sdst = (((size_t)blk * p.nkv + kh) << p.kv_bs_log2) + row_in_blk;
-    const uint16_t kc = (uint16_t)((kv_code(k.x, kq.recip) & 0xff) | ((kv_code(k.y, kq.recip) & 0xff) << 8));
-    const uint16_t vc = (uint16_t)((kv_code(v.x, vq.recip) & 0xff) | ((kv_code(v.y, vq.recip) & 0xff) << 8));
-    *reinterpret_cast<uint16_t *>(p.k_codes + dst) = kc;
-    *reinterpret_cast<uint16_t *>(p.v_codes + dst) = vc;
-    if (p.k_f32) {   // the fp32 mirror keeps the row unchanged
-        *reinterpret_cast<float2 *>(p.k_f32 + dst) = k;
-        *reinterpret_cast<float2 *>(p.v_f32 + dst) = v;
-    }
-    if (lane == 0) {
-        p.k_scale[sdst] = kq.step;
-        p.v_scale[sdst] = vq.step;
-    }
+    const size_t src = (size_t)row * kHeadDim;
+    append_row(p.k_codes, p.v_codes, p.k_scale, p.v_scale, p.k_f32, p.v_f32, p.nkv, p.kv_bs_log2, blk,
+               pos & ((1 << p.kv_bs_log2) - 1), kh, p.k_new + src, p.v_new + src, lane);
 }
 
 hipError_t launch_append(const q8_kv_layer &layer, const q8_batch &batch, int32_t n_tokens,

@@ -440,8 +440,8 @@ piece_done:
 template <int G, bool Big>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
-    __shared__ int pref[kMaxBatch + 1];
-    walk_ranges(p, pref, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
+    extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
+    walk_ranges(p, lds_batch, lds_batch + p.batch + 1, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
         if constexpr (G == 4 && Big)
             attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
         else
@@ -562,11 +562,14 @@ static const void *partial_kernel(int group, bool big)
     }
 }
 
-int decode_blocks_per_cu(int group, int waves)
+// LDS of one partial workgroup: the batch's tile prefix and lengths.
+static size_t partial_lds_bytes(int batch) { return (size_t)(2 * batch + 1) * sizeof(int); }
+
+int decode_blocks_per_cu(int group, int waves, int batch)
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, true), waves * 64, 0) !=
-            hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, true), waves * 64,
+                                                     partial_lds_bytes(batch)) != hipSuccess || nb < 1)
         nb = 1;
     return nb;
 }
@@ -593,7 +596,8 @@ int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq)
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
             cus = v;
     }
-    const long long slots = (long long)cus * decode_blocks_per_cu(nq / layer.nkv_heads, waves) / head_groups;
+    const long long slots = (long long)cus * decode_blocks_per_cu(nq / layer.nkv_heads, waves, batch.batch) /
+                            head_groups;
     const long long tiles_ub = (long long)batch.batch * ((batch.max_seq_len + kTile - 1) / kTile);
     long long parts = slots < tiles_ub ? slots : tiles_ub;
     if (parts < 1) parts = 1;
@@ -642,6 +646,8 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
     p.ws_ms = reinterpret_cast<float2 *>(ws + plan.off_ms);
     p.ws_acc = reinterpret_cast<float *>(ws + plan.off_acc);
     p.dev_status = dev_status;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
     p.batch = batch.batch;
     p.nq = nq;
     p.max_blocks_per_seq = batch.max_blocks_per_seq;
@@ -654,13 +660,16 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
 
 hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
                                  const float *q, float scale, float *out, const DecodePlan &plan,
-                                 void *workspace, int32_t *dev_status, hipStream_t stream)
+                                 void *workspace, int32_t *dev_status, hipStream_t stream,
+                                 const float *k_new, const float *v_new)
 {
     DecodeParams p = fill_decode_params(layer, batch, nq, q, scale, out, plan, workspace, dev_status);
+    p.k_new = k_new;
+    p.v_new = v_new;
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
     const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile);
     void *args[] = {&p};
-    const hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+    const hipError_t e = hipLaunchKernel(fn, grid, block, args, partial_lds_bytes(batch.batch), stream);
     return e != hipSuccess ? e : hipGetLastError();
 }
 

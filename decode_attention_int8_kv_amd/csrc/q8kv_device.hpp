@@ -243,6 +243,48 @@ __device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, ui
     qscale = bq.qscale;
 }
 
+// One (token, KV head) row of the append, one wave: each lane holds 2 of the
+// 128 K and V values (k, v: dims 2 lane, 2 lane + 1), the wave max gives the
+// exact max-abs, every lane writes its 2 codes (a 128-byte row per wave) and
+// lane 0 the steps.  The codes go to cache row `cache_row` (= block * kv_bs +
+// row in block), head kh; steps are stored [block][kv head][row]; the fp32
+// mirror, if any, gets the row as is.
+__device__ __forceinline__ void append_row_vals(int8_t *k_codes, int8_t *v_codes, float *k_scale, float *v_scale,
+                                                float *k_f32, float *v_f32, int nkv, int kv_bs_log2, int blk,
+                                                int row_in_blk, int kh, float2 k, float2 v, int lane)
+{
+    const float ka = wave_max(fmaxf(fabsf(k.x), fabsf(k.y)));
+    const float va = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+    const RowQuant kq = kv_row_params(ka);
+    const RowQuant vq = kv_row_params(va);
+    const size_t cache_row = ((size_t)blk << kv_bs_log2) + row_in_blk;
+    const size_t dst = (cache_row * nkv + kh) * kHeadDim + 2 * lane;
+    const size_t sdst = (((size_t)blk * nkv + kh) << kv_bs_log2) + row_in_blk;
+    const uint16_t kc = (uint16_t)((kv_code(k.x, kq.recip) & 0xff) | ((kv_code(k.y, kq.recip) & 0xff) << 8));
+    const uint16_t vc = (uint16_t)((kv_code(v.x, vq.recip) & 0xff) | ((kv_code(v.y, vq.recip) & 0xff) << 8));
+    *reinterpret_cast<uint16_t *>(k_codes + dst) = kc;
+    *reinterpret_cast<uint16_t *>(v_codes + dst) = vc;
+    if (k_f32) {   // the fp32 mirror keeps the row unchanged
+        *reinterpret_cast<float2 *>(k_f32 + dst) = k;
+        *reinterpret_cast<float2 *>(v_f32 + dst) = v;
+    }
+    if (lane == 0) {
+        k_scale[sdst] = kq.step;
+        v_scale[sdst] = vq.step;
+    }
+}
+
+// append_row_vals with the row read from k_src / v_src (128 fp32 each).
+__device__ __forceinline__ void append_row(int8_t *k_codes, int8_t *v_codes, float *k_scale, float *v_scale,
+                                           float *k_f32, float *v_f32, int nkv, int kv_bs_log2, int blk,
+                                           int row_in_blk, int kh, const float *k_src, const float *v_src, int lane)
+{
+    const float2 k = *reinterpret_cast<const float2 *>(k_src + 2 * lane);
+    const float2 v = *reinterpret_cast<const float2 *>(v_src + 2 * lane);
+    append_row_vals(k_codes, v_codes, k_scale, v_scale, k_f32, v_f32, nkv, kv_bs_log2, blk, row_in_blk, kh, k, v,
+                    lane);
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 }  // namespace q8kv

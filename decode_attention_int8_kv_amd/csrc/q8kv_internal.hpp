@@ -22,9 +22,12 @@ hipError_t launch_append(const q8_kv_layer &layer, const q8_batch &batch, int32_
                          const int32_t *tok_seq, const int32_t *tok_pos, const float *k_new,
                          const float *v_new, int32_t *dev_status, hipStream_t stream);
 
+// k_new / v_new (or null): the token at position seq_lens[b] - 1 of every
+// sequence, appended by the partial kernel before it reads the cache.
 hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch, int nq,
                                  const float *q, float scale, float *out, const DecodePlan &plan,
-                                 void *workspace, int32_t *dev_status, hipStream_t stream);
+                                 void *workspace, int32_t *dev_status, hipStream_t stream,
+                                 const float *k_new = nullptr, const float *v_new = nullptr);
 
 hipError_t launch_decode_partial_f32(const q8_kv_layer &layer, const q8_batch &batch, int nq,
                                      const float *q, float scale, float *out, const DecodePlan &plan,
@@ -43,7 +46,7 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
                                const DecodePlan &plan, void *workspace, hipStream_t stream);
 
 // Resident workgroups per CU of the decode kernel for this group size.
-int decode_blocks_per_cu(int group, int waves);
+int decode_blocks_per_cu(int group, int waves, int batch);
 
 hipError_t launch_quantize_q(const float *q, int32_t rows, int8_t *codes, float *qscale,
                              hipStream_t stream);

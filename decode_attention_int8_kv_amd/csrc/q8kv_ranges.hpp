@@ -27,6 +27,10 @@ struct DecodeParams {
     float2 *ws_ms;        // [nparts][2][nq] (M, S) of cut pieces
     float *ws_acc;        // [nparts][2][nq][128] accumulators of cut pieces
     int32_t *dev_status;
+    // fused append (or null): the token at position seq_lens[b] - 1 of every
+    // sequence, [batch][nkv][128] fp32, quantized into the cache first
+    const float *k_new;
+    const float *v_new;
     int32_t batch;
     int32_t nq;
     int32_t max_blocks_per_seq;
@@ -48,8 +52,9 @@ __device__ __forceinline__ int part_of(int x, int total, int nparts)
 }
 
 // Tile prefix over the batch into LDS: pref[b] = number of tiles of the
-// sequences before b.  A length outside [0, max_seq_len] counts as empty.
-__device__ inline void build_prefix(const DecodeParams &p, int *pref, bool report)
+// sequences before b; and, if lens is given, the lengths.  A length outside
+// [0, max_seq_len] counts as empty.
+__device__ inline void build_prefix(const DecodeParams &p, int *pref, int *lens, bool report)
 {
     for (int b = threadIdx.x; b < p.batch; b += blockDim.x) {
         int n = p.seq_lens[b];
@@ -58,6 +63,7 @@ __device__ inline void build_prefix(const DecodeParams &p, int *pref, bool repor
             n = 0;
         }
         pref[b + 1] = (n + kTile - 1) / kTile;
+        if (lens) lens[b] = n;
     }
     if (threadIdx.x == 0) pref[0] = 0;
     __syncthreads();
@@ -86,22 +92,86 @@ __device__ inline void build_prefix(const DecodeParams &p, int *pref, bool repor
 // goes to slot `slot` (0: first piece of the range, 1: later) of record
 // `part`.  Afterwards the output rows of empty sequences whose tile position
 // falls in this range are zeroed (the last range also takes those at the
-// very end).
+// very end).  With p.k_new set, `lens` (LDS, batch entries) is required and
+// the range's new tokens are appended first.
 template <class Attend>
-__device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, Attend &&attend)
+__device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
 {
     const int part = blockIdx.x / p.head_groups;
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int kh = hg * (int)(blockDim.x >> 6) + wave;
 
-    build_prefix(p, pref, blockIdx.x == 0);
+    build_prefix(p, pref, lens, blockIdx.x == 0);
     if (blockIdx.x == 0)
         for (int b = threadIdx.x; b <= p.batch; b += blockDim.x) p.ws_prefix[b] = pref[b];
 
     const int total = pref[p.batch];
     const int start = part_start(part, total, p.nparts);
     const int end = part_start(part + 1, total, p.nparts);
+
+    if (p.k_new && lens && kh < p.cache.nkv && start < end) {
+        // Fused append: the new token of every sequence whose last tile lies
+        // in this range (its position n - 1 is in that tile, which no other
+        // range reads), for this wave's KV head, before any tile is loaded.
+        // Lane i looks up sequence lo + i's block while the rows of the first
+        // four such sequences are read; rows are written four at a time.  The
+        // wave reads back only rows it wrote itself, and a wave's vector
+        // memory operations are performed in order, so a wavefront-scope
+        // fence (no wait; it keeps the compiler from moving the tile loads
+        // above the stores) is all the ordering needed.  An agent-scope fence
+        // would write back and invalidate L2 in every workgroup.
+        int lo = 0, hi = p.batch - 1;   // the first sequence whose tiles end after `start`
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pref[mid + 1] <= start) lo = mid + 1; else hi = mid;
+        }
+        bool wrote = false;
+        for (int b0 = uniform(lo); b0 < p.batch && pref[b0 + 1] <= end; b0 += 64) {
+            const int b = b0 + lane;
+            const bool own = b < p.batch && pref[b + 1] <= end && pref[b + 1] > pref[b];
+            const int pos = own ? lens[b] - 1 : 0;
+            int blk = 0;
+            if (own) blk = p.block_table[(size_t)b * p.max_blocks_per_seq + (pos >> p.cache.kv_bs_log2)];
+            uint64_t todo = __builtin_amdgcn_ballot_w64(own);
+            int idx[4];
+            float2 k[4], v[4];
+            auto load_group = [&]() {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    idx[j] = todo ? __builtin_ctzll(todo) : -1;
+                    todo &= todo - 1;
+                    if (idx[j] >= 0) {
+                        const size_t src = ((size_t)(b0 + idx[j]) * p.cache.nkv + kh) * kHeadDim + 2 * lane;
+                        k[j] = *reinterpret_cast<const float2 *>(p.k_new + src);
+                        v[j] = *reinterpret_cast<const float2 *>(p.v_new + src);
+                    }
+                }
+            };
+            if (!todo) continue;
+            load_group();
+            const uint64_t bad = __builtin_amdgcn_ballot_w64(own && (unsigned)blk >= (unsigned)p.cache.num_blocks);
+            if (bad != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
+            for (;;) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (idx[j] < 0) break;
+                    if ((bad >> idx[j]) & 1) continue;
+                    const int ps = __builtin_amdgcn_readlane(pos, idx[j]);
+                    const int bk = __builtin_amdgcn_readlane(blk, idx[j]);
+                    append_row_vals(const_cast<int8_t *>(p.cache.k_codes), const_cast<int8_t *>(p.cache.v_codes),
+                                    const_cast<float *>(p.cache.k_scale), const_cast<float *>(p.cache.v_scale),
+                                    const_cast<float *>(p.k_f32), const_cast<float *>(p.v_f32), p.cache.nkv,
+                                    p.cache.kv_bs_log2, bk, ps & ((1 << p.cache.kv_bs_log2) - 1), kh, k[j], v[j],
+                                    lane);
+                    wrote = true;
+                }
+                if (!todo) break;
+                load_group();
+            }
+        }
+        if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
 
     if (kh < p.cache.nkv && start < end) {
         // the sequence holding tile `start`: the largest b with pref[b] <= start

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 3
+#define Q8KV_ABI_VERSION 4
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -163,6 +163,30 @@ q8_status q8_decode_attn_merge(const q8_kv_layer *layer, const q8_batch *batch, 
                                const float *q, float scale, float *out, int32_t nparts,
                                void *workspace, size_t workspace_bytes,
                                int32_t *dev_status, void *stream);
+
+/* One decode step of a layer in one call: exactly q8_kv_append of the
+ * token at position seq_lens[b] - 1 of every sequence b with seq_lens[b] >= 1
+ * (K/V rows k_new[b], v_new[b]: device fp32 [batch][nkv_heads][head_dim],
+ * 8-byte aligned; the fp32 mirror too, if the layer has one), followed by
+ * q8_decode_attn with the same arguments ("9-3" §2 append, "9-2" §2
+ * attention).  The append is done inside the decode's partial kernel by the
+ * workgroup that reads that token's tile, so the step needs no separate
+ * append launch; the codes and steps written are bit-identical to
+ * q8_kv_append's and the outputs to q8_decode_attn's.  A bad block id for
+ * position seq_lens[b] - 1 sets Q8_DEV_BAD_BLOCK_ID and the row is not
+ * written.  Workspace, nparts and errors as q8_decode_attn. */
+q8_status q8_decode_step(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                         const float *k_new, const float *v_new, const float *q, float scale, float *out,
+                         int32_t nparts, void *workspace, size_t workspace_bytes,
+                         int32_t *dev_status, void *stream);
+
+/* The step's first launch alone (append + cache walk): _step_partial
+ * followed by q8_decode_attn_merge with the same layer, batch, heads, q,
+ * scale, out, nparts and workspace is exactly q8_decode_step. */
+q8_status q8_decode_step_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                 const float *k_new, const float *v_new, const float *q, float scale,
+                                 float *out, int32_t nparts, void *workspace, size_t workspace_bytes,
+                                 int32_t *dev_status, void *stream);
 
 /* Exact decode attention over the layer's fp32 mirror ("9-3" §1: scores of
  * the raw fp32 q and K, max-subtracted softmax, weighted raw V), for every

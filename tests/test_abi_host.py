@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     for want in ("q8_kv_append", "q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge",
                  "q8_decode_attn_workspace_bytes", "q8_decode_attn_auto_parts", "q8_quantize_q",
                  "q8_qk_block_partials", "q8_status_string", "q8_last_error", "q8_abi_version",
-                 "q8_decode_attn_f32", "q8_decode_attn_sparse", "q8_prefill_attn"):
+                 "q8_decode_attn_f32", "q8_decode_attn_sparse", "q8_prefill_attn", "q8_decode_step"):
         assert want in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 3
+    assert q8.abi_version() == 4
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
@@ -208,3 +208,21 @@ def test_prefill_validation(q8):
     assert call_prefill(q8, L, B, total_q=0) == 0        # nothing to do, nothing enqueued
     assert call_prefill(q8, L, B, max_new=0) == 0
     assert call_prefill(q8, layer(q8, kv_bs=24), B) == -2
+
+
+def call_step(q8, L, B, nq=16, k_new=FAKE, v_new=FAKE, q=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, status=None):
+    return q8.lib().q8_decode_step(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, k_new, v_new, q, 0.088, out, 0,
+                                   ws, ws_bytes, status, None)
+
+
+def test_decode_step_validation(q8):
+    L, B = layer(q8), batch(q8)
+    assert call_step(q8, L, B, nq=24) == -2
+    assert call_step(q8, L, B, k_new=0) == -1
+    assert call_step(q8, L, B, v_new=0) == -1
+    assert call_step(q8, L, B, k_new=FAKE + 4) == -1
+    assert call_step(q8, L, B, v_new=FAKE + 2) == -1
+    assert call_step(q8, L, B, q=FAKE + 4) == -1
+    assert call_step(q8, L, B, status=FAKE + 2) == -1
+    assert call_step(q8, L, B, ws=0) == -3
+    assert call_step(q8, L, B, ws_bytes=q8.decode_attn_workspace_bytes(L, B, 16, 0) - 1) == -3
