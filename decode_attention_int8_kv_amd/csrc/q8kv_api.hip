@@ -47,8 +47,8 @@ q8_status check_batch(const q8_batch *b, const q8_kv_layer *l)
     if (b->batch > q8kv::kMaxBatch) return Q8_EUNSUPPORTED;
     if (b->max_blocks_per_seq < 1 || b->max_seq_len < 0) return Q8_EINVAL;
     if ((long long)b->max_seq_len > (long long)b->max_blocks_per_seq * l->kv_bs) return Q8_EINVAL;
-    // the batch's tile count must fit int32
-    if ((long long)b->batch * ((b->max_seq_len + q8kv::kTile - 1) / q8kv::kTile) > 0x7fffffffLL)
+    // the batch's cut-axis units (tiles plus the units charged per sequence) must fit int32
+    if ((long long)b->batch * ((b->max_seq_len + q8kv::kTile - 1) / q8kv::kTile + q8kv::kPieceCost) > 0x7fffffffLL)
         return Q8_EUNSUPPORTED;
     if (!b->block_table || !b->seq_lens) return Q8_EINVAL;
     if (!aligned(b->block_table, 4) || !aligned(b->seq_lens, 4)) return Q8_EINVAL;

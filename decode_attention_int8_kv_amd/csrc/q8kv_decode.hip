@@ -458,6 +458,7 @@ struct MergeParams {
     int32_t batch;
     int32_t nq;
     int32_t nparts;
+    int32_t piece_cost;
 };
 
 constexpr int kMaxMergeWaves = 16;
@@ -475,14 +476,19 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     const int b = blockIdx.x / p.nq, h = blockIdx.x - b * p.nq;
     const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1], total = p.ws_prefix[p.batch];
     if (e0 == a0) return;
-    const int i0 = part_of(a0, total, p.nparts), i1 = part_of(e0 - 1, total, p.nparts);
+    // ranges of the first and the last tile (before the first tile of a
+    // sequence other than 0 lie piece_cost units that hold none)
+    const int first = a0 + (b > 0 ? p.piece_cost : 0);
+    const int i0 = part_of(first, total, p.nparts), i1 = part_of(e0 - 1, total, p.nparts);
     if (i0 == i1) return;
     const int np = i1 - i0 + 1;
     // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
     const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
     // a range can be empty (and write no record) only when there are more
-    // ranges than tiles; otherwise skip the two 64-bit divisions per record
+    // ranges than cut-axis units; otherwise skip the two 64-bit divisions per
+    // record (a range strictly between the first and the last tile's holds
+    // only tiles of this sequence)
     const bool may_be_empty = p.nparts > total;
 
     float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
@@ -608,6 +614,7 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
 {
     DecodePlan pl;
     pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
+    pl.piece_cost = kPieceCost;
     choose_width(layer.nkv_heads, nq / layer.nkv_heads, pl.waves, pl.head_groups);
     // merge waves: enough that a sequence cut into about twice the average
     // number of pieces is read in one round (kMergeBatch pieces per wave);
@@ -654,6 +661,7 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
     p.max_seq_len = batch.max_seq_len;
     p.nparts = plan.nparts;
     p.head_groups = plan.head_groups;
+    p.piece_cost = plan.piece_cost;
     p.sc = (float)((double)scale * 1.4426950408889634);
     return p;
 }
@@ -687,6 +695,7 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
     p.batch = batch.batch;
     p.nq = nq;
     p.nparts = plan.nparts;
+    p.piece_cost = plan.piece_cost;
     hipLaunchKernelGGL(q8_attn_merge_kernel, dim3(batch.batch * nq), dim3(plan.merge_waves * 64), 0,
                        stream, p);
     return hipGetLastError();

@@ -14,8 +14,15 @@ struct DecodePlan {
     int head_groups;     // workgroups per range (8 KV heads each)
     int waves;           // waves per decode workgroup
     int merge_waves;     // waves per merge workgroup
+    int piece_cost;      // cut-axis units charged per non-empty sequence (see q8kv_ranges.hpp)
     size_t off_prefix, off_ms, off_acc, bytes;
 };
+
+// Units charged per non-empty sequence when the batch is cut into ranges: a
+// piece start costs about one tile's time (its query, block-id and first tile
+// loads are dependent round trips), so ranges that start many sequences get
+// fewer tiles.
+constexpr int kPieceCost = 2;
 
 DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq);

@@ -1,13 +1,18 @@
 // q8kv_ranges.hpp -- what the decode partial kernels share: their launch
-// parameters, the cut of the batch's tiles into equal contiguous ranges, and
+// parameters, the cut of the batch's tiles into contiguous ranges, and
 // the walk of one range piece by piece.
 //
-// The batch's 32-token tiles are laid end to end; range i covers tiles
-// [i*T/nparts, (i+1)*T/nparts).  A piece is the part of one sequence inside
-// one range: a sequence inside a single range is finished in place, the
-// pieces of a cut sequence leave (M, S, acc) states for the merge kernel
-// ("9-2 flash_attn_single_q_q8_neon" §2 segment 2, the rescale rule applied
-// to whole partial states).
+// The batch's 32-token tiles are laid end to end on a cut axis; every
+// non-empty sequence but sequence 0 is preceded by piece_cost units that hold
+// no tile.  They stand for the fixed cost of starting a piece inside a range
+// (the query load and the first block-id and tile loads), so a range that
+// starts many sequences gets fewer tiles; sequence 0 starts with range 0
+// anyway.  Range i covers units [i*T/nparts, (i+1)*T/nparts) of the T units,
+// and a tile belongs to the range that holds its unit.  A piece is the part of
+// one sequence inside one range: a sequence inside a single range is finished
+// in place, the pieces of a cut sequence leave (M, S, acc) states for the
+// merge kernel ("9-2 flash_attn_single_q_q8_neon" §2 segment 2, the rescale
+// rule applied to whole partial states).
 #pragma once
 
 #include "q8kv_tile.hpp"
@@ -37,6 +42,7 @@ struct DecodeParams {
     int32_t max_seq_len;
     int32_t nparts;
     int32_t head_groups;
+    int32_t piece_cost;   // cut-axis units in front of every non-empty sequence's tiles
     float sc;             // softmax scale * log2(e)
 };
 
@@ -51,9 +57,10 @@ __device__ __forceinline__ int part_of(int x, int total, int nparts)
     return (int)((((long long)x + 1) * nparts - 1) / total);
 }
 
-// Tile prefix over the batch into LDS: pref[b] = number of tiles of the
-// sequences before b; and, if lens is given, the lengths.  A length outside
-// [0, max_seq_len] counts as empty.
+// Cut-axis prefix over the batch into LDS: pref[b] = units of the sequences
+// before b (tiles, plus piece_cost per non-empty sequence after sequence 0);
+// and, if lens is given, the lengths.  A length outside [0, max_seq_len]
+// counts as empty.
 __device__ inline void build_prefix(const DecodeParams &p, int *pref, int *lens, bool report)
 {
     for (int b = threadIdx.x; b < p.batch; b += blockDim.x) {
@@ -72,7 +79,8 @@ __device__ inline void build_prefix(const DecodeParams &p, int *pref, int *lens,
         int carry = 0;
         for (int base = 1; base <= p.batch; base += 64) {
             const int idx = base + lane;
-            int v = (idx <= p.batch) ? pref[idx] : 0;
+            const int tiles = (idx <= p.batch) ? pref[idx] : 0;
+            int v = tiles + ((idx > 1 && tiles > 0) ? p.piece_cost : 0);
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int u = __shfl_up(v, off, 64);
@@ -186,12 +194,16 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
             while (pref[b + 1] <= x) ++b;
             b = uniform(b);
             const int a0 = uniform(pref[b]), e0 = uniform(pref[b + 1]);
-            const int x1 = min(end, e0);
-            const bool whole = (x == a0) && (x1 == e0);
-            const int slot = (x == start) ? 0 : 1;
-            int n = p.seq_lens[b];
-            n = uniform(n);
-            attend(b, kh, lane, x - a0, x1 - a0, n, whole, part, slot);
+            const int f = a0 + (b > 0 ? p.piece_cost : 0);   // unit of the sequence's first tile
+            const int x0 = max(x, f), x1 = min(end, e0);
+            if (x0 < x1) {   // else the range ends before the sequence's first tile
+                const bool whole = (x0 == f) && (x1 == e0);
+                // slot 0 unless a piece of an earlier sequence lies in this range
+                const int slot = (start >= a0) ? 0 : 1;
+                int n = p.seq_lens[b];
+                n = uniform(n);
+                attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot);
+            }
             x = x1;
         }
     }

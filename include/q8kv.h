@@ -138,8 +138,10 @@ size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *
  * over t < seq_lens[b], where qhat, khat, vhat are the dequantized query
  * (32-blocks, see q8_quantize_q) and cache rows, computed in one pass with an
  * online softmax.  `scale` is the caller's softmax scale (1/sqrt(head_dim) in
- * the pages).  The batch's total tile count is cut into `nparts` equal
- * contiguous ranges (nparts = 0: automatic), one workgroup each; a sequence
+ * the pages).  The batch's 32-token tiles, with two extra units of cost in
+ * front of every non-empty sequence after the first (the cost of starting a
+ * piece), are cut into `nparts` equal contiguous ranges (nparts = 0:
+ * automatic), one workgroup each; a sequence
  * cut across ranges is finished by a merge of the partial (M, S, acc) states
  * with the same rescale rule ("9-2" §2 segment 2 applied to whole partial
  * states).  A sequence of length 0 gives a zero row.  Results are
