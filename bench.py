@@ -600,15 +600,23 @@ def copy_probe(torch, dev, mib, reps):
 KERNEL_SOURCES = ("q8kv_decode.hip", "q8kv_device.hpp", "q8kv_plan.hpp", "q8kv_ranges.hpp", "q8kv_tile.hpp")
 
 
+def _code_only(text: str) -> str:
+    """Source text with comments removed and white space collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
-    """Hash of the q8 decode kernel's sources: counter figures taken on other
-    sources are stale."""
+    """Hash of the code (comments and layout ignored) of the q8 decode
+    kernel's sources: counter figures taken on other code are stale."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_int8_kv_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

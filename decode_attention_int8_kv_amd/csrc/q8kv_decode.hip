@@ -43,12 +43,38 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     const int c = lane & 7, tslot = lane >> 3;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
 
+    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
+    const int log2bs = p.cache.kv_bs_log2;
+    const int ne = min(n, lt1 * kTile);
+    constexpr int D = PipeDepth<G>::value;
+    Tile t[D];
+    TileBlocks bl[D];
+    // The query rows and the first tile's block ids are loaded together, and
+    // the first tile's loads go out before the query is quantized (the
+    // scheduling barrier keeps the compiler from moving them below it): a
+    // piece starts after two memory round trips (block id, tile), not three.
+    float4 qv[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float4 *qp = reinterpret_cast<const float4 *>(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim + 16 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[g][i] = qp[i];
+    }
+    fetch_blocks_ahead<Big>(bt, log2bs, lt0 * kTile, ne, bl[0]);
+    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+        if (d > 0) fetch_blocks_ahead<Big>(bt, log2bs, (lt0 + d) * kTile, ne, bl[d]);
+        load_tile<true, Big>(p.cache, bl[d], lo, lane, (lt0 + d) * kTile, ne, p.dev_status, t[d]);
+    }
+    fetch_blocks_ahead<Big>(bt, log2bs, (lt0 + D - 1) * kTile, ne, bl[D - 1]);
+    __builtin_amdgcn_sched_barrier(0);
+
     // Q quantized once per (sequence, head) ("9-2" §2 segment 1).
     uint4 qc[G];
     float qs[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        quantize_q_quarter(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim, c, qc[g], qs[g]);
+    for (int g = 0; g < G; ++g) quantize_q_quarter_vals(qv[g][0], qv[g][1], qv[g][2], qv[g][3], qc[g], qs[g]);
 
     // PV on the matrix cores for groups of four heads: lane (slot, c) is in
     // the 4-lane block of token slot and bytes [16c, 16c + 16); with the
@@ -77,10 +103,6 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
 #pragma unroll
             for (int j = 0; j < 16; ++j) accm[q][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
-
-    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
-    const int log2bs = p.cache.kv_bs_log2;
-    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
 
     auto process = [&](const Tile &t) {
         float ks[4], vs[4];
@@ -174,20 +196,11 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
         }
     };
 
-    // D register tiles: while tile i is processed, the loads of tiles
-    // i + 1 .. i + D - 1 are in flight and the block ids of tile i + D are
-    // being read.  Tile i lives in t[i % D].  Tokens past the piece count as
-    // past the end, so the tiles loaded beyond the piece cost no HBM traffic.
-    constexpr int D = PipeDepth<G>::value;
-    const int ne = min(n, lt1 * kTile);
-    Tile t[D];
-    TileBlocks bl[D];
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d) {
-        fetch_blocks(bt, log2bs, (lt0 + d) * kTile, ne, bl[d]);
-        load_tile<true, Big>(p.cache, bl[d], lo, lane, (lt0 + d) * kTile, ne, p.dev_status, t[d]);
-    }
-    fetch_blocks(bt, log2bs, (lt0 + D - 1) * kTile, ne, bl[D - 1]);
+    // D register tiles (the first D - 1 loaded above): while tile i is
+    // processed, the loads of tiles i + 1 .. i + D - 1 are in flight and the
+    // block ids of tile i + D are being read.  Tile i lives in t[i % D].
+    // Tokens past the piece count as past the end, so the tiles loaded
+    // beyond the piece cost no HBM traffic.
     int lt = lt0;
     while (true) {
 #pragma unroll
@@ -195,7 +208,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
             // here lt % D == (lt0 + d) % D relative to the prologue's slots
             const int nxt = (d + D - 1) % D;
             load_tile<true, Big>(p.cache, bl[nxt], lo, lane, (lt + D - 1) * kTile, ne, p.dev_status, t[nxt]);
-            fetch_blocks(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
+            fetch_blocks_ahead<Big>(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
             process(t[d]);
             if (++lt >= lt1) goto piece_done;
         }
@@ -285,16 +298,37 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
     // A operands: head g = j / 4's codes of block beta = j % 4 in k-group
     // beta (this lane's group lg), 16 bytes per MFMA; qs[r] = head lg's step
     // of block r
+    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
+    const int log2bs = p.cache.kv_bs_log2;
+    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
+    constexpr int D = 2;
+    const int ne = min(n, lt1 * kTile);
+    Tile t[D];
+    TileBlocks bl[D];
+    // the query block and the first tile's block id together, the first
+    // tile's loads before the quantization (as in attend_piece)
+    float4 qv[8];
+    {
+        const float4 *qp = reinterpret_cast<const float4 *>(p.q + ((size_t)b * p.nq + kh * G + (j >> 2)) * kHeadDim +
+                                                            32 * (j & 3));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = qp[i];
+    }
+    fetch_blocks_ahead<true>(bt, log2bs, lt0 * kTile, ne, bl[0]);
+    load_tile_mf(p.cache, bl[0], lo, lane, lt0 * kTile, ne, p.dev_status, t[0]);
+    fetch_blocks_ahead<true>(bt, log2bs, (lt0 + 1) * kTile, ne, bl[1]);
+    __builtin_amdgcn_sched_barrier(0);
+
     v4i_dec qa[2];
     float qs[4];
     {
-        const int g = j >> 2, beta = j & 3;
-        uint4 lo, hi;
+        const int beta = j & 3;
+        uint4 qlo, qhi;
         float step;
-        quantize_q_block(p.q + ((size_t)b * p.nq + kh * G + g) * kHeadDim + 32 * beta, lo, hi, step);
+        quantize_q_block_vals(qv, qlo, qhi, step);
         const bool mine = lg == beta;
-        qa[0] = __builtin_bit_cast(v4i_dec, mine ? lo : make_uint4(0, 0, 0, 0));
-        qa[1] = __builtin_bit_cast(v4i_dec, mine ? hi : make_uint4(0, 0, 0, 0));
+        qa[0] = __builtin_bit_cast(v4i_dec, mine ? qlo : make_uint4(0, 0, 0, 0));
+        qa[1] = __builtin_bit_cast(v4i_dec, mine ? qhi : make_uint4(0, 0, 0, 0));
 #pragma unroll
         for (int r = 0; r < 4; ++r) qs[r] = __shfl(step, 4 * lg + r, 64);
     }
@@ -306,9 +340,6 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) accm[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
-    const int log2bs = p.cache.kv_bs_log2;
-    const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
     // ds_bpermute byte addresses of the score lanes holding head c % 4's
     // weight of token slot (+ 8)
     const int src_lo = (16 * (c & 3) + tslot) * 4, src_hi = src_lo + 32;
@@ -380,20 +411,13 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         (void)m2;
     };
 
-    constexpr int D = 2;
-    const int ne = min(n, lt1 * kTile);
-    Tile t[D];
-    TileBlocks bl[D];
-    fetch_blocks(bt, log2bs, lt0 * kTile, ne, bl[0]);
-    load_tile_mf(p.cache, bl[0], lo, lane, lt0 * kTile, ne, p.dev_status, t[0]);
-    fetch_blocks(bt, log2bs, (lt0 + 1) * kTile, ne, bl[1]);
     int lt = lt0;
     while (true) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int nxt = (d + D - 1) % D;
             load_tile_mf(p.cache, bl[nxt], lo, lane, (lt + D - 1) * kTile, ne, p.dev_status, t[nxt]);
-            fetch_blocks(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
+            fetch_blocks_ahead<true>(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
             process(t[d]);
             if (++lt >= lt1) goto piece_done;
         }

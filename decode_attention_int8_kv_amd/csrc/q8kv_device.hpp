@@ -192,12 +192,12 @@ __device__ __forceinline__ v4f mfma_outer4(float a, float b, v4f c)
 // ------------------------------------------------------ query quantization
 // Lane (slot, c) of a wave owns elements [16c, 16c+16) of a 128-element query
 // row; the 32-block of those elements is shared with lane c^1.  Quantizes the
-// lane's 16 elements and returns their codes (16 bytes) and the block scale.
-__device__ __forceinline__ void quantize_q_quarter(const float *__restrict__ qrow, int c,
-                                                   uint4 &codes, float &qscale)
+// lane's 16 elements, given in registers (a, b, d, e in element order, so a
+// caller can issue other loads between loading them and this call), and
+// returns their codes (16 bytes) and the block scale.
+__device__ __forceinline__ void quantize_q_quarter_vals(const float4 &a, const float4 &b, const float4 &d,
+                                                        const float4 &e, uint4 &codes, float &qscale)
 {
-    const float4 *p = reinterpret_cast<const float4 *>(qrow + 16 * c);
-    float4 a = p[0], b = p[1], d = p[2], e = p[3];
     float x[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, d.x, d.y, d.z, d.w, e.x, e.y, e.z, e.w};
     float m = 0.0f;
 #pragma unroll
@@ -214,12 +214,19 @@ __device__ __forceinline__ void quantize_q_quarter(const float *__restrict__ qro
     qscale = bq.qscale;
 }
 
+// The same, loading the lane's 16 elements of query row `qrow`.
+__device__ __forceinline__ void quantize_q_quarter(const float *__restrict__ qrow, int c,
+                                                   uint4 &codes, float &qscale)
+{
+    const float4 *p = reinterpret_cast<const float4 *>(qrow + 16 * c);
+    quantize_q_quarter_vals(p[0], p[1], p[2], p[3], codes, qscale);
+}
+
 // Codes and step of one 32-float block of a query row, in one lane: the
 // decode kernel's query quantizer (step = max|x| * fl(1/127), code =
 // clamp(x * 127 / max|x|) truncated toward zero).
-__device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, uint4 &hi, float &qscale)
+__device__ __forceinline__ void quantize_q_block_vals(const float4 (&p)[8], uint4 &lo, uint4 &hi, float &qscale)
 {
-    const float4 *p = reinterpret_cast<const float4 *>(q32);
     float x[32];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -241,6 +248,16 @@ __device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, ui
     hi = make_uint4(pack4_i8(cd[16], cd[17], cd[18], cd[19]), pack4_i8(cd[20], cd[21], cd[22], cd[23]),
                     pack4_i8(cd[24], cd[25], cd[26], cd[27]), pack4_i8(cd[28], cd[29], cd[30], cd[31]));
     qscale = bq.qscale;
+}
+
+// The same, loading the block from q32.
+__device__ __forceinline__ void quantize_q_block(const float *q32, uint4 &lo, uint4 &hi, float &qscale)
+{
+    const float4 *p = reinterpret_cast<const float4 *>(q32);
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[i];
+    quantize_q_block_vals(v, lo, hi, qscale);
 }
 
 // One (token, KV head) row of the append, one wave: each lane holds 2 of the

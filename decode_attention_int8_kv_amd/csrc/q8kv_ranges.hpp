@@ -200,7 +200,7 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
                 const bool whole = (x0 == f) && (x1 == e0);
                 // slot 0 unless a piece of an earlier sequence lies in this range
                 const int slot = (start >= a0) ? 0 : 1;
-                int n = p.seq_lens[b];
+                int n = lens ? lens[b] : p.seq_lens[b];
                 n = uniform(n);
                 attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot);
             }

@@ -85,6 +85,31 @@ __device__ __forceinline__ void fetch_blocks(const int32_t *bt, int log2bs, int 
     }
 }
 
+// The same for the decode walk, branch-free: every scalar load reads an
+// entry of the sequence's own table row (token index clamped to the last
+// token; n >= 1 for a walked piece, and n <= max_seq_len <=
+// max_blocks_per_seq * kv_bs), so a tile's loads issue together and the
+// compiler can hoist them above other work.  BigBlocks (kv_bs >= 32): the
+// four sub-tiles of a tile lie in one block, read once.
+template <bool BigBlocks>
+__device__ __forceinline__ void fetch_blocks_ahead(const int32_t *bt, int log2bs, int t0, int n, TileBlocks &b)
+{
+    const_i32 *sbt = (const_i32 *)bt;
+    const int last = max(n - 1, 0);
+    if (BigBlocks) {
+        const int id = sbt[min(t0, last) >> log2bs];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b.id[kk] = (t0 + kSub * kk < n) ? id : -1;
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int tk = t0 + kSub * kk;
+            const int id = sbt[min(tk, last) >> log2bs];
+            b.id[kk] = (tk < n) ? id : -1;
+        }
+    }
+}
+
 // Per-lane constants of the tile walk (loop invariant).
 struct LaneOffsets {
     int code;     // byte offset of this lane's 16 bytes inside an 8-row sub-tile
