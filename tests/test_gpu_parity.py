@@ -46,6 +46,26 @@ def test_append_codes_and_scales_bit_exact(kv_bs, dist):
     np.testing.assert_array_equal(host.v_step.reshape(-1, 8)[slots].view(np.uint32), dv.view(np.uint32))
 
 
+# rows = tokens x KV heads picks the heads per append wave: < 16384 rows one,
+# then two, four, and eight from 65536 rows; 12 and 3 KV heads leave part of
+# the last group of eight empty
+@pytest.mark.parametrize("nkv,lens", [(8, [1000, 1048]), (8, [4096]), (12, [3000, 2999, 1]), (3, [24000])],
+                         ids=["h2", "h4", "h8-nkv12", "h8-nkv3"])
+def test_append_heads_per_wave_bit_exact(nkv, lens):
+    say(f"[append] nkv={nkv} tokens={sum(lens)}")
+    lens = np.array(lens, np.int32)
+    k, v = dense_kv(lens, nkv, seed=int(lens.sum()) + nkv, dist="student3x3")
+    dc = DeviceCache(lens, nkv, 32, seed=5)
+    dc.append_dense(k, v)
+    assert dc.status_word() == 0
+    host = dc.host()
+    slots, ck, cv, dk, dv = expected_codes(dc, k, v)
+    np.testing.assert_array_equal(host.k_codes.reshape(-1, nkv, 128)[slots], ck)
+    np.testing.assert_array_equal(host.v_codes.reshape(-1, nkv, 128)[slots], cv)
+    np.testing.assert_array_equal(host.k_step.reshape(-1, nkv)[slots].view(np.uint32), dk.view(np.uint32))
+    np.testing.assert_array_equal(host.v_step.reshape(-1, nkv)[slots].view(np.uint32), dv.view(np.uint32))
+
+
 def test_append_one_token_per_step_matches_bulk():
     # decode-style appends (one token per sequence per call at seq_lens - 1)
     # leave exactly the bytes a bulk append leaves.
@@ -144,7 +164,7 @@ def test_qwen2b_batch1(n):
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("kv_bs", [8, 32, 64])
+@pytest.mark.parametrize("kv_bs", [8, 16, 32, 64, 256])
 def test_ragged_edges(group, kv_bs):
     say(f"[decode] ragged edges group={group} kv_bs={kv_bs}")
     nkv = 2
