@@ -65,6 +65,54 @@ def test_decode_full_size_sampled(name, nseq):
     say(f"  {rows.size} rows of sequences {seqs} (lengths {lens[seqs].tolist()}), worst err/tol {worst:.3f}")
 
 
+@pytest.mark.parametrize("name,nseq", [("qwen2b_b64_ragged", 6), ("qwen8b_b128_stress", 10)])
+def test_decode_step_full_size_sampled(name, nseq):
+    # the call bench.py times: q8_decode_step (the newest token of every
+    # sequence appended inside the decode kernel), automatic partitions
+    w = workloads.WORKLOADS[name]
+    say(f"[full size] decode step {name}: batch {w.batch}, {w.nq}/{w.nkv} heads, {w.lens}")
+    t, m = torch(), q8()
+    lens = workloads.seq_lens(w)
+    dc = DeviceCache(lens, w.nkv, w.kv_bs, seed=930, garbage=False)
+    hist = np.maximum(lens - 1, 0)
+    seqs = np.concatenate([np.full(n, b, np.int32) for b, n in enumerate(hist)])
+    poss = np.concatenate([np.arange(n, dtype=np.int32) for n in hist])
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(931)
+    for c0 in range(0, seqs.size, CHUNK):
+        c1 = min(seqs.size, c0 + CHUNK)
+        k = workloads.kv_pool_torch(w, c1 - c0, gen, "cuda")
+        v = workloads.kv_pool_torch(w, c1 - c0, gen, "cuda")
+        m.kv_append(dc.layer, dc.batch, t.from_numpy(seqs[c0:c1]).cuda(), t.from_numpy(poss[c0:c1]).cuda(), k, v,
+                    dev_status=dc.status)
+    k_new = workloads.kv_pool_torch(w, w.batch, gen, "cuda").reshape(w.batch, w.nkv, 128).contiguous()
+    v_new = workloads.kv_pool_torch(w, w.batch, gen, "cuda").reshape(w.batch, w.nkv, 128).contiguous()
+    q = t.randn((w.batch, w.nq, 128), generator=gen, device="cuda")
+    out = t.full((w.batch, w.nq, 128), float("nan"), dtype=t.float32, device="cuda")
+    ws = t.empty(m.decode_attn_workspace_bytes(dc.layer, dc.batch, w.nq, 0), dtype=t.uint8, device="cuda")
+    m.decode_step(dc.layer, dc.batch, w.nq, k_new, v_new, q, SCALE, out, ws, nparts=0, dev_status=dc.status)
+    assert dc.status_word() == 0
+    host = dc.host()
+    # every appended row: codes and steps bit-exact
+    live = np.nonzero(lens > 0)[0]
+    pos = lens[live] - 1
+    slots = dc.table[live, pos // w.kv_bs] * w.kv_bs + pos % w.kv_bs
+    ck, dk = oracle.quantize_kv(k_new.cpu().numpy()[live])
+    cv, dv = oracle.quantize_kv(v_new.cpu().numpy()[live])
+    np.testing.assert_array_equal(host.k_codes.reshape(-1, w.nkv, 128)[slots], ck)
+    np.testing.assert_array_equal(host.v_codes.reshape(-1, w.nkv, 128)[slots], cv)
+    np.testing.assert_array_equal(host.k_step.reshape(-1, w.nkv)[slots].view(np.uint32), dk.view(np.uint32))
+    np.testing.assert_array_equal(host.v_step.reshape(-1, w.nkv)[slots].view(np.uint32), dv.view(np.uint32))
+    # sampled output rows within tolerance of the oracle over the whole cache
+    seqs_s = _sample_seqs(lens, nseq, 932)
+    if name == "qwen8b_b128_stress":
+        seqs_s = sorted(set(seqs_s) | {int(b) for b in np.nonzero(lens <= 65)[0][:8]})
+    rows = np.array([b * w.nq + h for b in seqs_s for h in range(w.nq)], np.int64)
+    want = oracle.decode_attn_rows(host, q.cpu().numpy(), w.nq, SCALE, rows)
+    worst = assert_rows_close(out.cpu().numpy().reshape(-1, 128)[rows], want, name)
+    say(f"  {live.size} appended rows exact; {rows.size} rows of sequences {seqs_s}, worst err/tol {worst:.3f}")
+
+
 def test_sparse_full_size_ragged():
     # every (sequence, query head) of the ragged 2B batch: kept blocks exact,
     # outputs within tolerance
