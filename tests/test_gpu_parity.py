@@ -223,6 +223,28 @@ def test_placement_invariance_and_reproducibility():
     assert_rows_close(other, outs[0], "nparts 1 vs 6")
 
 
+def test_batch_composition_changes_bits_only_within_tolerance():
+    # The cut runs over the whole batch, so other sequences move the places
+    # where a long sequence is cut: its output may change in the last bits,
+    # never beyond the tolerance.  Sub-batch and super-batch against the batch.
+    say("[decode] batch composition")
+    lens = np.array([3000, 40, 1700, 1, 640, 2100], np.int32)
+    k, v = dense_kv(lens, 8, seed=43)
+    q = np.random.default_rng(43).standard_normal((lens.size, 16, 128)).astype(np.float32)
+
+    def run(idx):
+        dc = DeviceCache(lens[idx], 8, 32, seed=7)
+        dc.append_dense(k[idx], v[idx])
+        out = dc.decode(q[idx], 16, SCALE, nparts=12).cpu().numpy()
+        assert dc.status_word() == 0
+        return out
+
+    full = run(np.arange(lens.size))
+    for idx in (np.array([0, 2, 5]), np.array([2]), np.array([5, 4, 3, 2, 1, 0])):
+        part = run(idx)
+        assert_rows_close(part, full[idx], f"sequences {idx.tolist()}")
+
+
 def test_zero_query_gives_mean_of_values():
     say("[decode] q = 0")
     lens = np.array([77, 300], np.int32)
