@@ -491,7 +491,7 @@ def main():
         traffic_from(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(each GPU would run the same kernels on its own share of sequences or KV heads). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
