@@ -23,13 +23,19 @@
 //   softmax online per query (log2 domain): the tile max across the 4 lane
 //           groups with v_permlane16/32_swap, one rescale of S and the
 //           accumulators per tile;
-//   values  O^T += V^T P^T with v_mfma_f32_16x16x16_bf16.  P^T arrives in
+//   values  O^T += V^T P^T on the bf16 matrix cores.  P^T arrives in
 //           exactly the B layout (query j, tokens 4 lg + e); each weight
 //           w = p * vs is split exactly into three bf16 terms
 //           (w = hi + mid + lo by truncation; the "bf16x3" form of an fp32
 //           product), and V codes (|code| <= 127) are exact in bf16, so the
 //           products are exact and only the fp32 accumulation order differs
-//           from a scalar loop.  V^T is staged per tile through LDS: each
+//           from a scalar loop.  The hi and mid terms go through one
+//           v_mfma_f32_16x16x32_bf16 (same cost as a K = 16 product, twice
+//           the work): its A operand holds the lane's 4 V values twice and its
+//           B operand the 4 hi then the 4 mid weights, so each k slot pairs a
+//           token's V code with one of its terms (A and B hold the same k
+//           slots in a lane, whatever their order); lo uses
+//           v_mfma_f32_16x16x16_bf16.  V^T is staged per tile through LDS: each
 //           lane loads 4 bytes of 8 token rows, transposes them with v_perm
 //           and writes one dword (4 tokens of one dim) per dim.
 #include "q8kv_tile.hpp"
@@ -40,6 +46,14 @@ namespace q8kv {
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+
+// Eight bf16 from two groups of four (the operand of a K = 32 product).
+__device__ __forceinline__ v8bf_t cat_bf16(v4s_t a, v4s_t b)
+{
+    const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+    return __builtin_bit_cast(v8bf_t, make_uint4(x.x, x.y, y.x, y.y));
+}
 
 constexpr int kPrefillWaves = 4;   // query tiles per workgroup
 constexpr int kSets = 2;           // 16-row query sets per wave (share each key tile's loads and V operands)
@@ -299,8 +313,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         }
         asm volatile("" ::: "memory");
         v4s_t va[8];
+        v8bf_t va2[8];   // the same 4 values twice: the A operand of the paired hi + mid product
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) va[dt] = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
+        for (int dt = 0; dt < 8; ++dt) {
+            va[dt] = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
+            va2[dt] = cat_bf16(va[dt], va[dt]);
+        }
 
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
@@ -360,10 +378,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
             S[st] += psum;
             v4s_t whi, wmid, wlo;
             split_bf16x3(w, whi, wmid, wlo);
+            const v8bf_t whm = cat_bf16(whi, wmid);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], whi, acc[st][dt], 0, 0, 0);
-                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], wmid, acc[st][dt], 0, 0, 0);
+                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2[dt], whm, acc[st][dt], 0, 0, 0);
                 acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], wlo, acc[st][dt], 0, 0, 0);
             }
         }
