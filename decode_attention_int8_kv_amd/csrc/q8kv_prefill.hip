@@ -13,8 +13,9 @@
 //
 // A wave owns 32 query rows of one KV head (two sets of 16): row rho =
 // position * G + head of the flattened (position, query head) list.  It
-// walks the keys 0..p_max of its rows in tiles of 16 tokens; each tile's
-// loads, V transpose and V operands serve both sets:
+// walks the keys 0..p_max of its rows in tiles of 16 tokens (for a fresh
+// prompt, a quarter of them: see prefill_segments); each tile's loads, V
+// transpose and V operands serve both sets:
 //   scores  S^T = K Q^T with v_mfma_i32_16x16x32_i8, one instruction per
 //           32-block beta (A: token j's bytes 32 beta + [8 lg, 8 lg + 8) in
 //           lane (lg, j); B: the query codes in the same places), so lane
@@ -70,8 +71,17 @@ struct PrefillParams {
     float *out;
     int32_t *dev_status;
     int32_t nq, max_blocks_per_seq, max_seq_len, max_new, total_q, log2g;
-    float sc;   // softmax scale * log2(e)
+    int32_t ks;   // key segments per query tile (1, 2 or 4 waves of a workgroup)
+    float sc;     // softmax scale * log2(e)
 };
+
+// Partial states of the key segments other than the first, per lane:
+// [slot][set][32 accumulators, M, S][lane].
+constexpr int kCombVals = 8 * 4 + 2;
+#ifndef Q8KV_PREFILL_SPLIT
+#define Q8KV_PREFILL_SPLIT 4
+#endif
+constexpr int kPrefillSplit = Q8KV_PREFILL_SPLIT;   // 1, 2 or 4
 
 // 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
 __device__ __forceinline__ v4s_t codes_to_bf16(uint32_t w)
@@ -179,15 +189,22 @@ template <bool Big>
 __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillParams p)
 {
     __shared__ uint32_t vt_all[kPrefillWaves][kHeadDim * kVtStride];
+    __shared__ float comb[kPrefillWaves - 1][kSets][kCombVals][64];
     const int nkv = p.cache.nkv;
     const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     uint32_t *vt = vt_all[wave];
-    // the last query tiles (the longest key ranges under the causal mask) are
-    // dispatched first, so the short ones fill in behind them
-    const int tile = (gridDim.y - 1 - blockIdx.y) * kPrefillWaves + wave;
+    // With ks > 1 the ks waves of a group share one query tile, each taking a
+    // contiguous segment of its key tiles; their states are combined at the
+    // end.  The last query tiles (the longest key ranges under the causal
+    // mask) are dispatched first, so the short ones fill in behind them.
+    const int ks = p.ks, seg = wave % ks;
+    const int tile = (gridDim.y - 1 - blockIdx.y) * (kPrefillWaves / ks) + wave / ks;
     const int G = 1 << p.log2g;
     const int j = lane & 15, lg = lane >> 4;
+    // every wave meets the combine barrier (ks > 1), so nothing returns
+    // early: waves without work skip to it
+    bool active = true;
 
     const int r0 = uniform(p.q_start[b]), r1 = uniform(p.q_start[b + 1]);
     const int n = uniform(p.seq_lens[b]);
@@ -195,8 +212,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     const int nn = r1 - r0;
     if (!range_ok || n < nn || n > p.max_seq_len || nn > p.max_new) {
         // a bad sequence: reported; its rows that this wave covers are zeros
+        active = false;
         if (kh == 0 && tile == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
-        if (range_ok) {
+        if (range_ok && seg == 0) {
 #pragma unroll
             for (int st = 0; st < kSets; ++st) {
                 const int rho = tile * kPrefillRows + 16 * st + j;
@@ -209,15 +227,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
                 }
             }
         }
-        return;
     }
     const int rows = nn << p.log2g;
-    if (tile * kPrefillRows >= rows) return;
+    if (tile * kPrefillRows >= rows) active = false;
 
+    // state of this wave (declared for the combine; set by active waves)
+    bool live[kSets] = {};
+    int qi[kSets] = {}, qg[kSets] = {}, pos[kSets] = {};
+    // M is a reference max per query: the weights exp2(s - M) may exceed 1 by
+    // up to 2^kLazyRescale, and S and the accumulators are rescaled only when
+    // some query's tile max rises above its M by more than that (the result
+    // is the same quantity; only rounding differs)
+    constexpr float kLazyRescale = 8.0f;
+    float M[kSets], S[kSets];
+    v4f_t acc[kSets][8];
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        M[st] = -INFINITY;
+        S[st] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[st][dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (active) {
     // this lane's query row in each set (clamped to a real row; lanes past the
     // end are computed and discarded) and its position
-    bool live[kSets];
-    int qi[kSets], qg[kSets], pos[kSets];
 #pragma unroll
     for (int st = 0; st < kSets; ++st) {
         const int rho = tile * kPrefillRows + 16 * st + j;
@@ -259,32 +293,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     const const_i32 *sbt = (const const_i32 *)(p.block_table + (size_t)b * p.max_blocks_per_seq);
     const int vh = lane >> 5, vd = lane & 31;   // V staging: tokens 8 vh + u, dims 4 vd .. 4 vd + 3
 
-    // M is a reference max per query: the weights exp2(s - M) may exceed 1 by
-    // up to 2^kLazyRescale, and S and the accumulators are rescaled only when
-    // some query's tile max rises above its M by more than that (the result
-    // is the same quantity; only rounding differs)
-    constexpr float kLazyRescale = 8.0f;
-    float M[kSets], S[kSets];
-    v4f_t acc[kSets][8];
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        M[st] = -INFINITY;
-        S[st] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[st][dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
-    }
     bool bad = false;
-
     // tile kt + 1 (block id, K, steps, V rows) is in flight while tile kt is
     // computed; past the end the last tile is reloaded, unused.  (Loading the
     // V rows at the start of their own tile, or two tiles used in turn
     // without the copy, both measured slower.)
+    // this wave's key segment: tiles [kt_lo, kt_hi) of the nkt, split evenly
+    // over the ks waves of the query tile (possibly empty: then nothing is
+    // loaded, since tile positions past the sequence have no table entry)
+    const int kt_lo = (seg * nkt) / ks, kt_hi = ((seg + 1) * nkt) / ks;
     KeyTile nxt;
-    load_key_tile<Big>(p, sbt, kh, 0, n, j, lg, vh, vd, nxt);
-    for (int kt = 0; kt < nkt; ++kt) {
+    if (kt_lo < kt_hi) load_key_tile<Big>(p, sbt, kh, kt_lo * kKeyTile, n, j, lg, vh, vd, nxt);
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int t0 = kt * kKeyTile;
         const KeyTile tl = nxt;
-        load_key_tile<Big>(p, sbt, kh, min(kt + 1, nkt - 1) * kKeyTile, n, j, lg, vh, vd, nxt);
+        load_key_tile<Big>(p, sbt, kh, min(kt + 1, kt_hi - 1) * kKeyTile, n, j, lg, vh, vd, nxt);
         bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
         // every row of the wave sees all 16 tokens of the tile: no masks
         const bool full = t0 + kKeyTile - 1 <= pos_lo && tl.good_lo && tl.good_hi;
@@ -388,6 +411,50 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
 
+    }
+
+    // the other segments' states into the first's: M the largest, S and the
+    // accumulators rescaled to it and summed in segment order ("9-2" §2
+    // segment 2 rule applied to partial states); deterministic
+    if (ks > 1) {
+        const int slot = (wave / ks) * (ks - 1) + seg - 1;
+        if (active && seg > 0) {
+#pragma unroll
+            for (int st = 0; st < kSets; ++st) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) comb[slot][st][4 * dt + e][lane] = acc[st][dt][e];
+                comb[slot][st][32][lane] = M[st];
+                comb[slot][st][33][lane] = S[st];
+            }
+        }
+        __syncthreads();
+        if (active && seg == 0) {
+#pragma unroll
+            for (int st = 0; st < kSets; ++st) {
+                float Mn = M[st];
+                for (int w = 1; w < ks; ++w) Mn = fmaxf(Mn, comb[slot + w][st][32][lane]);
+                const float a0 = M[st] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
+                S[st] *= a0;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= a0;
+                for (int w = 1; w < ks; ++w) {
+                    const float Mw = comb[slot + w][st][32][lane];
+                    const float aw = Mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mw - Mn);
+                    S[st] = fmaf(comb[slot + w][st][33][lane], aw, S[st]);
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[st][dt][e] = fmaf(comb[slot + w][st][4 * dt + e][lane], aw, acc[st][dt][e]);
+                }
+                M[st] = Mn;
+            }
+        }
+    }
+    if (!active || seg != 0) return;
+
     float Ssum[kSets];
 #pragma unroll
     for (int st = 0; st < kSets; ++st) Ssum[st] = sum_rows32(sum_rows16(S[st]));   // lane groups hold different tokens
@@ -405,6 +472,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
+}
+
+// Key segments per query tile.  When at least half of the keys are new (a
+// fresh prompt, or a chunk as long as its history), the causal triangle makes
+// the last query tiles' key ranges about twice the average, and the waves
+// that walk them alone set the launch time: their keys are split over four
+// waves.  Chunks after a long history have query tiles of nearly equal
+// length and keep one wave per tile.  The grid stays within 65535 rows of
+// workgroups.
+static int prefill_segments(int max_new, int max_seq_len, long long rows)
+{
+    int ks = (2LL * max_new >= max_seq_len) ? kPrefillSplit : 1;
+    while (ks > 1 && (rows + (long long)kPrefillRows * (kPrefillWaves / ks) - 1) /
+                             ((long long)kPrefillRows * (kPrefillWaves / ks)) > 65535)
+        ks >>= 1;
+    return ks;
 }
 
 hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int nq, const int32_t *q_start,
@@ -433,8 +516,9 @@ hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int n
     p.log2g = ilog2(nq / layer.nkv_heads);
     p.sc = (float)((double)scale * 1.4426950408889634);
     const long long rows = (long long)max_new * (nq / layer.nkv_heads);
-    const dim3 grid(batch.batch * layer.nkv_heads,
-                    (unsigned)((rows + kPrefillRows * kPrefillWaves - 1) / (kPrefillRows * kPrefillWaves)));
+    p.ks = prefill_segments(max_new, batch.max_seq_len, rows);
+    const long long rows_per_wg = (long long)kPrefillRows * (kPrefillWaves / p.ks);
+    const dim3 grid(batch.batch * layer.nkv_heads, (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
     void *args[] = {&p};
     const void *fn = layer.kv_bs >= kKeyTile ? reinterpret_cast<const void *>(&q8_prefill_kernel<true>)
                                              : reinterpret_cast<const void *>(&q8_prefill_kernel<false>);
