@@ -58,7 +58,7 @@ def parse():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "q8_attn_partial_kernel_hbm_traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="no GPU work: read rocprofv3 counter CSVs under DIR/{copyf,copyw,fetch,write} "
