@@ -44,14 +44,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kRsrcWord3);
 }
 
+// Cache policy of the K/V code and scale loads: the SLC bit, which gfx950
+// encodes as `nt` (non-temporal).  Every cache byte is read once per call,
+// and streaming loads keep it from displacing lines in L2 and the Infinity
+// Cache; on an MI355X a plain read of 0.5-2 GiB runs 15-20% faster with the
+// hint (5.8 -> 6.7-7.0 TB/s), and the decode kernel 12% faster.
+constexpr int kStreamPolicy = 2;
+
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamPolicy));
 }
 
 __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy));
 }
 
 constexpr int kOutOfRange = 0x7ffffff0;   // a lane offset past any resource
