@@ -510,7 +510,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
     // a range can be empty (and write no record) only when there are more
-    // ranges than cut-axis units; otherwise skip the two 64-bit divisions per
+    // ranges than cut-axis units; otherwise skip the two divisions per
     // record (a range strictly between the first and the last tile's holds
     // only tiles of this sequence)
     const bool may_be_empty = p.nparts > total;

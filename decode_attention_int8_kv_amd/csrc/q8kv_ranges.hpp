@@ -46,15 +46,41 @@ struct DecodeParams {
     float sc;             // softmax scale * log2(e)
 };
 
+// Range bounds take one integer division; it is a 32-bit one whenever
+// nparts * total < 2^31 (every product below is at most that), which is far
+// cheaper than the 64-bit form and runs at the start of every workgroup.
+__device__ __forceinline__ bool narrow_cut(int total, int nparts)
+{
+    return (long long)total * nparts < (1LL << 31);
+}
+
 __device__ __forceinline__ int part_start(int i, int total, int nparts)
 {
+    if (narrow_cut(total, nparts)) return (int)((unsigned)(i * total) / (unsigned)nparts);
     return (int)(((long long)i * total) / nparts);
 }
 
 // The range that holds tile x (0 <= x < total).
 __device__ __forceinline__ int part_of(int x, int total, int nparts)
 {
+    if (narrow_cut(total, nparts)) return (int)((unsigned)((x + 1) * nparts - 1) / (unsigned)total);
     return (int)((((long long)x + 1) * nparts - 1) / total);
+}
+
+// Number of entries i in [0, count) with v[i] <= u, for v non-decreasing
+// (LDS); 64 entries per step, so a batch of up to 64 sequences takes one
+// LDS read and a ballot instead of a binary search's dependent reads.  The
+// whole wave calls it with the same arguments.
+__device__ __forceinline__ int count_le(const int *v, int count, int u, int lane)
+{
+    int n = 0;
+    for (int base = 0; base < count; base += 64) {
+        const int i = base + lane;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(i < count && v[i] <= u);
+        n += __builtin_popcountll(m);
+        if (m != ~0ull) break;   // no later entry is <= u
+    }
+    return uniform(n);
 }
 
 // Cut-axis prefix over the batch into LDS: pref[b] = units of the sequences
@@ -129,13 +155,10 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
         // fence (no wait; it keeps the compiler from moving the tile loads
         // above the stores) is all the ordering needed.  An agent-scope fence
         // would write back and invalidate L2 in every workgroup.
-        int lo = 0, hi = p.batch - 1;   // the first sequence whose tiles end after `start`
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (pref[mid + 1] <= start) lo = mid + 1; else hi = mid;
-        }
+        // the first sequence whose tiles end after `start` (one exists: start < total)
+        const int lo = p.batch == 1 ? 0 : count_le(pref + 1, p.batch, start, lane);
         bool wrote = false;
-        for (int b0 = uniform(lo); b0 < p.batch && pref[b0 + 1] <= end; b0 += 64) {
+        for (int b0 = lo; b0 < p.batch && pref[b0 + 1] <= end; b0 += 64) {
             const int b = b0 + lane;
             const bool own = b < p.batch && pref[b + 1] <= end && pref[b + 1] > pref[b];
             const int pos = own ? lens[b] - 1 : 0;
@@ -183,12 +206,8 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
 
     if (kh < p.cache.nkv && start < end) {
         // the sequence holding tile `start`: the largest b with pref[b] <= start
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pref[mid] <= start) lo = mid; else hi = mid - 1;
-        }
-        int b = uniform(lo);
+        // (pref[0] = 0, so there is one)
+        int b = p.batch == 1 ? 0 : count_le(pref, p.batch, start, lane) - 1;
         int x = start;
         while (x < end) {
             while (pref[b + 1] <= x) ++b;
@@ -209,11 +228,8 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
     }
 
     if (hg == 0) {
-        int lo = 0, hi = p.batch;   // first b with pref[b] >= start
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (pref[mid] < start) lo = mid + 1; else hi = mid;
-        }
+        // first b with pref[b] >= start (start <= total = pref[batch])
+        const int lo = p.batch == 1 ? (start > 0 ? 1 : 0) : count_le(pref, p.batch + 1, start - 1, lane);
         const bool last = (part == p.nparts - 1);
         for (int b = lo; b < p.batch && (pref[b] < end || (last && pref[b] <= total)); ++b) {
             if (pref[b + 1] != pref[b]) continue;
