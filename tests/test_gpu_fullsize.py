@@ -142,3 +142,31 @@ def test_f32_mirror_full_size_ragged():
     want = oracle.decode_attn_f32(dc.host_mirror(), q.cpu().numpy(), w.nq, SCALE, rows_bh=rows)
     worst = assert_rows_close(out.reshape(-1, 128)[rows], want, "f32 full size")
     say(f"  {rows.size} rows, worst err/tol {worst:.3f}")
+
+
+def test_decode_wide_cut_long_sequence():
+    """One 1M-token sequence (32768 tiles, one KV head) cut into 65536
+    ranges: nparts * tiles = 2^31, so the range bounds take the 64-bit
+    division in the partial and the merge kernels, and half of the ranges are
+    empty.  The automatic cut (32-bit division) is checked beside it."""
+    t, m = torch(), q8()
+    n = 1 << 20
+    lens = np.array([n], np.int32)
+    say(f"[wide cut] one sequence of {n} tokens, 1/1 heads, kv_bs 32")
+    dc = DeviceCache(lens, 1, 32, seed=951, garbage=False)
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(951)
+    seqs = t.zeros(CHUNK, dtype=t.int32, device="cuda")
+    for c0 in range(0, n, CHUNK):
+        pos = t.arange(c0, c0 + CHUNK, dtype=t.int32, device="cuda")
+        k = t.randn((CHUNK, 1, 128), generator=gen, device="cuda")
+        v = t.randn((CHUNK, 1, 128), generator=gen, device="cuda")
+        m.kv_append(dc.layer, dc.batch, seqs, pos, k, v, dev_status=dc.status)
+    q = t.randn((1, 1, 128), generator=gen, device="cuda")
+    assert dc.status_word() == 0
+    want = oracle.decode_attn_rows(dc.host(), q.cpu().numpy(), 1, SCALE, np.array([0], np.int64))
+    for nparts in (65536, 0):
+        out = dc.decode(q, 1, SCALE, nparts=nparts).cpu().numpy()
+        assert dc.status_word() == 0
+        worst = assert_rows_close(out.reshape(-1, 128), want, f"1M tokens, nparts {nparts}")
+        say(f"  nparts {nparts}: worst err/tol {worst:.3f}")
