@@ -173,6 +173,19 @@ def test_ragged_edges(group, kv_bs):
     say(f"  worst err/tol {w:.3f}")
 
 
+# more than 64 sequences, with empty ones at the edges of the 64-entry steps
+# of the range lookups (and at both ends of the batch)
+WIDE_LENS = [0 if b in (0, 62, 63, 64, 65, 127, 128, 130) else int(x)
+             for b, x in enumerate(np.random.default_rng(77).integers(1, 300, 131))]
+
+
+@pytest.mark.parametrize("kv_bs", [8, 32])
+def test_wide_batch_with_empty_sequences(kv_bs):
+    say(f"[decode] 131 sequences, 8 empty, kv_bs={kv_bs}")
+    w = _decode_case(WIDE_LENS, 4, 2, kv_bs, seed=77 + kv_bs, nparts_list=[0, 1, 3, 64, 65, 300, 5000])
+    say(f"  worst err/tol {w:.3f}")
+
+
 def test_heavy_tails_and_guard_rows():
     say("[decode] student-t x3 with near-zero rows")
     lens = np.array([1, 2, 31, 32, 33, 63, 64, 65, 500, 1500, 3000], np.int32)

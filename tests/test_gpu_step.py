@@ -77,6 +77,24 @@ def test_step_equals_append_then_decode(group, kv_bs):
         assert t.equal(got, want), f"nparts={nparts}"
 
 
+def test_step_wide_batch():
+    # 131 sequences (more than one 64-entry step of the range lookups), short
+    # and tile-edge lengths around the step edges
+    say("[step] 131 sequences")
+    t = torch()
+    lens = np.random.default_rng(78).integers(1, 300, 131).astype(np.int32)
+    lens[[62, 63, 64, 65, 127, 128, 130]] = [1, 32, 33, 31, 1, 64, 2]
+    nkv, nq = 2, 4
+    (a, b), k_new, v_new = _pair(lens, nkv, 32, seed=978)
+    q = t.from_numpy(np.random.default_rng(979).standard_normal((len(lens), nq, 128)).astype(np.float32)).cuda()
+    for nparts in (0, 3, 65, 300):
+        want = _separate(b, k_new, v_new, q, nq, nparts)
+        got = _fused(a, k_new, v_new, q, nq, nparts)
+        assert a.status_word() == 0 and b.status_word() == 0
+        _same_cache(a, b)
+        assert t.equal(got, want), f"nparts={nparts}"
+
+
 def test_step_with_mirror_and_8b_shape():
     say("[step] 8B shape with the fp32 mirror")
     t = torch()
