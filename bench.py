@@ -56,6 +56,9 @@ def parse():
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="only measure the read ceiling: stream a buffer of this many MiB once per launch "
+                         "(q8_stream_read), plain and non-temporal, over 256 / 512 / 1024 workgroups")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "q8_attn_partial_kernel_hbm_traffic.json"),
@@ -419,7 +422,7 @@ def prefill_cpu_baseline(w, lens):
     q = rng.standard_normal((rows, w.nq, w.head_dim), dtype=np.float32)
     tab, nbl = workloads.block_table(np.array([sample_len], np.int32), w.kv_bs, w.seed)
     cache = oracle.build_cache(k, v, np.array([sample_len], np.int32), tab, nbl, w.kv_bs)
-    threads = min(oracle.threads_available(), 16)
+    threads, host = oracle_threads(oracle)
     keys = rows * (sample_len - rows) + rows * (rows + 1) // 2
     flops = keys * w.nq * 4 * w.head_dim
     reps, t0 = 0, time.perf_counter()
@@ -431,7 +434,7 @@ def prefill_cpu_baseline(w, lens):
     dt = time.perf_counter() - t0
     return {"value": round(flops * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} query rows at positions {n - nb}..{n - nb + rows - 1} of one sequence, all "
-                      f"{w.nq} query heads, one layer, oracle prefill_attn repeated {reps}x in {dt:.1f} s"}
+                      f"{w.nq} query heads, one layer, oracle prefill_attn repeated {reps}x in {dt:.1f} s", **host}
 
 
 def prefill_main(args, torch, q8, dev):
@@ -503,6 +506,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe:
         copy_probe(torch, dev, args.copy_probe, args.steps)
+        return
+    if args.read_probe:
+        read_probe(torch, q8, dev, args.read_probe, args.steps, args.warmup)
         return
     w = workloads.WORKLOADS[args.workload]
     if args.path == "prefill":
@@ -596,6 +602,35 @@ def copy_probe(torch, dev, mib, reps):
     print(json.dumps({"copy_probe_bytes": mib * 2 ** 20, "reps": reps}), flush=True)
 
 
+def read_probe(torch, q8, dev, mib, reps, warmup):
+    """The read ceiling: q8_stream_read over a buffer of `mib` MiB (larger
+    than the 256 MB last-level cache, so every launch reads HBM), plain and
+    non-temporal loads, over 256 / 512 / 1024 workgroups; `reps` launches per
+    setting timed with HIP events on the library's stream (mean)."""
+    buf = torch.ones(mib * 2 ** 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    reps = max(reps, 3)
+    res = {}
+    for nt in (0, 1):
+        for wg in (256, 512, 1024):
+            for _ in range(max(warmup, 1)):
+                q8.stream_read(buf, wg, nt, sink)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(stream)
+            for i in range(reps):
+                q8.stream_read(buf, wg, nt, sink)
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            us = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) * 1e3
+            res[f"{'nt' if nt else 'plain'}_wg{wg}"] = {"us_mean": round(float(us.mean()), 2),
+                                                         "GBps": round(buf.numel() / (us.mean() * 1e-6) / 1e9, 1)}
+    best = max(res.values(), key=lambda r: r["GBps"])
+    print(json.dumps({"read_probe_bytes": buf.numel(), "reps": reps, "results": res,
+                      "best_GBps": best["GBps"], "best_pct_of_hbm_peak": round(100 * best["GBps"] / HBM_PEAK_GBS, 2)}),
+          flush=True)
+
+
 # the sources that define the q8 decode partial kernel and its launch plan
 KERNEL_SOURCES = ("q8kv_decode.hip", "q8kv_device.hpp", "q8kv_plan.hpp", "q8kv_ranges.hpp", "q8kv_tile.hpp")
 
@@ -627,7 +662,7 @@ def cpu_baseline(w, lens, table, nblocks, attn_bytes):
     own quantizer.  The oracle decode is repeated until ~10 s have passed;
     returns GB/s of the same algorithmic attention bytes."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    threads, host = oracle_threads(oracle)
     keep = np.cumsum(lens) <= 98304
     keep[0] = True
     sl = lens[keep]
@@ -650,7 +685,18 @@ def cpu_baseline(w, lens, table, nblocks, attn_bytes):
     b = int(n.sum()) * w.nkv * (2 * w.head_dim + 8) + sub.batch * w.nq * w.head_dim * 8
     return {"value": round(b * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{sub.batch} of {w.batch} sequences ({int(n.sum())} tokens, all {w.nq} query heads) "
-                      f"of one layer-step, oracle decode_attn repeated {reps}x in {dt:.1f} s"}
+                      f"of one layer-step, oracle decode_attn repeated {reps}x in {dt:.1f} s", **host}
+
+
+def oracle_threads(oracle):
+    """Threads for the CPU baseline: every thread this job may use -- the
+    OpenMP thread count (OMP_NUM_THREADS, which the GPU host sets to the CPU
+    share it gives a one-GPU job), else the CPUs in this process's affinity
+    mask -- and a record of what the host reports."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = oracle.threads_available() if omp else aff
+    return threads, {"nproc": os.cpu_count(), "affinity_cpus": aff, "omp_num_threads": omp}
 
 
 if __name__ == "__main__":

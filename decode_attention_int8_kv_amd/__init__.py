@@ -8,8 +8,14 @@ handle raises.
 
 Entry points (same names as the C ABI, without the ``q8_`` prefix):
   kv_append, decode_attn, decode_attn_partial, decode_attn_merge,
-  decode_attn_workspace_bytes, decode_attn_auto_parts, quantize_q,
-  qk_block_partials, abi_version, status_string, last_error.
+  decode_attn_workspace_bytes, decode_attn_auto_parts, decode_step,
+  decode_step_partial, decode_attn_f32, decode_attn_f32_partial,
+  decode_attn_sparse, decode_attn_sparse_workspace_bytes, prefill_attn,
+  quantize_q, qk_block_partials, abi_version, status_string, last_error.
+
+Every entry point checks the tensors it passes on (dtype, contiguity, size,
+one GPU device) and raises ValueError before anything is enqueued; the C ABI
+itself only sees pointers and cannot.
 """
 from __future__ import annotations
 
@@ -21,6 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq8kv.so")
 
 Q8_OK, Q8_EINVAL, Q8_EUNSUPPORTED, Q8_EWORKSPACE, Q8_EHIP = 0, -1, -2, -3, -4
+QPATH_VALU, QPATH_MFMA = 0, 1   # q8_quantize_q: two lanes or one lane per 32-block
 DEV_BAD_SEQ_LEN, DEV_BAD_BLOCK_ID, DEV_BAD_TOKEN = 0x1, 0x2, 0x4
 HEAD_DIM = 128
 
@@ -80,10 +87,12 @@ def _load():
         fn.restype = I32
     lib.q8_prefill_attn.argtypes = [LP, BP, I32, P, I32, I32, P, F, P, P, P]
     lib.q8_prefill_attn.restype = I32
-    lib.q8_quantize_q.argtypes = [P, I32, I32, P, P, P]
+    lib.q8_quantize_q.argtypes = [P, I32, I32, I32, P, P, P]
     lib.q8_quantize_q.restype = I32
-    lib.q8_qk_block_partials.argtypes = [LP, BP, I32, P, P, P, P]
+    lib.q8_qk_block_partials.argtypes = [LP, BP, I32, P, P, P, P, P, P]
     lib.q8_qk_block_partials.restype = I32
+    lib.q8_stream_read.argtypes = [P, SZ, I32, I32, P, P]
+    lib.q8_stream_read.restype = I32
     lib.q8_status_string.argtypes = [I32]
     lib.q8_status_string.restype = ctypes.c_char_p
     lib.q8_last_error.restype = ctypes.c_char_p
@@ -118,6 +127,73 @@ def _stream(stream):
 def _check(status: int, where: str):
     if status != Q8_OK:
         raise Q8Error(status, where)
+
+
+# Argument checks of the Python entry points.  The C ABI sees only pointers
+# and sizes, so it cannot tell an int64 table from an int32 one or a short
+# buffer from a long one; a wrong dtype, a strided view or an undersized
+# tensor would become an out-of-bounds device access.  Every tensor an entry
+# point hands to the library is checked here first (ValueError otherwise):
+# dtype, contiguity and size of each, then that all sit on one GPU.
+class _Args:
+    def __init__(self):
+        self.tensors = []
+
+    def need(self, t, name: str, dtype, min_numel: int, exact: bool = False):
+        """t: a contiguous tensor of `dtype` with at least (exactly, if
+        `exact`) `min_numel` elements; None is passed over."""
+        import torch
+        if t is None:
+            return self
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__} "
+                             "(raw pointers go through lib() directly)")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        n = t.numel()
+        if (exact and n != min_numel) or n < min_numel:
+            raise ValueError(f"{name}: {n} elements, expected {'' if exact else 'at least '}{min_numel}")
+        self.tensors.append((name, t))
+        return self
+
+    def layer(self, layer: "KVLayer"):
+        import torch
+        if (layer.k_f32 is None) != (layer.v_f32 is None):
+            raise ValueError("layer.k_f32 and layer.v_f32: both or neither")
+        row = layer.nkv_heads * layer.head_dim
+        rows = layer.num_blocks * layer.kv_bs
+        self.need(layer.k_codes, "layer.k_codes", torch.int8, rows * row, exact=True)
+        self.need(layer.v_codes, "layer.v_codes", torch.int8, rows * row, exact=True)
+        self.need(layer.k_scale, "layer.k_scale", torch.float32, rows * layer.nkv_heads, exact=True)
+        self.need(layer.v_scale, "layer.v_scale", torch.float32, rows * layer.nkv_heads, exact=True)
+        self.need(layer.k_f32, "layer.k_f32", torch.float32, rows * row, exact=True)
+        self.need(layer.v_f32, "layer.v_f32", torch.float32, rows * row, exact=True)
+        return self
+
+    def batch(self, batch: "Batch"):
+        import torch
+        self.need(batch.block_table, "batch.block_table", torch.int32, batch.batch * batch.max_blocks_per_seq,
+                  exact=True)
+        self.need(batch.seq_lens, "batch.seq_lens", torch.int32, batch.batch, exact=True)
+        return self
+
+    def done(self):
+        """All tensors on one GPU; returns the workspace-independent device."""
+        dev = None
+        for name, t in self.tensors:
+            if not t.is_cuda:
+                raise ValueError(f"{name}: must be on a GPU (is on {t.device})")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name}: on {t.device}, the other arguments are on {dev}")
+        return dev
+
+
+def _nbytes(workspace) -> int:
+    return workspace.numel() * workspace.element_size()
 
 
 @dataclasses.dataclass
@@ -178,13 +254,40 @@ def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head
 
 
 def make_batch(block_table, seq_lens, max_seq_len: int) -> Batch:
-    return Batch(block_table, seq_lens, int(block_table.shape[0]), int(block_table.shape[1]), int(max_seq_len))
+    """Batch from block_table int32 [batch, max_blocks_per_seq] and seq_lens
+    int32 [batch] (contiguous GPU tensors on one device)."""
+    import torch
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        raise ValueError("block_table: expected a 2-D torch tensor [batch, max_blocks_per_seq]")
+    b, mb = int(block_table.shape[0]), int(block_table.shape[1])
+    (_Args().need(block_table, "block_table", torch.int32, b * mb, exact=True)
+            .need(seq_lens, "seq_lens", torch.int32, b, exact=True).done())
+    return Batch(block_table, seq_lens, b, mb, int(max_seq_len))
 
 
 # ------------------------------------------------------------- entry points --
+def _common(layer, batch, dev_status):
+    import torch
+    return _Args().layer(layer).batch(batch).need(dev_status, "dev_status", torch.int32, 1)
+
+
+def _q_out(args, batch, nq_heads, q, out, head_dim=HEAD_DIM):
+    import torch
+    n = batch.batch * nq_heads * head_dim
+    return args.need(q, "q", torch.float32, n).need(out, "out", torch.float32, n)
+
+
 def kv_append(layer: KVLayer, batch: Batch, tok_seq, tok_pos, k_new, v_new, dev_status=None, stream=None):
-    """q8_kv_append: quantize k_new/v_new [n_tokens, nkv, 128] fp32 into the cache."""
-    n = int(tok_seq.shape[0])
+    """q8_kv_append: quantize k_new/v_new [n_tokens, nkv, 128] fp32 into the
+    cache at (tok_seq, tok_pos) (int32 [n_tokens])."""
+    import torch
+    if not isinstance(tok_seq, torch.Tensor):
+        raise ValueError("tok_seq: expected a torch tensor")
+    n = int(tok_seq.numel())
+    row = layer.nkv_heads * layer.head_dim
+    (_common(layer, batch, dev_status).need(tok_seq, "tok_seq", torch.int32, n, exact=True)
+        .need(tok_pos, "tok_pos", torch.int32, n, exact=True)
+        .need(k_new, "k_new", torch.float32, n * row).need(v_new, "v_new", torch.float32, n * row).done())
     st = _load().q8_kv_append(ctypes.byref(layer.c()), ctypes.byref(batch.c()), n, _ptr(tok_seq),
                               _ptr(tok_pos), _ptr(k_new), _ptr(v_new), _ptr(dev_status), _stream(stream))
     _check(st, "q8_kv_append")
@@ -200,10 +303,11 @@ def decode_attn_workspace_bytes(layer: KVLayer, batch: Batch, nq_heads: int, npa
 
 
 def _decode(name, layer, batch, nq_heads, q, scale, out, workspace, nparts, dev_status, stream):
+    args = _q_out(_common(layer, batch, dev_status), batch, nq_heads, q, out, layer.head_dim)
+    args.need(workspace, "workspace", None, 0).done()
     fn = getattr(_load(), name)
-    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     st = fn(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q), float(scale), _ptr(out),
-            nparts, _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(stream))
+            nparts, _ptr(workspace), _nbytes(workspace), _ptr(dev_status), _stream(stream))
     _check(st, name)
 
 
@@ -240,18 +344,26 @@ def decode_attn_sparse(layer, batch, nq_heads, q, scale, out, workspace, topk=32
                        stream=None):
     """q8_decode_attn_sparse: top-k 32-token blocks per query head by probe,
     exact q8 attention over them.  selected: optional int32 [batch, nq, topk]."""
-    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    import torch
+    args = _q_out(_common(layer, batch, dev_status), batch, nq_heads, q, out, layer.head_dim)
+    (args.need(selected, "selected", torch.int32, batch.batch * nq_heads * int(topk))
+         .need(workspace, "workspace", None, 0).done())
     st = _load().q8_decode_attn_sparse(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q),
                                        float(scale), _ptr(out), int(topk), _ptr(selected), _ptr(workspace),
-                                       ws_bytes, _ptr(dev_status), _stream(stream))
+                                       _nbytes(workspace), _ptr(dev_status), _stream(stream))
     _check(st, "q8_decode_attn_sparse")
 
 
 def _step(name, layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts, dev_status, stream):
-    ws_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    import torch
+    row = layer.nkv_heads * layer.head_dim
+    args = _q_out(_common(layer, batch, dev_status), batch, nq_heads, q, out, layer.head_dim)
+    (args.need(k_new, "k_new", torch.float32, batch.batch * row)
+         .need(v_new, "v_new", torch.float32, batch.batch * row)
+         .need(workspace, "workspace", None, 0).done())
     st = getattr(_load(), name)(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(k_new),
                                 _ptr(v_new), _ptr(q), float(scale), _ptr(out), int(nparts), _ptr(workspace),
-                                ws_bytes, _ptr(dev_status), _stream(stream))
+                                _nbytes(workspace), _ptr(dev_status), _stream(stream))
     _check(st, name)
 
 
@@ -275,25 +387,63 @@ def prefill_attn(layer, batch, nq_heads, q_start, max_new, q, scale, out, dev_st
     """q8_prefill_attn: causal attention of the new tokens' queries (the last
     q_start[b + 1] - q_start[b] positions of each sequence's cache) over the
     q8 cache.  q_start: device int32 [batch + 1]; q, out: [total_q, nq, 128]."""
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() < 1:
+        raise ValueError("q: expected a torch tensor [total_q, nq, 128]")
     total_q = int(q.shape[0])
+    n = total_q * nq_heads * layer.head_dim
+    (_common(layer, batch, dev_status).need(q_start, "q_start", torch.int32, batch.batch + 1, exact=True)
+        .need(q, "q", torch.float32, n, exact=True).need(out, "out", torch.float32, n).done())
     st = _load().q8_prefill_attn(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q_start),
                                  total_q, int(max_new), _ptr(q), float(scale), _ptr(out), _ptr(dev_status),
                                  _stream(stream))
     _check(st, "q8_prefill_attn")
 
 
-def quantize_q(q, codes, qscale, stream=None):
-    """q8_quantize_q test hook: q [rows, 128] fp32 -> codes int8 [rows, 128], qscale fp32 [rows, 4]."""
+def quantize_q(q, codes, qscale, path=QPATH_VALU, stream=None):
+    """q8_quantize_q test hook: q [rows, 128] fp32 -> codes int8 [rows, 128],
+    qscale fp32 [rows, 4], by the decode's two-lanes-per-block routine
+    (path=QPATH_VALU) or its one-lane-per-block matrix-core one (QPATH_MFMA)."""
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() < 1:
+        raise ValueError("q: expected a torch tensor [rows, 128]")
     rows = int(q.shape[0])
-    st = _load().q8_quantize_q(_ptr(q), rows, HEAD_DIM, _ptr(codes), _ptr(qscale), _stream(stream))
+    (_Args().need(q, "q", torch.float32, rows * HEAD_DIM, exact=True)
+        .need(codes, "codes", torch.int8, rows * HEAD_DIM)
+        .need(qscale, "qscale", torch.float32, rows * (HEAD_DIM // 32)).done())
+    st = _load().q8_quantize_q(_ptr(q), rows, HEAD_DIM, int(path), _ptr(codes), _ptr(qscale), _stream(stream))
     _check(st, "q8_quantize_q")
 
 
-def qk_block_partials(layer, batch, nq_heads, q, partials, dev_status=None, stream=None):
-    """q8_qk_block_partials test hook: partials int32 [batch, nq, max_seq_len, 4]."""
+def qk_block_partials(layer, batch, nq_heads, q, partials, qcodes=None, qscale=None, dev_status=None, stream=None):
+    """q8_qk_block_partials test hook: partials int32 [batch, nq, max_seq_len, 4]
+    and, optionally, the query codes int8 [batch, nq, 128] and scales fp32
+    [batch, nq, 4] they were formed with, by the decode's routine for the
+    shape."""
+    import torch
+    nblk = layer.head_dim // 32
+    if (qcodes is None) != (qscale is None):
+        raise ValueError("qcodes and qscale: both or neither")
+    (_common(layer, batch, dev_status).need(q, "q", torch.float32, batch.batch * nq_heads * layer.head_dim)
+        .need(partials, "partials", torch.int32, batch.batch * nq_heads * batch.max_seq_len * nblk)
+        .need(qcodes, "qcodes", torch.int8, batch.batch * nq_heads * layer.head_dim)
+        .need(qscale, "qscale", torch.float32, batch.batch * nq_heads * nblk).done())
     st = _load().q8_qk_block_partials(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(q),
-                                      _ptr(partials), _ptr(dev_status), _stream(stream))
+                                      _ptr(partials), _ptr(qcodes), _ptr(qscale), _ptr(dev_status),
+                                      _stream(stream))
     _check(st, "q8_qk_block_partials")
+
+
+def stream_read(buf, workgroups: int, nontemporal: bool, sink, stream=None):
+    """q8_stream_read measurement hook: read every byte of buf (a contiguous
+    GPU tensor, size a multiple of 16 bytes) once; sink: int32 GPU tensor."""
+    import torch
+    if not isinstance(buf, torch.Tensor):
+        raise ValueError("buf: expected a torch tensor")
+    _Args().need(buf, "buf", buf.dtype, 0).need(sink, "sink", torch.int32, 1).done()
+    st = _load().q8_stream_read(_ptr(buf), _nbytes(buf), int(workgroups), int(bool(nontemporal)), _ptr(sink),
+                                _stream(stream))
+    _check(st, "q8_stream_read")
 
 
 def abi_version() -> int:

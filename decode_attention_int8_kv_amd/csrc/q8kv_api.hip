@@ -259,32 +259,47 @@ q8_status q8_prefill_attn(const q8_kv_layer *layer, const q8_batch *batch, int32
     return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_prefill_attn");
 }
 
-q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int8_t *codes, float *qscale,
-                        void *stream)
+q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int32_t path, int8_t *codes,
+                        float *qscale, void *stream)
 {
     if (head_dim != q8kv::kHeadDim) return Q8_EUNSUPPORTED;
-    if (rows < 0) return Q8_EINVAL;
+    if (rows < 0 || (path != Q8_QPATH_VALU && path != Q8_QPATH_MFMA)) return Q8_EINVAL;
     if (rows == 0) return Q8_OK;
     if (!q || !codes || !qscale || !aligned(q, 16) || !aligned(codes, 16) || !aligned(qscale, 4))
         return Q8_EINVAL;
-    hipError_t e = q8kv::launch_quantize_q(q, rows, codes, qscale, static_cast<hipStream_t>(stream));
+    if ((long long)rows > 0x7fffffffLL / 4) return Q8_EUNSUPPORTED;
+    hipError_t e = q8kv::launch_quantize_q(q, rows, path, codes, qscale, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_quantize_q");
 }
 
 q8_status q8_qk_block_partials(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
-                               const float *q, int32_t *partials, int32_t *dev_status, void *stream)
+                               const float *q, int32_t *partials, int8_t *qcodes, float *qscale,
+                               int32_t *dev_status, void *stream)
 {
     q8_status s;
     if ((s = check_layer(layer)) != Q8_OK) return s;
     if ((s = check_batch(batch, layer)) != Q8_OK) return s;
     if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
-    if (!q || !partials || !aligned(q, 16) || !aligned(partials, 4)) return Q8_EINVAL;
+    if (!q || !partials || !aligned(q, 16) || !aligned(partials, 16)) return Q8_EINVAL;
+    if (!qcodes != !qscale) return Q8_EINVAL;
+    if (qcodes && (!aligned(qcodes, 16) || !aligned(qscale, 4))) return Q8_EINVAL;
     if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
     if ((batch->max_seq_len + q8kv::kTile - 1) / q8kv::kTile > 65535) return Q8_EUNSUPPORTED;
     if ((long long)batch->batch * layer->nkv_heads > 0x7fffffffLL) return Q8_EUNSUPPORTED;
-    hipError_t e = q8kv::launch_qk_partials(*layer, *batch, nq_heads, q, partials, dev_status,
+    hipError_t e = q8kv::launch_qk_partials(*layer, *batch, nq_heads, q, partials, qcodes, qscale, dev_status,
                                             static_cast<hipStream_t>(stream));
     return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_qk_block_partials");
+}
+
+q8_status q8_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t nontemporal, uint32_t *sink,
+                         void *stream)
+{
+    if (bytes == 0) return Q8_OK;
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes % 16) return Q8_EINVAL;
+    if (workgroups < 1 || workgroups > 65536 || (nontemporal != 0 && nontemporal != 1)) return Q8_EINVAL;
+    hipError_t e = q8kv::launch_stream_read(buf, bytes, workgroups, nontemporal, sink,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_stream_read");
 }
 
 const char *q8_status_string(int32_t status)

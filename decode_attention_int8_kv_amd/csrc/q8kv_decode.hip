@@ -258,18 +258,15 @@ piece_done:
     }
 }
 
-// Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores.
-// v_mfma_i32_16x16x64_i8 with A = the four heads' query codes (row 4 g + beta
-// holds head g's codes of 32-block beta, in k-group beta only) and B = K rows
-// (column j = token, lane (lg, j) holding bytes [32 lg, 32 lg + 32)) leaves
-// in lane (lg, j) the exact int32 partials of head lg with token j, four
-// blocks in four registers, two instructions per 16 tokens.  The score is
-// then formed once per (head, token) instead of in eight lanes: x_b = P_b *
-// qscale_b, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc).  The per-head
-// tile max is a row-of-16 reduction; each V lane (slot, c) receives its
-// head's (c % 4) weights with ds_bpermute and the value path is the 4x4x1
-// matrix-core outer product of attend_piece.
-typedef int v4i_dec __attribute__((ext_vector_type(4)));
+// Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores
+// (mf_query_operands / mf_block_partials in q8kv_tile.hpp): lane (lg, j)
+// receives the exact int32 partials of head lg with token j, four blocks in
+// four registers, two instructions per 16 tokens.  The score is then formed
+// once per (head, token) instead of in eight lanes: x_b = P_b * qscale_b,
+// y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc).  The per-head tile max is
+// a row-of-16 reduction; each V lane (slot, c) receives its head's (c % 4)
+// weights with ds_bpermute and the value path is the 4x4x1 matrix-core outer
+// product of attend_piece.
 
 __device__ __forceinline__ float row16_max(float v)
 {
@@ -292,7 +289,7 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
 {
     constexpr int G = 4;
     const int c = lane & 7, tslot = lane >> 3;
-    const int j = lane & 15, lg = lane >> 4;
+    const int lg = lane >> 4;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
 
     // A operands: head g = j / 4's codes of block beta = j % 4 in k-group
@@ -308,30 +305,19 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
     // the query block and the first tile's block id together, the first
     // tile's loads before the quantization (as in attend_piece)
     float4 qv[8];
-    {
-        const float4 *qp = reinterpret_cast<const float4 *>(p.q + ((size_t)b * p.nq + kh * G + (j >> 2)) * kHeadDim +
-                                                            32 * (j & 3));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[i] = qp[i];
-    }
+    mf_load_query(p.q + ((size_t)b * p.nq + kh * G) * kHeadDim, lane, qv);
     fetch_blocks_ahead<true>(bt, log2bs, lt0 * kTile, ne, bl[0]);
     load_tile_mf(p.cache, bl[0], lo, lane, lt0 * kTile, ne, p.dev_status, t[0]);
     fetch_blocks_ahead<true>(bt, log2bs, (lt0 + 1) * kTile, ne, bl[1]);
     __builtin_amdgcn_sched_barrier(0);
 
-    v4i_dec qa[2];
-    float qs[4];
+    MfQuery mq;
     {
-        const int beta = j & 3;
         uint4 qlo, qhi;
         float step;
-        quantize_q_block_vals(qv, qlo, qhi, step);
-        const bool mine = lg == beta;
-        qa[0] = __builtin_bit_cast(v4i_dec, mine ? qlo : make_uint4(0, 0, 0, 0));
-        qa[1] = __builtin_bit_cast(v4i_dec, mine ? qhi : make_uint4(0, 0, 0, 0));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) qs[r] = __shfl(step, 4 * lg + r, 64);
+        mf_query_operands(qv, lane, mq, qlo, qhi, step);
     }
+    const float *qs = mq.qs;
 
     float M[G], Sl = 0.0f;   // M per head (uniform); Sl: this lane's share of head lg's sum
     v4f accm[16];
@@ -353,10 +339,7 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         float s[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            v4i_dec acc_i = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[0], __builtin_bit_cast(v4i_dec, t.k[2 * m]),
-                                                                  v4i_dec{0, 0, 0, 0}, 0, 0, 0);
-            acc_i = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[1], __builtin_bit_cast(v4i_dec, t.k[2 * m + 1]), acc_i,
-                                                          0, 0, 0);
+            const v4i_mf acc_i = mf_block_partials(mq, t.k, m);
             const float x0 = (float)acc_i[0] * qs[0], x1 = (float)acc_i[1] * qs[1];
             const float x2 = (float)acc_i[2] * qs[2], x3 = (float)acc_i[3] * qs[3];
             const float y = (x0 + x1) + (x3 + x2);
@@ -466,6 +449,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
 {
     extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
     walk_ranges(p, lds_batch, lds_batch + p.batch + 1, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
+        // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
         if constexpr (G == 4 && Big)
             attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
         else

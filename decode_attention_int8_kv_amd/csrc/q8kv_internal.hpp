@@ -48,11 +48,19 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
 // Resident workgroups per CU of the decode kernel for this group size.
 int decode_blocks_per_cu(int group, int waves, int batch);
 
-hipError_t launch_quantize_q(const float *q, int32_t rows, int8_t *codes, float *qscale,
+// The decode's score path for a shape: the i8 matrix cores at four query
+// heads per KV head when a 32-token tile lies in one block (kv_bs >= 32),
+// else sdot4 over two lanes per 32-block.
+inline bool decode_uses_mfma_scores(int group, int kv_bs) { return group == 4 && kv_bs >= 32; }
+
+hipError_t launch_quantize_q(const float *q, int32_t rows, int32_t path, int8_t *codes, float *qscale,
                              hipStream_t stream);
 
-hipError_t launch_qk_partials(const q8_kv_layer &layer, const q8_batch &batch, int nq,
-                              const float *q, int32_t *partials, int32_t *dev_status,
+hipError_t launch_qk_partials(const q8_kv_layer &layer, const q8_batch &batch, int nq, const float *q,
+                              int32_t *partials, int8_t *qcodes, float *qscale, int32_t *dev_status,
+                              hipStream_t stream);
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, int workgroups, int nontemporal, uint32_t *sink,
                               hipStream_t stream);
 
 }  // namespace q8kv

@@ -7,10 +7,15 @@
 // at most k blocks (which includes every sequence of at most two blocks, the
 // page's gate, since k >= 2) keep every block.  Readings where the page
 // defers to another: probe rows 0, 4, ..., 28 of a block; a block's
-// importance is the largest q8 attention score of its probe rows, in fp32
-// with every product and sum rounded on its own (x_b = P_b * qscale_b,
-// y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc)); selection per query
-// head, ties to the lower block index, nothing forced in.
+// importance is the largest q8 attention score of its probe rows ("9-2
+// flash_attn_single_q_q8_neon" §2 segment 2: s = (sum over 32-blocks of
+// P_b * qscale_b) * kscale * scale); selection per query head, ties to the
+// lower block index, nothing forced in.  The probe evaluates s in fp32 with
+// every product and sum rounded on its own (x_b = P_b * qscale_b exact
+// partials, y = (x0 + x1) + (x3 + x2), s = y * (kscale * sc), sc = scale *
+// log2 e, a positive factor common to all blocks), so its value lies within
+// about 5 * 2^-24 * scale * kscale * sum_b |x_b| of the exact score, and the
+// kept set is the exact top k up to blocks whose scores lie that close.
 //
 // Kernels (one call enqueues them in this order):
 //   probe  -- one wave per (sequence, KV head, 16 blocks), the waves of a
@@ -163,9 +168,9 @@ __global__ __launch_bounds__(64 * kProbeWaves) void q8_sparse_probe_kernel(Spars
                                                       c, 0, 0, 0);
             float sv;
             {
-                // every product and sum rounded on its own: the score decides
-                // which blocks are kept, so it must be the formula's exact fp32
-                // value (no fused multiply-add)
+                // every product and sum rounded on its own (no fused
+                // multiply-add), so the error against the exact score stays
+                // within the bound stated at the top of this file
 #pragma clang fp contract(off)
                 const float x0 = (float)c[0] * qsc[st][0], x1 = (float)c[1] * qsc[st][1];
                 const float x2 = (float)c[2] * qsc[st][2], x3 = (float)c[3] * qsc[st][3];

@@ -264,6 +264,56 @@ __device__ __forceinline__ void load_tile_mf(const CacheView &cv, const TileBloc
     for (int kk = 0; kk < 4; ++kk) t.v[kk] = buf_load16(rv, lo.code, kk * kSub * row_bytes);
 }
 
+// ------------------------------------- four query heads per KV head, MFMA --
+// The score path of q8_decode_attn when nq / nkv == 4 and kv_bs >= 32 (and
+// of the partials test hook on those shapes): v_mfma_i32_16x16x64_i8 with
+// A = the four heads' query codes -- row 4 g + beta holds head g's codes of
+// 32-block beta, placed in k-group beta only, zeros elsewhere -- and B = 16
+// K rows in load_tile_mf's layout.  Lane (lg, j) = (lane / 16, lane % 16)
+// then holds the exact int32 partials of head lg with token j of the
+// 16-token half, block beta in register beta ("9-2 flash_attn_single_q_q8_neon"
+// §2 segments 1-2: one exact int32 sum per 32-block).
+typedef int v4i_mf __attribute__((ext_vector_type(4)));
+
+struct MfQuery {
+    v4i_mf a[2];   // A operand: 32 code bytes of (head (lane % 16) / 4, block lane % 4) in k-group lane / 16 only
+    float qs[4];   // qscale of head lane / 16, blocks 0..3
+};
+
+// The query block lane (lg, j) quantizes: head j / 4 of the group, 32-block
+// j % 4 (q_group: the group's first query row; 128 fp32 per head).
+__device__ __forceinline__ void mf_load_query(const float *q_group, int lane, float4 (&qv)[8])
+{
+    const int j = lane & 15;
+    const float4 *qp = reinterpret_cast<const float4 *>(q_group + (j >> 2) * kHeadDim + 32 * (j & 3));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = qp[i];
+}
+
+// Quantizes the lane's block ("9-2" §2 segment 1, one lane per 32-block) and
+// forms the A operands and the per-lane block scales; lo, hi, step are the
+// lane's own codes and scale.
+__device__ __forceinline__ void mf_query_operands(const float4 (&qv)[8], int lane, MfQuery &mq, uint4 &lo,
+                                                  uint4 &hi, float &step)
+{
+    const int j = lane & 15, lg = lane >> 4;
+    quantize_q_block_vals(qv, lo, hi, step);
+    const bool mine = lg == (j & 3);
+    mq.a[0] = __builtin_bit_cast(v4i_mf, mine ? lo : make_uint4(0, 0, 0, 0));
+    mq.a[1] = __builtin_bit_cast(v4i_mf, mine ? hi : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mq.qs[r] = __shfl(step, 4 * lg + r, 64);
+}
+
+// The exact int32 block partials of 16 tokens (m = 0: t0 .. t0 + 15, m = 1:
+// t0 + 16 .. t0 + 31) of a tile loaded by load_tile_mf.
+__device__ __forceinline__ v4i_mf mf_block_partials(const MfQuery &mq, const uint4 (&k)[4], int m)
+{
+    v4i_mf acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(mq.a[0], __builtin_bit_cast(v4i_mf, k[2 * m]),
+                                                       v4i_mf{0, 0, 0, 0}, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(mq.a[1], __builtin_bit_cast(v4i_mf, k[2 * m + 1]), acc, 0, 0, 0);
+}
+
 // K and V scales of this lane's token in sub-tile kk, from the lanes of the
 // same 8-lane group that loaded them (see Tile::sc).
 template <int KK>

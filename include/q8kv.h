@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 4
+#define Q8KV_ABI_VERSION 5
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -214,9 +214,10 @@ q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *b
 /* Block-sparse decode ("why long context must be sparse" §1-§2): per
  * sequence b and query head h, the history is cut into 32-token blocks; each
  * block is probed at its rows 0, 4, ..., 28 and scored by the largest q8
- * attention score among them (fp32, each product and sum rounded on its
- * own: x_b = P_b * qscale_b, y = (x0 + x1) + (x3 + x2), s = y * (kscale *
- * scale * log2 e)); the `topk`
+ * attention score among them ("9-2" §2 segment 2: s = (sum over 32-blocks of
+ * P_b * qscale_b) * kscale * scale, evaluated in fp32 with each product and
+ * sum rounded on its own, within about 5 * 2^-24 * scale * kscale *
+ * sum_b |P_b * qscale_b| of the exact value); the `topk`
  * highest-scoring blocks (ties: lower block index) are kept, and out[b][h]
  * is the exact q8 single-pass attention ("9-2" §2) over the tokens of those
  * blocks.  A sequence of at most topk blocks keeps every block (the result
@@ -264,21 +265,50 @@ q8_status q8_prefill_attn(const q8_kv_layer *layer, const q8_batch *batch, int32
  * `rows` rows of head_dim (== 128) values: per 32-block, m = max |q| (m := 1
  * when m < 1e-6), qscale = m * fl(1/127), r = 127 / m,
  * code = (int8) truncation toward zero of clamp(q * r, -128, 127).
+ * path selects which of the decode's two device routines runs (they compute
+ * the same codes in different lane layouts):
+ *   Q8_QPATH_VALU -- two lanes per 32-block; q8_decode_attn and
+ *                    q8_decode_step use it unless nq/nkv == 4 with
+ *                    kv_bs >= 32, and so does the sparse attention;
+ *   Q8_QPATH_MFMA -- one lane per 32-block, four rows per wave (the A-operand
+ *                    layout of the i8 matrix-core scores); the decode uses it
+ *                    at nq/nkv == 4 with kv_bs >= 32, and the sparse probe.
  * q: device fp32 [rows][head_dim] (16-byte aligned); codes: device int8
- * [rows][head_dim]; qscale: device fp32 [rows][head_dim / 32].
- * Runs the same device routine as q8_decode_attn. */
-q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim,
+ * [rows][head_dim]; qscale: device fp32 [rows][head_dim / 32].  Q8_EINVAL
+ * for an unknown path. */
+#define Q8_QPATH_VALU 0
+#define Q8_QPATH_MFMA 1
+q8_status q8_quantize_q(const float *q, int32_t rows, int32_t head_dim, int32_t path,
                         int8_t *codes, float *qscale, void *stream);
 
 /* Test hook: the exact int32 block sums the decode kernel forms ("9-2" §2
  * segment 2), P[b][h][t][blk] = sum over i in block blk of qcode[i] *
  * kcode_t[i], for every sequence b, query head h and t < seq_lens[b];
  * entries with seq_lens[b] <= t < max_seq_len are written as 0.
- * partials: device int32 [batch][nq_heads][max_seq_len][head_dim / 32].
- * Runs the same device routines as q8_decode_attn. */
+ * partials: device int32 [batch][nq_heads][max_seq_len][head_dim / 32],
+ * 16-byte aligned.  qcodes, qscale: both NULL, or device int8
+ * [batch][nq_heads][head_dim] (16-byte aligned) and fp32
+ * [batch][nq_heads][head_dim / 32] receiving the query codes and scales the
+ * partials were formed with.  Runs the device routines and operand layout
+ * q8_decode_attn uses for this shape: the i8 matrix cores
+ * (v_mfma_i32_16x16x64_i8, query quantized one lane per 32-block) at
+ * nq/nkv == 4 with kv_bs >= 32, else sdot4 with the query quantized two
+ * lanes per 32-block. */
 q8_status q8_qk_block_partials(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
-                               const float *q, int32_t *partials,
+                               const float *q, int32_t *partials, int8_t *qcodes, float *qscale,
                                int32_t *dev_status, void *stream);
+
+/* Measurement hook: reads `bytes` (a multiple of 16) of device memory at buf
+ * (16-byte aligned) exactly once with 16-byte loads -- the buffer split
+ * evenly over `workgroups` workgroups of 512 lanes, four loads in flight per
+ * lane, plain (nontemporal = 0) or non-temporal (1, the hint the decode's
+ * cache loads carry) -- and writes *sink (device uint32) only if a value
+ * folded from all loads equals a fixed constant.  The time it takes is the
+ * read ceiling the decode kernel is measured against: the decode must read
+ * every byte of the cache once ("why long context must be sparse" §1).
+ * bytes == 0 is a no-op; workgroups in [1, 65536]. */
+q8_status q8_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t nontemporal,
+                         uint32_t *sink, void *stream);
 
 /* Short English name of a status code (static string). */
 const char *q8_status_string(int32_t status);

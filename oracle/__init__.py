@@ -31,7 +31,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q8kv_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle_q8kv.so")
+# Q8KV_ORACLE_LIB names another build of the same source (a sanitizer build,
+# for instance); by default the library is built next to the source.
+_LIB_PATH = os.environ.get("Q8KV_ORACLE_LIB") or os.path.join(_HERE, "liboracle_q8kv.so")
 _lib = None
 
 HEAD_BLOCK = 32  # Q block length (9-2 §2 segment 1)
@@ -73,8 +75,10 @@ def _load():
     lib.orc_decode_attn_f32.restype = I
     lib.orc_decode_attn_sparse.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, P, P, F, I, P, P, I]
     lib.orc_decode_attn_sparse.restype = I
-    lib.orc_sparse_scores.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, I, P]
+    lib.orc_sparse_scores.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, F, I, P, P]
     lib.orc_sparse_scores.restype = I
+    lib.orc_decode_attn_blocks.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, P, P, F, P, I, P, I]
+    lib.orc_decode_attn_blocks.restype = I
     lib.orc_prefill_attn.argtypes = [I, I, I, I, I, P, I, P, I, P, P, P, P, P, I, P, F, P, I]
     lib.orc_prefill_attn.restype = I
     lib.orc_num_threads_available.restype = I
@@ -335,7 +339,8 @@ SPARSE_PROBES = 8     # probe samples per block
 
 def decode_attn_sparse(cache: Cache, q: np.ndarray, nq: int, scale: float, topk: int = 32, nthreads: int = 0):
     """Block-sparse decode ("10-1" §1-§2): per (b, h) the top-k 32-token blocks
-    by probe score, then exact attention over their tokens.  Returns
+    by importance (``sparse_scores``, ranked exactly in double, ties to the
+    lower block), then exact attention over their tokens.  Returns
     (out [batch, nq, hd] fp32, selected [batch, nq, topk] int32 block indices
     ascending, -1 after the last)."""
     if topk < 2:
@@ -378,17 +383,45 @@ def prefill_attn(cache: Cache, q: np.ndarray, q_start, nq: int, scale: float, nt
     return out
 
 
-def sparse_scores(cache: Cache, q: np.ndarray, nq: int, scale: float) -> np.ndarray:
-    """Probe score of every 32-token block of every (b, h) -> [batch, nq,
-    max blocks] fp32, -inf past a sequence's last block."""
+def sparse_scores(cache: Cache, q: np.ndarray, nq: int, scale: float):
+    """Importance of every 32-token block of every (b, h) ("10-1" §1-§2,
+    readings in the C source): the largest over the block's probe rows 0, 4,
+    ..., 28 of the page's q8 score s = (sum_b P_b * qscale_b) * kscale * scale
+    ("9-2" §2 segment 2), in double.  Returns (scores [batch, nq, max blocks]
+    float64, -inf past a sequence's last block; mags, the same shape: the
+    largest over the block's probe rows of the same expression with every
+    block term taken by absolute value, 0 past the end)."""
     q = _c(q, np.float32)
     max_nb = max(1, (int(cache.seq_lens.max()) + SPARSE_BLOCK - 1) // SPARSE_BLOCK)
-    out = np.empty((cache.batch, nq, max_nb), np.float32)
+    out = np.empty((cache.batch, nq, max_nb), np.float64)
+    mag = np.empty((cache.batch, nq, max_nb), np.float64)
     rc = _load().orc_sparse_scores(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
                                    _p(cache.block_table), cache.max_blocks_per_seq,
                                    _p(cache.seq_lens), cache.num_blocks,
                                    _p(cache.k_codes), _p(cache.k_step),
-                                   _p(q), float(np.float32(scale)), max_nb, _p(out))
+                                   _p(q), float(np.float32(scale)), max_nb, _p(out), _p(mag))
     if rc:
         raise ValueError("oracle: bad sequence length or block id")
+    return out, mag
+
+
+def decode_attn_blocks(cache: Cache, q: np.ndarray, nq: int, scale: float, sel, nthreads: int = 0) -> np.ndarray:
+    """Attention (O4-O7) of every (b, h) over the tokens of a given set of
+    32-token blocks: sel [batch, nq, width] int32 block indices, ended by the
+    first negative entry (the block order given is the summation order).
+    q: [batch, nq, hd] -> [batch, nq, hd] fp32."""
+    q = _c(q, np.float32)
+    sel = _c(np.asarray(sel), np.int32)
+    if sel.ndim != 3 or sel.shape[:2] != (cache.batch, nq):
+        raise ValueError("sel must be [batch, nq, width]")
+    out = np.empty(q.shape, np.float32)
+    nthreads = nthreads or threads_available()
+    rc = _load().orc_decode_attn_blocks(cache.batch, nq, cache.nkv, cache.hd, cache.kv_bs,
+                                        _p(cache.block_table), cache.max_blocks_per_seq,
+                                        _p(cache.seq_lens), cache.num_blocks,
+                                        _p(cache.k_codes), _p(cache.v_codes),
+                                        _p(cache.k_step), _p(cache.v_step),
+                                        _p(q), float(np.float32(scale)), _p(sel), sel.shape[2], _p(out), nthreads)
+    if rc:
+        raise ValueError("oracle: bad sequence length, block index or block id")
     return out

@@ -441,132 +441,135 @@ void orc_single_pass(const int8_t *cq, const float *qsc,
  * is not available; the readings taken here:
  *   - probe rows: 8 evenly spaced rows 0, 4, ..., 28 of each block (those
  *     below the sequence length);
- *   - a block's importance: the maximum, over its probe rows, of the same
- *     q8 attention score the exact path uses;
- *   - selection per query head, top k by importance, ties to the lower block
- *     index; nothing forced in; all blocks when the sequence has at most 2
- *     blocks' worth of tokens or at most k blocks;
- *   - attention over every token of the chosen blocks, in block order.
- * The selection is a decision taken in floating point, so it uses the GPU
- * kernel's fp32 score formula, step for step: per 32-element Q block
- * x_b = fl(float(P_b) * qscale_b), y = fl(fl(x0 + x1) + fl(x3 + x2)), score =
- * fl(y * fl(kscale * sc)) with sc = fl(scale * log2 e) (a monotone image of
- * the page's score, so the ranking is the same up to that rounding). */
+ *   - a probe row's value is the q8 attention score of that row as [9-2] §2
+ *     segment 2 defines it: the int32 block sums P_b of the query and key
+ *     codes, s = (sum over blocks of P_b * qscale_b) * kscale * scale --
+ *     evaluated here in double (every P_b * qscale_b is exact in double; the
+ *     sum and the two products round once each, far below any fp32 ulp);
+ *   - a block's importance: the maximum over its probe rows ("max-dot
+ *     fusion");
+ *   - selection per query head: the k blocks of highest importance, ties to
+ *     the lower block index; nothing forced in; every block when the
+ *     sequence has at most 2 blocks' worth of tokens or at most k blocks;
+ *   - attention over every token of the chosen blocks (O4-O7 restricted to
+ *     them).
+ * An implementation that evaluates the score in lower precision may keep a
+ * different set only among blocks whose importances lie within its rounding
+ * of each other; the tests judge its kept set against these double scores. */
 #define ORC_SPARSE_BLOCK 32
 #define ORC_SPARSE_PROBES 8
 
-static float orc_probe_score(const int8_t *cq, const float *qsc, const int8_t *ck, float ks, float sc)
+/* The page's score of one key row against the quantized query, in double;
+ * *mag (if not NULL) receives the same expression with every block term
+ * taken by absolute value (the scale of the terms the sum cancels). */
+static double orc_probe_score(const int8_t *cq, const float *qsc, const int8_t *ck, float ks, float scale,
+                              double *mag)
 {
-    float x[4];
+    double s = 0.0, a = 0.0;
     for (int blk = 0; blk < 4; ++blk) {
         int64_t p = 0;
         for (int i = 32 * blk; i < 32 * blk + 32; ++i) p += (int64_t)cq[i] * (int64_t)ck[i];
-        x[blk] = (float)p * qsc[blk];
+        double x = (double)p * (double)qsc[blk];
+        s += x;
+        a += fabs(x);
     }
-    float y = (x[0] + x[1]) + (x[3] + x[2]);
-    float f = ks * sc;
-    return y * f;
+    if (mag) *mag = a * (double)ks * (double)scale;
+    return s * (double)ks * (double)scale;
 }
 
-/* Probe score of every sparse block of every (b, h): scores[b][h][j] for
- * j < ceil(seq_lens[b] / 32), -inf up to max_nb.  Returns 0, or -1 on a bad
- * length or block id. */
+/* Importance of every block of one (b, h) of length n into score[0..nb) (and
+ * mag[0..nb) if not NULL: the largest mag over the block's probe rows, which
+ * bounds how far any row score can move under a rounding of its terms).
+ * Returns 0, or -1 on a bad block id. */
+static int orc_block_importance(int b, int kh, int nkv, int hd, int kv_bs, const int32_t *block_table,
+                                int max_blocks_per_seq, int num_blocks, int64_t n, const int8_t *k_codes,
+                                const float *k_step, const int8_t *cq, const float *qsc, float scale,
+                                double *score, double *mag)
+{
+    int nb = (int)((n + ORC_SPARSE_BLOCK - 1) / ORC_SPARSE_BLOCK);
+    for (int j = 0; j < nb; ++j) {
+        double best = -INFINITY, best_mag = 0.0;
+        for (int pr = 0; pr < ORC_SPARSE_PROBES; ++pr) {
+            int64_t t = (int64_t)j * ORC_SPARSE_BLOCK + pr * (ORC_SPARSE_BLOCK / ORC_SPARSE_PROBES);
+            if (t >= n) break;
+            int64_t r = orc_row_of(block_table, max_blocks_per_seq, b, t, kv_bs, num_blocks);
+            if (r < 0) return -1;
+            double m;
+            double sc = orc_probe_score(cq, qsc, k_codes + (r * nkv + kh) * hd, k_step[r * nkv + kh], scale, &m);
+            if (sc > best) best = sc;
+            if (m > best_mag) best_mag = m;
+        }
+        score[j] = best;
+        if (mag) mag[j] = best_mag;
+    }
+    return 0;
+}
+
+/* Importance of every block of every (b, h): scores[b][h][j] for j <
+ * ceil(seq_lens[b] / 32), -inf up to max_nb; mags (may be NULL) likewise,
+ * 0 past the end.  Returns 0, or -1 on a bad length or block id. */
 int orc_sparse_scores(int batch, int nq, int nkv, int hd, int kv_bs,
                       const int32_t *block_table, int max_blocks_per_seq,
                       const int32_t *seq_lens, int num_blocks,
                       const int8_t *k_codes, const float *k_step,
-                      const float *q, float scale, int max_nb, float *scores)
+                      const float *q, float scale, int max_nb, double *scores, double *mags)
 {
     int status = 0;
-    const float sc = (float)((double)scale * 1.4426950408889634);
     for (int b = 0; b < batch; ++b) {
         int64_t n = seq_lens[b];
         for (int h = 0; h < nq; ++h) {
-            float *o = scores + ((int64_t)b * nq + h) * max_nb;
-            for (int j = 0; j < max_nb; ++j) o[j] = -INFINITY;
+            double *o = scores + ((int64_t)b * nq + h) * max_nb;
+            double *m = mags ? mags + ((int64_t)b * nq + h) * max_nb : NULL;
+            for (int j = 0; j < max_nb; ++j) {
+                o[j] = -INFINITY;
+                if (m) m[j] = 0.0;
+            }
             if (n < 0 || n > (int64_t)max_blocks_per_seq * kv_bs || (n + 31) / 32 > max_nb) { status = -1; continue; }
-            int kh = h / (nq / nkv);
             int8_t cq[128];
             float qsc[4];
             orc_quantize_q(q + ((int64_t)b * nq + h) * hd, hd, cq, qsc);
-            for (int64_t t = 0; t < n; t += ORC_SPARSE_BLOCK / ORC_SPARSE_PROBES) {
-                int64_t r = orc_row_of(block_table, max_blocks_per_seq, b, t, kv_bs, num_blocks);
-                if (r < 0) { status = -1; break; }
-                float s = orc_probe_score(cq, qsc, k_codes + (r * nkv + kh) * hd, k_step[r * nkv + kh], sc);
-                int j = (int)(t / ORC_SPARSE_BLOCK);
-                if (s > o[j]) o[j] = s;
-            }
+            if (orc_block_importance(b, h / (nq / nkv), nkv, hd, kv_bs, block_table, max_blocks_per_seq,
+                                     num_blocks, n, k_codes, k_step, cq, qsc, scale, o, m))
+                status = -1;
         }
     }
     return status;
 }
 
-/* One (b, h): the selected sparse blocks (ascending) into sel[0..count), and
- * the attention over their tokens into o.  Returns count, or -1 on a bad
- * length or block id (o = zeros). */
-static int orc_one_row_sparse(int b, int h, int nq, int nkv, int hd, int kv_bs,
-                              const int32_t *block_table, int max_blocks_per_seq,
-                              const int32_t *seq_lens, int num_blocks,
-                              const int8_t *k_codes, const int8_t *v_codes,
-                              const float *k_step, const float *v_step,
-                              const float *q_row, float scale, int topk, float *o, int32_t *sel)
+/* One (b, h): attention (O4-O7) over the tokens of the blocks sel[0..count)
+ * of sequence b (32-token blocks; the last one ends at seq_lens[b]), taken in
+ * the order given.  o = zeros when count is 0.  Returns 0, or -1 on a bad
+ * length, block index or block id (o = zeros). */
+static int orc_attend_blocks(int b, int h, int nq, int nkv, int hd, int kv_bs,
+                             const int32_t *block_table, int max_blocks_per_seq,
+                             const int32_t *seq_lens, int num_blocks,
+                             const int8_t *k_codes, const int8_t *v_codes,
+                             const float *k_step, const float *v_step,
+                             const float *q_row, float scale, const int32_t *sel, int count, float *o)
 {
     int kh = h / (nq / nkv);
     int64_t n = seq_lens[b];
     for (int i = 0; i < hd; ++i) o[i] = 0.0f;
     if (n < 0 || n > (int64_t)max_blocks_per_seq * kv_bs) return -1;
-    if (n == 0) return 0;
     int nb = (int)((n + ORC_SPARSE_BLOCK - 1) / ORC_SPARSE_BLOCK);
-    int8_t cq[128];
-    float qsc[4];
-    orc_quantize_q(q_row, hd, cq, qsc);
-    const float sc = (float)((double)scale * 1.4426950408889634);
-
-    int count = 0;
-    if (n <= 2 * ORC_SPARSE_BLOCK || nb <= topk) {
-        for (int j = 0; j < nb; ++j) sel[count++] = j;
-    } else {
-        float *score = (float *)malloc(sizeof(float) * (size_t)nb);
-        char *taken = (char *)calloc((size_t)nb, 1);
-        for (int j = 0; j < nb; ++j) {
-            float best = -INFINITY;
-            for (int pr = 0; pr < ORC_SPARSE_PROBES; ++pr) {
-                int64_t t = (int64_t)j * ORC_SPARSE_BLOCK + pr * (ORC_SPARSE_BLOCK / ORC_SPARSE_PROBES);
-                if (t >= n) break;
-                int64_t r = orc_row_of(block_table, max_blocks_per_seq, b, t, kv_bs, num_blocks);
-                if (r < 0) { free(score); free(taken); return -1; }
-                float s = orc_probe_score(cq, qsc, k_codes + (r * nkv + kh) * hd, k_step[r * nkv + kh], sc);
-                if (s > best) best = s;
-            }
-            score[j] = best;
-        }
-        /* k rounds of "the highest score not taken yet, lowest index on ties" */
-        for (int round = 0; round < topk; ++round) {
-            int arg = -1;
-            for (int j = 0; j < nb; ++j)
-                if (!taken[j] && (arg < 0 || score[j] > score[arg])) arg = j;
-            taken[arg] = 1;
-        }
-        for (int j = 0; j < nb; ++j)
-            if (taken[j]) sel[count++] = j;
-        free(score);
-        free(taken);
-    }
-
-    /* exact attention over the chosen blocks' tokens (O4-O7) */
     int64_t m = 0;
     for (int c = 0; c < count; ++c) {
+        if (sel[c] < 0 || sel[c] >= nb) return -1;
         int64_t t1 = (int64_t)(sel[c] + 1) * ORC_SPARSE_BLOCK;
         m += (t1 < n ? t1 : n) - (int64_t)sel[c] * ORC_SPARSE_BLOCK;
     }
+    if (m == 0) return 0;
+    int8_t cq[128];
+    float qsc[4];
+    orc_quantize_q(q_row, hd, cq, qsc);
     double *qh = (double *)malloc(sizeof(double) * (size_t)hd);
     double *kk = (double *)malloc(sizeof(double) * (size_t)(m * hd));
     double *vv = (double *)malloc(sizeof(double) * (size_t)(m * hd));
     double *oh = (double *)malloc(sizeof(double) * (size_t)hd);
     for (int i = 0; i < hd; ++i) qh[i] = (double)cq[i] * (double)qsc[i / 32];
-    int rc = count;
+    int rc = 0;
     int64_t u = 0;
-    for (int c = 0; c < count && rc >= 0; ++c) {
+    for (int c = 0; c < count && rc == 0; ++c) {
         for (int64_t t = (int64_t)sel[c] * ORC_SPARSE_BLOCK; t < (int64_t)(sel[c] + 1) * ORC_SPARSE_BLOCK && t < n; ++t) {
             int64_t r = orc_row_of(block_table, max_blocks_per_seq, b, t, kv_bs, num_blocks);
             if (r < 0) { rc = -1; break; }
@@ -580,12 +583,60 @@ static int orc_one_row_sparse(int b, int h, int nq, int nkv, int hd, int kv_bs,
             ++u;
         }
     }
-    if (rc >= 0) {
+    if (rc == 0) {
         orc_attend_dense(qh, kk, vv, m, hd, (double)scale, oh);
         for (int i = 0; i < hd; ++i) o[i] = (float)oh[i];
     }
     free(qh); free(kk); free(vv); free(oh);
     return rc;
+}
+
+/* One (b, h) of the block-sparse decode: the kept blocks (ascending) into
+ * sel[0..count) and the attention over their tokens into o.  Returns count,
+ * or -1 on a bad length or block id (o = zeros). */
+static int orc_one_row_sparse(int b, int h, int nq, int nkv, int hd, int kv_bs,
+                              const int32_t *block_table, int max_blocks_per_seq,
+                              const int32_t *seq_lens, int num_blocks,
+                              const int8_t *k_codes, const int8_t *v_codes,
+                              const float *k_step, const float *v_step,
+                              const float *q_row, float scale, int topk, float *o, int32_t *sel)
+{
+    int64_t n = seq_lens[b];
+    for (int i = 0; i < hd; ++i) o[i] = 0.0f;
+    if (n < 0 || n > (int64_t)max_blocks_per_seq * kv_bs) return -1;
+    if (n == 0) return 0;
+    int nb = (int)((n + ORC_SPARSE_BLOCK - 1) / ORC_SPARSE_BLOCK);
+    int count = 0;
+    if (n <= 2 * ORC_SPARSE_BLOCK || nb <= topk) {
+        for (int j = 0; j < nb; ++j) sel[count++] = j;
+    } else {
+        int8_t cq[128];
+        float qsc[4];
+        orc_quantize_q(q_row, hd, cq, qsc);
+        double *score = (double *)malloc(sizeof(double) * (size_t)nb);
+        char *taken = (char *)calloc((size_t)nb, 1);
+        if (orc_block_importance(b, h / (nq / nkv), nkv, hd, kv_bs, block_table, max_blocks_per_seq, num_blocks,
+                                 n, k_codes, k_step, cq, qsc, scale, score, NULL)) {
+            free(score);
+            free(taken);
+            return -1;
+        }
+        /* k rounds of "the highest importance not taken yet, lowest index on ties" */
+        for (int round = 0; round < topk; ++round) {
+            int arg = -1;
+            for (int j = 0; j < nb; ++j)
+                if (!taken[j] && (arg < 0 || score[j] > score[arg])) arg = j;
+            taken[arg] = 1;
+        }
+        for (int j = 0; j < nb; ++j)
+            if (taken[j]) sel[count++] = j;
+        free(score);
+        free(taken);
+    }
+    if (orc_attend_blocks(b, h, nq, nkv, hd, kv_bs, block_table, max_blocks_per_seq, seq_lens, num_blocks,
+                          k_codes, v_codes, k_step, v_step, q_row, scale, sel, count, o))
+        return -1;
+    return count;
 }
 
 /* Every (b, h).  out: [batch][nq][hd]; sel (optional): [batch][nq][topk]
@@ -617,6 +668,37 @@ int orc_decode_attn_sparse(int batch, int nq, int nkv, int hd, int kv_bs,
         }
         free(s);
         if (rc < 0) {
+#pragma omp atomic write
+            status = -1;
+        }
+    }
+    return status;
+}
+
+/* Attention over a given block set for every (b, h): sel[b][h][0..width)
+ * lists block indices, ended by the first negative entry.  out:
+ * [batch][nq][hd].  Returns 0, or -1 if any row had a bad length, block
+ * index or block id (that row is zeros). */
+int orc_decode_attn_blocks(int batch, int nq, int nkv, int hd, int kv_bs,
+                           const int32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *seq_lens, int num_blocks,
+                           const int8_t *k_codes, const int8_t *v_codes,
+                           const float *k_step, const float *v_step,
+                           const float *q, float scale, const int32_t *sel, int width, float *out,
+                           int nthreads)
+{
+    int status = 0;
+    int64_t rows = (int64_t)batch * nq;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < rows; ++bh) {
+        const int32_t *s = sel + bh * width;
+        int count = 0;
+        while (count < width && s[count] >= 0) ++count;
+        int rc = orc_attend_blocks((int)(bh / nq), (int)(bh % nq), nq, nkv, hd, kv_bs, block_table,
+                                   max_blocks_per_seq, seq_lens, num_blocks, k_codes, v_codes, k_step, v_step,
+                                   q + bh * hd, scale, s, count, out + bh * hd);
+        if (rc) {
 #pragma omp atomic write
             status = -1;
         }

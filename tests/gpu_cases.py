@@ -162,3 +162,82 @@ def assert_rows_close(got, want, what=""):
     assert bad.size == 0, (f"{what}: {bad.size} rows out of tolerance; worst row {bad[np.argmax(err[bad] / tol[bad])]} "
                            f"err {err[bad].max():.3e} tol {tol[bad].min():.3e}")
     return float((err / tol).max()) if err.size else 0.0
+
+
+# ------------------------------------------------------- block-sparse decisions
+# The GPU evaluates each probe row's score s = (sum_b P_b * qscale_b) *
+# kscale * scale in fp32, scaled by the positive constant fl(scale * log2 e) /
+# scale common to every block (the block ranking is unchanged by it): the
+# four block terms x_b = fl(P_b * qscale_b) (P_b exact), two pairwise sums and
+# their sum, then one product with fl(kscale * sc).  Each block term passes
+# through at most three roundings on its way into the sum and the result
+# through two more, so |gpu / const - s| <= ~5 u * sum_b |x_b| * kscale *
+# scale with u = 2^-24; a block's importance (a max over probe rows) moves
+# by at most the largest such bound over its rows.  SPARSE_EPS_U = 8 gives
+# margin over 5.
+SPARSE_EPS_U = 8 * 2.0 ** -24
+
+
+def check_sparse_selection(sel, scores, mags, lens, topk):
+    """The GPU's kept blocks sel [batch, nq, topk] (ascending, -1 after the
+    last) against the oracle's exact importances (scores, mags from
+    oracle.sparse_scores): for every (b, h) with more than topk blocks,
+    exactly topk distinct blocks of the sequence are kept, every kept block's
+    importance plus its bound is at least every dropped block's importance
+    minus its bound, and no dropped block ties exactly with a kept block of
+    higher index; otherwise every block is kept.  Returns the number of rows
+    whose kept set differs from the exact top-k (decisions inside the fp32
+    rounding band)."""
+    sel = np.asarray(sel)
+    batch, nq, _ = sel.shape
+    inside_band = 0
+    for b in range(batch):
+        n = int(lens[b])
+        nb = (n + 31) // 32
+        for h in range(nq):
+            row = [int(x) for x in sel[b, h]]
+            k = sum(1 for x in row if x >= 0)
+            assert all(x >= 0 for x in row[:k]) and all(x == -1 for x in row[k:]), (b, h, row)
+            kept = row[:k]
+            if nb <= topk:
+                assert kept == list(range(nb)), (b, h, kept)
+                continue
+            assert k == topk and kept == sorted(set(kept)) and 0 <= kept[0] and kept[-1] < nb, (b, h, kept)
+            d = scores[b, h, :nb]
+            e = SPARSE_EPS_U * mags[b, h, :nb] + 1e-300
+            mask = np.zeros(nb, bool)
+            mask[kept] = True
+            lo = np.min(d[mask] + e[mask])
+            hi = np.max(d[~mask] - e[~mask])
+            assert lo >= hi, f"(b {b}, h {h}): kept block scored {lo} below dropped {hi}"
+            for i in np.nonzero(~mask)[0]:
+                assert not np.any(mask[i + 1:] & (d[i + 1:] == d[i])), f"(b {b}, h {h}): tie not to block {i}"
+            exact = sorted(sorted(range(nb), key=lambda j: (-d[j], j))[:topk])
+            inside_band += kept != exact
+    return inside_band
+
+
+def run_sparse_and_check(dc, q, nq, scale, topk, what=""):
+    """Block-sparse decode on the GPU cache dc (q: host [batch, nq, 128]
+    fp32), checked against the oracle over the codes read back: the kept
+    blocks by check_sparse_selection, the outputs within the decode
+    tolerance of the oracle's attention over the GPU's kept blocks.  Returns
+    (worst err/tol, rows decided inside the rounding band)."""
+    t = torch()
+    m = q8()
+    batch = len(dc.lens)
+    qd = q if isinstance(q, t.Tensor) else t.from_numpy(np.ascontiguousarray(q, np.float32)).cuda()
+    qh = qd.cpu().numpy()
+    out = t.full((batch, nq, 128), float("nan"), dtype=t.float32, device="cuda")
+    sel = t.full((batch, nq, topk), -7, dtype=t.int32, device="cuda")
+    ws = t.empty(m.decode_attn_sparse_workspace_bytes(dc.layer, dc.batch, nq, topk), dtype=t.uint8, device="cuda")
+    ws.fill_(0xCD)
+    m.decode_attn_sparse(dc.layer, dc.batch, nq, qd, scale, out, ws, topk=topk, selected=sel, dev_status=dc.status)
+    assert dc.status_word() == 0
+    host = dc.host()
+    got_sel = sel.cpu().numpy()
+    scores, mags = oracle.sparse_scores(host, qh, nq, scale)
+    band = check_sparse_selection(got_sel, scores, mags, dc.lens, topk)
+    want = oracle.decode_attn_blocks(host, qh, nq, scale, got_sel)
+    worst = assert_rows_close(out.cpu().numpy(), want, f"sparse topk={topk} {what}")
+    return worst, band

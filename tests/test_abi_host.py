@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 4
+    assert q8.abi_version() == 5
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
@@ -152,13 +152,34 @@ def test_workspace_size_grows_with_parts_and_heads(q8):
 
 def test_hook_validation(q8):
     lib = q8.lib()
-    assert lib.q8_quantize_q(FAKE, 4, 64, FAKE, FAKE, None) == -2
-    assert lib.q8_quantize_q(FAKE, -1, 128, FAKE, FAKE, None) == -1
-    assert lib.q8_quantize_q(FAKE, 0, 128, FAKE, FAKE, None) == 0
-    assert lib.q8_quantize_q(FAKE + 4, 1, 128, FAKE, FAKE, None) == -1
+    assert lib.q8_quantize_q(FAKE, 4, 64, 0, FAKE, FAKE, None) == -2
+    assert lib.q8_quantize_q(FAKE, -1, 128, 0, FAKE, FAKE, None) == -1
+    assert lib.q8_quantize_q(FAKE, 0, 128, 0, FAKE, FAKE, None) == 0
+    assert lib.q8_quantize_q(FAKE + 4, 1, 128, 0, FAKE, FAKE, None) == -1
+    assert lib.q8_quantize_q(FAKE, 1, 128, 2, FAKE, FAKE, None) == -1      # unknown path
+    assert lib.q8_quantize_q(FAKE, 1, 128, -1, FAKE, FAKE, None) == -1
     L, B = layer(q8), batch(q8)
-    assert lib.q8_qk_block_partials(ctypes.byref(L.c()), ctypes.byref(B.c()), 12, FAKE, FAKE, None, None) == -1
-    assert lib.q8_qk_block_partials(ctypes.byref(L.c()), ctypes.byref(B.c()), 16, FAKE, 0, None, None) == -1
+
+    def partials(nq=16, q=FAKE, p=FAKE, qc=None, qs=None):
+        return lib.q8_qk_block_partials(ctypes.byref(L.c()), ctypes.byref(B.c()), nq, q, p, qc, qs, None, None)
+
+    assert partials(nq=12) == -1
+    assert partials(p=0) == -1
+    assert partials(p=FAKE + 4) == -1          # the partials are written 16 bytes at a time
+    assert partials(qc=FAKE) == -1             # codes and scales: both or neither
+    assert partials(qs=FAKE) == -1
+    assert partials(qc=FAKE + 8, qs=FAKE) == -1
+
+
+def test_stream_read_validation(q8):
+    lib = q8.lib()
+    assert lib.q8_stream_read(FAKE, 0, 256, 1, FAKE, None) == 0          # nothing to read
+    assert lib.q8_stream_read(FAKE, 100, 256, 1, FAKE, None) == -1       # not a multiple of 16
+    assert lib.q8_stream_read(FAKE + 8, 1024, 256, 1, FAKE, None) == -1  # misaligned buffer
+    assert lib.q8_stream_read(FAKE, 1024, 0, 1, FAKE, None) == -1
+    assert lib.q8_stream_read(FAKE, 1024, 70000, 1, FAKE, None) == -1
+    assert lib.q8_stream_read(FAKE, 1024, 256, 2, FAKE, None) == -1
+    assert lib.q8_stream_read(FAKE, 1024, 256, 1, None, None) == -1
 
 
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
@@ -226,3 +247,70 @@ def test_decode_step_validation(q8):
     assert call_step(q8, L, B, status=FAKE + 2) == -1
     assert call_step(q8, L, B, ws=0) == -3
     assert call_step(q8, L, B, ws_bytes=q8.decode_attn_workspace_bytes(L, B, 16, 0) - 1) == -3
+
+
+# ------------------------------------------------- Python binding argument checks
+def _cpu_layer(q8, **over):
+    import torch
+    nb, bs, nkv = 4, 32, 2
+    d = dict(k_codes=torch.zeros((nb, bs, nkv * 128), dtype=torch.int8),
+             v_codes=torch.zeros((nb, bs, nkv * 128), dtype=torch.int8),
+             k_scale=torch.zeros((nb, nkv, bs)), v_scale=torch.zeros((nb, nkv, bs)),
+             nkv_heads=nkv, kv_bs=bs, num_blocks=nb)
+    d.update(over)
+    return q8.KVLayer(**d)
+
+
+def test_binding_rejects_wrong_tensors_before_any_call(q8):
+    # The checks run before the library is called; CPU tensors reach the
+    # dtype, contiguity and size checks (the device check comes last).
+    import torch
+    with pytest.raises(ValueError, match="dtype"):
+        q8.make_batch(torch.zeros((2, 3), dtype=torch.int64), torch.zeros(2, dtype=torch.int32), 10)
+    with pytest.raises(ValueError, match="dtype"):
+        q8.make_batch(torch.zeros((2, 3), dtype=torch.int32), torch.zeros(2, dtype=torch.int64), 10)
+    with pytest.raises(ValueError, match="contiguous"):
+        q8.make_batch(torch.zeros((3, 2), dtype=torch.int32).t(), torch.zeros(2, dtype=torch.int32), 10)
+    with pytest.raises(ValueError, match="elements"):
+        q8.make_batch(torch.zeros((2, 3), dtype=torch.int32), torch.zeros(3, dtype=torch.int32), 10)
+    with pytest.raises(ValueError, match="GPU"):
+        q8.make_batch(torch.zeros((2, 3), dtype=torch.int32), torch.zeros(2, dtype=torch.int32), 10)
+    # layer tensors: wrong dtype, wrong size
+    B = q8.Batch(torch.zeros((2, 3), dtype=torch.int32), torch.zeros(2, dtype=torch.int32), 2, 3, 10)
+    q = torch.zeros((2, 4, 128))
+    out = torch.zeros((2, 4, 128))
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="layer.k_codes: dtype"):
+        q8.decode_attn(_cpu_layer(q8, k_codes=torch.zeros((4, 32, 256))), B, 4, q, 0.1, out, ws)
+    with pytest.raises(ValueError, match="layer.v_scale: .*elements"):
+        q8.decode_attn(_cpu_layer(q8, v_scale=torch.zeros((4, 2, 16))), B, 4, q, 0.1, out, ws)
+    with pytest.raises(ValueError, match="torch tensor"):
+        q8.decode_attn(_cpu_layer(q8, k_codes=FAKE), B, 4, q, 0.1, out, ws)
+    # q / out: half precision, strided, too small
+    L = _cpu_layer(q8)
+    with pytest.raises(ValueError, match="GPU"):
+        q8.decode_attn(L, B, 4, q, 0.1, out, ws)      # everything right but on the CPU
+    with pytest.raises(ValueError, match="q: dtype"):
+        q8.decode_attn(L, B, 4, q.half(), 0.1, out, ws)
+    with pytest.raises(ValueError, match="out: must be contiguous"):
+        q8.decode_attn(L, B, 4, q, 0.1, torch.zeros((2, 128, 4)).transpose(1, 2), ws)
+    with pytest.raises(ValueError, match="out: .*elements"):
+        q8.decode_attn(L, B, 4, q, 0.1, out[:1], ws)
+    with pytest.raises(ValueError, match="dev_status: dtype"):
+        q8.decode_attn(L, B, 4, q, 0.1, out, ws, dev_status=torch.zeros(1, dtype=torch.int64))
+    # append: int64 token indices, short K rows
+    seq = torch.zeros(3, dtype=torch.int32)
+    kn = torch.zeros((3, 2, 128))
+    with pytest.raises(ValueError, match="tok_pos: dtype"):
+        q8.kv_append(L, B, seq, seq.long(), kn, kn)
+    with pytest.raises(ValueError, match="v_new: .*elements"):
+        q8.kv_append(L, B, seq, seq, kn, kn[:2])
+    # decode step: short new rows; sparse: short selection; prefill: q_start size
+    with pytest.raises(ValueError, match="k_new: .*elements"):
+        q8.decode_step(L, B, 4, kn[:1], kn, q, 0.1, out, ws)
+    with pytest.raises(ValueError, match="selected: .*elements"):
+        q8.decode_attn_sparse(L, B, 4, q, 0.1, out, ws, topk=8, selected=torch.zeros(8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="q_start: .*elements"):
+        q8.prefill_attn(L, B, 4, torch.zeros(2, dtype=torch.int32), 1, q, 0.1, out)
+    with pytest.raises(ValueError, match="partials: .*elements"):
+        q8.qk_block_partials(L, B, 4, q, torch.zeros(10, dtype=torch.int32))

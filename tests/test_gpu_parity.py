@@ -91,42 +91,62 @@ def test_append_one_token_per_step_matches_bulk():
 
 
 # ------------------------------------------------------- Q quantizer (a2)
-def test_quantize_q_bit_exact():
+@pytest.mark.parametrize("path,rows", [(0, 1000), (1, 1000), (1, 1001), (1, 1003)])
+def test_quantize_q_bit_exact(path, rows):
+    # both of the decode's device routines: two lanes per 32-block (path 0)
+    # and one lane per 32-block in the matrix-core A layout (path 1, four
+    # rows per wave; 1001 and 1003 rows end in a partial group)
     t = torch()
-    say("[quantize_q]")
+    say(f"[quantize_q] path {path}, {rows} rows")
     rng = np.random.default_rng(21)
-    q = rng.standard_normal((1000, 128)).astype(np.float32)
+    q = rng.standard_normal((rows, 128)).astype(np.float32)
     q[::5, 32:64] *= 1e-8                     # guarded blocks
     q[3] = 0.0
     q[7, :] = 0.25
     q[7, :12] = [127.0, -126.9, 2.5, -2.5, 0.99, -0.99, 126.99, -127.0, 64.7, -64.7, 0.0, 1.0]
     q[11] = (3 * rng.standard_t(3, 128)).astype(np.float32)
+    q[13, :32] = np.float32(1e-6)             # both sides of the 1e-6 guard
+    q[13, 32:64] = np.nextafter(np.float32(1e-6), np.float32(0))
     qd = t.from_numpy(q).cuda()
-    codes = t.empty((1000, 128), dtype=t.int8, device="cuda")
-    qsc = t.empty((1000, 4), dtype=t.float32, device="cuda")
-    q8().quantize_q(qd, codes, qsc)
+    codes = t.full((rows + 4, 128), 99, dtype=t.int8, device="cuda")
+    qsc = t.full((rows + 4, 4), -1.0, dtype=t.float32, device="cuda")
+    q8().quantize_q(qd, codes, qsc, path=path)
     want_c, want_s = oracle.quantize_q(q)
-    np.testing.assert_array_equal(codes.cpu().numpy(), want_c)
-    np.testing.assert_array_equal(qsc.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    np.testing.assert_array_equal(codes[:rows].cpu().numpy(), want_c)
+    np.testing.assert_array_equal(qsc[:rows].cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    assert bool((codes[rows:] == 99).all()) and bool((qsc[rows:] == -1.0).all())   # nothing past the rows
 
 
 # ------------------------------------------------------ int32 partials (a4)
-@pytest.mark.parametrize("nq,nkv,kv_bs", [(1, 1, 32), (16, 8, 32), (32, 8, 8), (8, 1, 64)])
+@pytest.mark.parametrize("nq,nkv,kv_bs", [(1, 1, 32), (16, 8, 32), (32, 8, 8), (8, 1, 64),
+                                          (32, 8, 32), (32, 8, 64), (32, 8, 256), (8, 2, 16), (8, 2, 32)])
 def test_qk_block_partials_bit_exact(nq, nkv, kv_bs):
+    # The decode's own routine for the shape: at four query heads per KV head
+    # with kv_bs >= 32 the matrix-core path (one-lane-per-block query codes,
+    # v_mfma_i32_16x16x64_i8), else sdot4; codes, scales and every partial
+    # bit-exact, partials past a sequence's end 0.
     t = torch()
     say(f"[partials] nq={nq} nkv={nkv} kv_bs={kv_bs}")
-    lens = np.array([70, 1, 0, 33, 128, 5], np.int32)
-    k, v = dense_kv(lens, nkv, seed=nq + kv_bs)
-    rng = np.random.default_rng(nq)
+    lens = np.array([70, 1, 0, 33, 128, 5, 300], np.int32)
+    k, v = dense_kv(lens, nkv, seed=nq + kv_bs, dist="student3x3" if nq == 32 else "normal")
+    rng = np.random.default_rng(nq + kv_bs)
     q = rng.standard_normal((len(lens), nq, 128)).astype(np.float32)
+    q[1, 0, 32:64] = np.float32(1e-6)
+    q[1, 0, 64:96] = 0.0
     dc = DeviceCache(lens, nkv, kv_bs, seed=4)
     dc.append_dense(k, v)
     out = t.full((len(lens), nq, dc.max_seq_len, 4), -7, dtype=t.int32, device="cuda")
-    q8().qk_block_partials(dc.layer, dc.batch, nq, t.from_numpy(q).cuda(), out, dev_status=dc.status)
+    qc = t.full((len(lens), nq, 128), 99, dtype=t.int8, device="cuda")
+    qs = t.full((len(lens), nq, 4), -1.0, dtype=t.float32, device="cuda")
+    q8().qk_block_partials(dc.layer, dc.batch, nq, t.from_numpy(q).cuda(), out, qcodes=qc, qscale=qs,
+                           dev_status=dc.status)
     assert dc.status_word() == 0
     ref_cache = oracle.build_cache(k, v, lens, dc.table, dc.num_blocks, kv_bs)
     want = oracle.qk_partials(ref_cache, q, nq, dc.max_seq_len)
     np.testing.assert_array_equal(out.cpu().numpy(), want)
+    want_c, want_s = oracle.quantize_q(q)
+    np.testing.assert_array_equal(qc.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(qs.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
 
 
 # ----------------------------------------------------------- decode (a3-a9)

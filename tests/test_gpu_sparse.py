@@ -1,16 +1,20 @@
 """GPU parity of the block-sparse decode ("why long context must be sparse"
 §1-§2) against the oracle, through the C ABI.
 
-The kept blocks are a decision taken in floating point on both sides with
-the same fp32 score formula, so they must be identical; the outputs must
-satisfy max |gpu - oracle| <= 2e-5 * max |oracle| + 1e-6 per (b, h) row.
+The kept blocks are a decision the GPU takes on fp32 scores; they are judged
+against the oracle's importances (the page's score of each probe row, in
+double): every kept block must score at least every dropped one within the
+fp32 evaluation bound, exact ties going to the lower block
+(gpu_cases.check_sparse_selection).  The outputs must satisfy max |gpu -
+oracle| <= 2e-5 * max |oracle| + 1e-6 per (b, h) row against the oracle's
+attention over the blocks the GPU kept.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gpu_cases import DeviceCache, assert_rows_close, dense_kv, q8, say, torch
+from gpu_cases import (SPARSE_EPS_U, DeviceCache, dense_kv, q8, run_sparse_and_check, say, torch)
 
 pytestmark = pytest.mark.gpu
 SCALE = float(workloads.softmax_scale(128))
@@ -18,28 +22,15 @@ EDGE_LENS = [0, 1, 31, 32, 33, 64, 65, 100, 255, 256, 257, 700, 1024, 1025, 2049
 
 
 def _sparse_case(lens, nq, nkv, kv_bs, topk, seed, dist="normal", q=None):
-    t = torch()
-    m = q8()
     lens = np.asarray(lens, np.int32)
     k, v = dense_kv(lens, nkv, seed=seed, dist=dist)
     if q is None:
         q = np.random.default_rng([seed, 7]).standard_normal((len(lens), nq, 128)).astype(np.float32)
     dc = DeviceCache(lens, nkv, kv_bs, seed=seed)
     dc.append_dense(k, v)
-    want, want_sel = oracle.decode_attn_sparse(oracle.build_cache(k, v, lens, dc.table, dc.num_blocks, kv_bs),
-                                               q, nq, SCALE, topk)
-    out = t.full((len(lens), nq, 128), float("nan"), dtype=t.float32, device="cuda")
-    sel = t.full((len(lens), nq, topk), -7, dtype=t.int32, device="cuda")
-    ws = t.empty(m.decode_attn_sparse_workspace_bytes(dc.layer, dc.batch, nq, topk), dtype=t.uint8, device="cuda")
-    ws.fill_(0xCD)
-    m.decode_attn_sparse(dc.layer, dc.batch, nq, t.from_numpy(q).cuda(), SCALE, out, ws, topk=topk, selected=sel,
-                         dev_status=dc.status)
-    assert dc.status_word() == 0
-    got_sel = sel.cpu().numpy()
-    mism = np.argwhere(np.any(got_sel != want_sel, axis=-1))
-    assert mism.size == 0, f"selection differs at (b, h) {mism[:4].tolist()}: {got_sel[tuple(mism[0])]} vs " \
-                           f"{want_sel[tuple(mism[0])]}"
-    return assert_rows_close(out.cpu().numpy(), want, f"sparse topk={topk}")
+    worst, band = run_sparse_and_check(dc, q, nq, SCALE, topk)
+    say(f"  rows decided inside the fp32 band: {band}")
+    return worst
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
@@ -115,12 +106,12 @@ def test_sparse_graph_replays_match_eager():
 
 
 @pytest.mark.parametrize("group,kv_bs", [(1, 32), (2, 8), (4, 32), (8, 16)])
-def test_sparse_probe_scores_bitwise(group, kv_bs):
+def test_sparse_probe_scores_within_fp32_bound(group, kv_bs):
     # White-box: the probe's block scores sit at the start of the workspace,
-    # [batch * nq][max_nb] fp32 (max_nb = ceil(max_seq_len / 32)).  Wherever a
-    # sequence has more than k blocks they must equal the oracle's probe
-    # scores bit for bit (the matrix-core dot products are exact integers and
-    # the fp32 steps follow the same order).
+    # [batch * nq][max_nb] fp32 (max_nb = ceil(max_seq_len / 32)), in the log2
+    # domain (times fl(scale * log2 e) / scale).  Wherever a sequence has more
+    # than k blocks they must lie within the fp32 evaluation bound of the
+    # oracle's double importances.
     say(f"[sparse] probe scores group={group} kv_bs={kv_bs}")
     t, m = torch(), q8()
     nkv, nq, topk = 2, 2 * group, 4
@@ -129,7 +120,7 @@ def test_sparse_probe_scores_bitwise(group, kv_bs):
     q = np.random.default_rng([600 + group, 7]).standard_normal((len(lens), nq, 128)).astype(np.float32)
     dc = DeviceCache(lens, nkv, kv_bs, seed=600 + group)
     dc.append_dense(k, v)
-    want = oracle.sparse_scores(oracle.build_cache(k, v, lens, dc.table, dc.num_blocks, kv_bs), q, nq, SCALE)
+    want, mag = oracle.sparse_scores(dc.host(), q, nq, SCALE)
     out = t.empty((len(lens), nq, 128), dtype=t.float32, device="cuda")
     ws = t.empty(m.decode_attn_sparse_workspace_bytes(dc.layer, dc.batch, nq, topk), dtype=t.uint8, device="cuda")
     ws.fill_(0xCD)
@@ -138,12 +129,14 @@ def test_sparse_probe_scores_bitwise(group, kv_bs):
     assert dc.status_word() == 0
     max_nb = want.shape[-1]
     got = ws[:len(lens) * nq * max_nb * 4].cpu().numpy().view(np.float32).reshape(len(lens), nq, max_nb)
+    sigma = float(np.float32(float(np.float32(SCALE)) * 1.4426950408889634)) / float(np.float32(SCALE))
     checked = 0
     for b, n in enumerate(lens):
         nb = (int(n) + 31) // 32
         if nb <= topk:
             continue
-        np.testing.assert_array_equal(got[b, :, :nb].view(np.uint32), want[b, :, :nb].view(np.uint32),
-                                      err_msg=f"sequence {b}")
+        err = np.abs(got[b, :, :nb].astype(np.float64) / sigma - want[b, :, :nb])
+        bound = SPARSE_EPS_U * mag[b, :, :nb] + 1e-300
+        assert np.all(err <= bound), f"sequence {b}: worst err/bound {(err / bound).max():.3f}"
         checked += nq * nb
     assert checked > 0

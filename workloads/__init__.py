@@ -147,6 +147,46 @@ def kv_host(w: Workload, lens: np.ndarray, layer: int = 0):
 
 
 # ------------------------------------------------------------ torch (device) --
+GUARD_ROWS_PER_DRAW = 4   # rows per torch draw pinned to the two sides of the 1e-6 guard
+
+
+def _guard_rows_torch(x, gen):
+    """In GUARD_ROWS_PER_DRAW rows of x ([..., head_dim] fp32, rows are
+    (token, head)) picked with generator `gen`: rescale the row so that its
+    max-abs is exactly 1e-6 (even picks) or the float just below it (odd
+    picks) -- the two sides of the 1e-6 guard."""
+    import torch
+    rows = x.view(-1, x.shape[-1])
+    if rows.shape[0] == 0:
+        return x
+    idx = torch.randint(0, rows.shape[0], (GUARD_ROWS_PER_DRAW,), generator=gen, device=x.device)
+    two = torch.tensor([1e-6, float(np.nextafter(np.float32(1e-6), np.float32(0)))], dtype=torch.float32,
+                       device=x.device)
+    t = two[torch.arange(GUARD_ROWS_PER_DRAW, device=x.device) % 2][:, None]      # fp32 targets
+    sel = rows[idx].double()
+    amax = sel.abs().amax(-1, keepdim=True)
+    scaled = torch.where(amax > 0, sel * (t.double() / torch.where(amax > 0, amax, 1.0)), 0.5 * t.double())
+    out = torch.maximum(torch.minimum(scaled.float(), t), -t)
+    j = scaled.abs().argmax(-1, keepdim=True)
+    sign = torch.where(scaled.gather(1, j) >= 0, 1.0, -1.0).float()
+    out.scatter_(1, j, sign * t)          # one element exactly +-target: max-abs == target
+    rows[idx] = out
+    return x
+
+
+def _student3x3_torch(shape, gen, device):
+    """3 * t(nu=3) (z / sqrt(chi2_3 / 3), times 3) with the stress rows: 1% of
+    rows scaled by 1e-7, 0.2% exactly zero, and guard-boundary rows."""
+    import torch
+    z = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    e = torch.randn((3,) + tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    x = 3.0 * z / torch.sqrt((e * e).sum(0) / 3.0)
+    u = torch.rand(shape[:-1], generator=gen, device=device)
+    x = torch.where((u < 0.01)[..., None], x * 1e-7, x)
+    x = torch.where(((u >= 0.01) & (u < 0.012))[..., None], torch.zeros_like(x), x)
+    return _guard_rows_torch(x.contiguous(), gen)
+
+
 def kv_chunk_torch(w: Workload, layer: int, b: int, chunk: int, which: int, device):
     """One chunk of CHUNK_TOKENS tokens of K (which=0) or V (which=1) for
     sequence b, [CHUNK_TOKENS, nkv, head_dim] fp32, drawn with torch's
@@ -159,13 +199,7 @@ def kv_chunk_torch(w: Workload, layer: int, b: int, chunk: int, which: int, devi
     shape = (CHUNK_TOKENS, w.nkv, w.head_dim)
     if w.dist == "normal":
         return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    e = torch.randn((3,) + shape, generator=g, device=device, dtype=torch.float32)
-    x = 3.0 * z / torch.sqrt((e * e).sum(0) / 3.0)
-    u = torch.rand(shape[:-1], generator=g, device=device)
-    x = torch.where((u < 0.01)[..., None], x * 1e-7, x)
-    x = torch.where(((u >= 0.01) & (u < 0.012))[..., None], torch.zeros_like(x), x)
-    return x
+    return _student3x3_torch(shape, g, device)
 
 
 def kv_pool_torch(w: Workload, n: int, gen, device):
@@ -176,13 +210,7 @@ def kv_pool_torch(w: Workload, n: int, gen, device):
     shape = (n, w.nkv, w.head_dim)
     if w.dist == "normal":
         return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
-    z = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
-    e = torch.randn((3,) + shape, generator=gen, device=device, dtype=torch.float32)
-    x = 3.0 * z / torch.sqrt((e * e).sum(0) / 3.0)
-    u = torch.rand(shape[:-1], generator=gen, device=device)
-    x = torch.where((u < 0.01)[..., None], x * 1e-7, x)
-    x = torch.where(((u >= 0.01) & (u < 0.012))[..., None], torch.zeros_like(x), x)
-    return x
+    return _student3x3_torch(shape, gen, device)
 
 
 def kv_range_torch(w: Workload, layer: int, b: int, t0: int, t1: int, which: int, device):
