@@ -85,6 +85,10 @@ def _load():
     for fn in (lib.q8_decode_step, lib.q8_decode_step_partial):
         fn.argtypes = [LP, BP, I32, P, P, P, F, P, I32, P, SZ, P, P]
         fn.restype = I32
+    lib.q8_decode_step_static.argtypes = [LP, BP, I32, P, P, P, F, P, I32, P, P]
+    lib.q8_decode_step_static.restype = I32
+    lib.q8_decode_step_static_scratch_bytes.argtypes = []
+    lib.q8_decode_step_static_scratch_bytes.restype = SZ
     lib.q8_prefill_attn.argtypes = [LP, BP, I32, P, I32, I32, P, F, P, P, P]
     lib.q8_prefill_attn.restype = I32
     lib.q8_quantize_q.argtypes = [P, I32, I32, I32, P, P, P]
@@ -381,6 +385,25 @@ def decode_step_partial(layer, batch, nq_heads, k_new, v_new, q, scale, out, wor
     with the same arguments completes it."""
     _step("q8_decode_step_partial", layer, batch, nq_heads, k_new, v_new, q, scale, out, workspace, nparts,
           dev_status, stream)
+
+
+def decode_step_static(layer, batch, nq_heads, k_new, v_new, q, scale, out, nparts=0, dev_status=None,
+                       stream=None):
+    """q8_decode_step_static: q8_decode_step without a workspace (the
+    library's own device scratch; nothing allocated)."""
+    import torch
+    row = layer.nkv_heads * layer.head_dim
+    args = _q_out(_common(layer, batch, dev_status), batch, nq_heads, q, out, layer.head_dim)
+    (args.need(k_new, "k_new", torch.float32, batch.batch * row)
+         .need(v_new, "v_new", torch.float32, batch.batch * row).done())
+    st = _load().q8_decode_step_static(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, _ptr(k_new),
+                                       _ptr(v_new), _ptr(q), float(scale), _ptr(out), int(nparts),
+                                       _ptr(dev_status), _stream(stream))
+    _check(st, "q8_decode_step_static")
+
+
+def decode_step_static_scratch_bytes() -> int:
+    return int(_load().q8_decode_step_static_scratch_bytes())
 
 
 def prefill_attn(layer, batch, nq_heads, q_start, max_new, q, scale, out, dev_status=None, stream=None):

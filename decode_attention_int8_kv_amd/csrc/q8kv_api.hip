@@ -183,6 +183,32 @@ q8_status q8_decode_step(const q8_kv_layer *layer, const q8_batch *batch, int32_
                                 dev_status, stream);
 }
 
+q8_status q8_decode_step_static(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                const float *k_new, const float *v_new, const float *q, float scale, float *out,
+                                int32_t nparts, int32_t *dev_status, void *stream)
+{
+    q8_status s;
+    if ((s = check_layer(layer)) != Q8_OK) return s;
+    if ((s = check_batch(batch, layer)) != Q8_OK) return s;
+    if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return Q8_EINVAL;
+    if (!k_new || !v_new || !aligned(k_new, 8) || !aligned(v_new, 8)) return Q8_EINVAL;
+    if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
+    if (nparts < 0) return Q8_EINVAL;
+    const q8kv::DecodePlan plan = q8kv::make_plan(*layer, *batch, nq_heads, nparts);
+    if (plan.bytes > q8kv::static_scratch_bytes()) return Q8_EWORKSPACE;
+    void *ws = nullptr;
+    hipError_t e = q8kv::static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "q8_decode_step_static (scratch address)");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    e = q8kv::launch_decode_partial(*layer, *batch, nq_heads, q, scale, out, plan, ws, dev_status, st, k_new, v_new);
+    if (e != hipSuccess) return hip_fail(e, "q8_decode_step_static");
+    e = q8kv::launch_decode_merge(*layer, *batch, nq_heads, out, plan, ws, st);
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_step_static");
+}
+
+size_t q8_decode_step_static_scratch_bytes(void) { return q8kv::static_scratch_bytes(); }
+
 q8_status q8_decode_attn_f32_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
                                      const float *q, float scale, float *out, int32_t nparts,
                                      void *workspace, size_t workspace_bytes, int32_t *dev_status,

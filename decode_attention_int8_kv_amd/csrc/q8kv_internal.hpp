@@ -60,6 +60,11 @@ hipError_t launch_qk_partials(const q8_kv_layer &layer, const q8_batch &batch, i
                               int32_t *partials, int8_t *qcodes, float *qscale, int32_t *dev_status,
                               hipStream_t stream);
 
+// The library's own device scratch (q8kv_static.hip): its size, and this
+// device's address of it.
+size_t static_scratch_bytes();
+hipError_t static_scratch(void **ptr);
+
 hipError_t launch_stream_read(const void *buf, size_t bytes, int workgroups, int nontemporal, uint32_t *sink,
                               hipStream_t stream);
 

@@ -190,6 +190,26 @@ q8_status q8_decode_step_partial(const q8_kv_layer *layer, const q8_batch *batch
                                  float *out, int32_t nparts, void *workspace, size_t workspace_bytes,
                                  int32_t *dev_status, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * q8_decode_step -- same kernels, results bit-identical for the same nparts
+ * -- with no workspace argument.  The partial records live in a device
+ * array of the library (q8_decode_step_static_scratch_bytes() = 16 MiB on
+ * every GPU it runs on, held until the process ends); nothing is allocated,
+ * freed or initialized by the call, and the array needs no clearing (every
+ * byte a call reads it has written first in the same call).  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress);
+ * make one call outside graph capture before capturing.  Every call on one
+ * GPU uses the same array: calls that may overlap on a GPU (different
+ * streams without ordering) race and must be ordered by the caller.
+ * Q8_EWORKSPACE if the plan for this shape and nparts needs more than the
+ * array holds (with nparts = 0 on an MI355X: up to 32 query heads); other
+ * errors as q8_decode_step. */
+size_t q8_decode_step_static_scratch_bytes(void);
+q8_status q8_decode_step_static(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                                const float *k_new, const float *v_new, const float *q, float scale, float *out,
+                                int32_t nparts, int32_t *dev_status, void *stream);
+
 /* Exact decode attention over the layer's fp32 mirror ("9-3" §1: scores of
  * the raw fp32 q and K, max-subtracted softmax, weighted raw V), for every
  * sequence b and query head h:
