@@ -45,9 +45,10 @@ def _run(cmd, verbose):
         print(err)
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = OUT, link_extra=()) -> str:
     """Compile every source to an object (in parallel, with its own flags),
-    then link the shared library."""
+    then link the shared library (at `out`; `extra` and `link_extra` are added
+    to every compile and to the link)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -60,9 +61,9 @@ def build(verbose: bool = False, extra=()) -> str:
         with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
             for fut in [ex.submit(_run, c, verbose) for c in cmds]:
                 fut.result()
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp", *objs], verbose)
-    os.replace(OUT + ".tmp", OUT)
-    return OUT
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, "-o", out + ".tmp", *objs], verbose)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
