@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--append", choices=("fused", "separate"), default="fused",
                     help="--path q8: the new tokens appended inside the decode's partial kernel "
                          "(q8_decode_step) or by q8_kv_append before it")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="decode without a step plan: every layer's partial kernel makes the cut itself "
+                         "(default: q8_decode_plan once per step, read by every layer)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -171,10 +174,12 @@ SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n405
 
 
 def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8", topk=32,
-            fused=True):
+            fused=True, planned=True):
     """One workload: fill `layers` cache pools, then time whole decode steps
     (graph replay unless eager) and, in an eager pass with HIP events on the
-    library's stream, each kernel.  Returns a dict of figures."""
+    library's stream, each kernel.  With `planned` (the q8 and f32 paths), a
+    step starts with q8_decode_plan and every layer's decode reads the plan;
+    the plan kernel is inside the timed step.  Returns a dict of figures."""
     lens = workloads.seq_lens(w)
     kv_bs = w.kv_bs
     B, nq, nkv, hd = w.batch, w.nq, w.nkv, w.head_dim
@@ -230,9 +235,18 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     if path == "sparse":
         ws_bytes = max(ws_bytes, q8.decode_attn_sparse_workspace_bytes(pools[0], batch, nq, topk))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    planned = planned and path in ("q8", "f32")
+    plan = None
+    if planned:
+        plan = torch.empty(q8.decode_plan_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
+    batch_p = batch.with_plan(plan)   # the decode calls' batch (the appends and the plan itself ignore it)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set during fill"
     setup_s = time.perf_counter() - t_setup
+
+    def make_plan():
+        if planned:
+            q8.decode_plan(pools[0], batch, nq, plan, nparts=nparts, dev_status=status)
 
     def append(li):
         if not fused:
@@ -240,16 +254,17 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
 
     def attend(li):
         if fused:
-            q8.decode_step_partial(pools[li], batch, nq, new_k[li], new_v[li], qs[li], scale, outs[li], ws,
+            q8.decode_step_partial(pools[li], batch_p, nq, new_k[li], new_v[li], qs[li], scale, outs[li], ws,
                                    nparts=nparts, dev_status=status)
         else:
-            partial(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            partial(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
 
     def step_plain():
+        make_plan()
         for li in range(layers):
             append(li)
             attend(li)
-            merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
 
     # ---- timed region 1: whole steps (one HIP graph per step unless eager)
     graph = None
@@ -279,6 +294,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     ev_steps = max(2, min(steps, 5))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ev_steps * layers)]
     for s_ in range(ev_steps + 1):
+        make_plan()
         for li in range(layers):
             e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
             if e: e[0].record(stream)
@@ -286,7 +302,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
             if e: e[1].record(stream)
             attend(li)
             if e: e[2].record(stream)
-            merge(pools[li], batch, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
             if e: e[3].record(stream)
     torch.cuda.synchronize()
     t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
@@ -296,12 +312,12 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
 
     attn_b, app_b = algorithmic_bytes(w, lens, kv_bs, path, topk)
     ms_per_step = wall * 1e3 / steps
-    del pools, outs, qs, new_k, new_v, ws
+    del pools, outs, qs, new_k, new_v, ws, plan
     return {
         "lens": lens, "table": table, "nblocks": nblocks, "nparts": nparts, "layers": layers,
         "ms_per_step": ms_per_step, "attn_bytes": attn_b, "append_bytes": app_b,
         "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
-        "graph": graph is not None, "setup_s": setup_s, "fused": fused,
+        "graph": graph is not None, "setup_s": setup_s, "fused": fused, "planned": planned,
     }
 
 
@@ -521,7 +537,7 @@ def main():
     layers = args.layers or w.layers
     fused = args.append == "fused" and args.path == "q8"
     m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk,
-                fused)
+                fused, not args.no_plan)
     lens = m["lens"]
     B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
     attn_b, app_b = m["attn_bytes"], m["append_bytes"]
@@ -557,7 +573,7 @@ def main():
                 continue
             ws_ = workloads.WORKLOADS[name]
             sweep.append(sweep_entry(ws_, measure(torch, q8, dev, ws_, ws_.layers, 10, 2, 0, args.eager,
-                                                  fused=fused)))
+                                                  fused=fused, planned=not args.no_plan)))
             torch.cuda.empty_cache()
             print(f"[sweep] {name} done", file=sys.stderr, flush=True)
 
@@ -572,7 +588,7 @@ def main():
         "vs_baseline": None, "dtype": "fp32" if args.path == "f32" else "int8/fp32", "data": "synthetic",
         "config": {
             "workload": w.name, "path": args.path, "topk": args.topk if args.path == "sparse" else None,
-            "append": "fused" if fused else "separate",
+            "append": "fused" if fused else "separate", "step_plan": m["planned"],
             "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -27,6 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq8kv.so")
 
 Q8_OK, Q8_EINVAL, Q8_EUNSUPPORTED, Q8_EWORKSPACE, Q8_EHIP = 0, -1, -2, -3, -4
+DEV_BAD_PLAN = 0x8
 QPATH_VALU, QPATH_MFMA = 0, 1   # q8_quantize_q: two lanes or one lane per 32-block
 DEV_BAD_SEQ_LEN, DEV_BAD_BLOCK_ID, DEV_BAD_TOKEN = 0x1, 0x2, 0x4
 HEAD_DIM = 128
@@ -52,7 +53,7 @@ class _Layer(ctypes.Structure):
 class _Batch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("plan", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +74,10 @@ def _load():
     lib.q8_decode_attn_auto_parts.restype = I32
     lib.q8_decode_attn_workspace_bytes.argtypes = [LP, BP, I32, I32]
     lib.q8_decode_attn_workspace_bytes.restype = SZ
+    lib.q8_decode_plan_bytes.argtypes = [LP, BP, I32, I32]
+    lib.q8_decode_plan_bytes.restype = SZ
+    lib.q8_decode_plan.argtypes = [LP, BP, I32, I32, P, SZ, P, P]
+    lib.q8_decode_plan.restype = I32
     for name in ("q8_decode_attn", "q8_decode_attn_partial", "q8_decode_attn_merge", "q8_decode_attn_f32",
                  "q8_decode_attn_f32_partial"):
         fn = getattr(lib, name)
@@ -181,6 +186,10 @@ class _Args:
         self.need(batch.block_table, "batch.block_table", torch.int32, batch.batch * batch.max_blocks_per_seq,
                   exact=True)
         self.need(batch.seq_lens, "batch.seq_lens", torch.int32, batch.batch, exact=True)
+        if batch.plan is not None:
+            if not isinstance(batch.plan, torch.Tensor):
+                raise ValueError("batch.plan: expected a torch tensor")
+            self.need(batch.plan, "batch.plan", batch.plan.dtype, 0)
         return self
 
     def done(self):
@@ -228,16 +237,22 @@ class KVLayer:
 @dataclasses.dataclass
 class Batch:
     """Per-step batch metadata: block_table int32 [batch, max_blocks_per_seq],
-    seq_lens int32 [batch] (device tensors), and host-side max_seq_len."""
+    seq_lens int32 [batch] (device tensors), host-side max_seq_len, and an
+    optional step plan (a device tensor filled by decode_plan)."""
     block_table: object
     seq_lens: object
     batch: int
     max_blocks_per_seq: int
     max_seq_len: int
+    plan: object = None
 
     def c(self) -> _Batch:
         return _Batch(self.batch, self.max_blocks_per_seq, self.max_seq_len,
-                      _ptr(self.block_table), _ptr(self.seq_lens))
+                      _ptr(self.block_table), _ptr(self.seq_lens), _ptr(self.plan))
+
+    def with_plan(self, plan) -> "Batch":
+        """The same batch with a step plan (or None)."""
+        return dataclasses.replace(self, plan=plan)
 
 
 def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head_dim: int = HEAD_DIM,
@@ -295,6 +310,20 @@ def kv_append(layer: KVLayer, batch: Batch, tok_seq, tok_pos, k_new, v_new, dev_
     st = _load().q8_kv_append(ctypes.byref(layer.c()), ctypes.byref(batch.c()), n, _ptr(tok_seq),
                               _ptr(tok_pos), _ptr(k_new), _ptr(v_new), _ptr(dev_status), _stream(stream))
     _check(st, "q8_kv_append")
+
+
+def decode_plan_bytes(layer: KVLayer, batch: Batch, nq_heads: int, nparts: int = 0) -> int:
+    return int(_load().q8_decode_plan_bytes(ctypes.byref(layer.c()), ctypes.byref(batch.c()), nq_heads, nparts))
+
+
+def decode_plan(layer: KVLayer, batch: Batch, nq_heads: int, plan, nparts: int = 0, dev_status=None, stream=None):
+    """q8_decode_plan: fill `plan` (a GPU tensor of at least decode_plan_bytes
+    bytes) with the step's cut; use it through batch.with_plan(plan) in every
+    layer's decode call of the step."""
+    _common(layer, batch.with_plan(None), dev_status).need(plan, "plan", None, 0).done()
+    st = _load().q8_decode_plan(ctypes.byref(layer.c()), ctypes.byref(batch.with_plan(None).c()), nq_heads,
+                                int(nparts), _ptr(plan), _nbytes(plan), _ptr(dev_status), _stream(stream))
+    _check(st, "q8_decode_plan")
 
 
 def decode_attn_auto_parts(layer: KVLayer, batch: Batch, nq_heads: int) -> int:

@@ -52,6 +52,7 @@ q8_status check_batch(const q8_batch *b, const q8_kv_layer *l)
         return Q8_EUNSUPPORTED;
     if (!b->block_table || !b->seq_lens) return Q8_EINVAL;
     if (!aligned(b->block_table, 4) || !aligned(b->seq_lens, 4)) return Q8_EINVAL;
+    if (b->plan && !aligned(b->plan, 64)) return Q8_EINVAL;
     return Q8_OK;
 }
 
@@ -115,6 +116,32 @@ size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *
         check_heads(layer, nq_heads) != Q8_OK || nparts < 0)
         return 0;
     return q8kv::make_plan(*layer, *batch, nq_heads, nparts).bytes;
+}
+
+size_t q8_decode_plan_bytes(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, int32_t nparts)
+{
+    if (check_layer(layer) != Q8_OK || check_batch(batch, layer) != Q8_OK ||
+        check_heads(layer, nq_heads) != Q8_OK || nparts < 0)
+        return 0;
+    return q8kv::step_plan_bytes(*batch, q8kv::make_plan(*layer, *batch, nq_heads, nparts).nparts);
+}
+
+q8_status q8_decode_plan(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, int32_t nparts,
+                         void *plan, size_t plan_bytes, int32_t *dev_status, void *stream)
+{
+    q8_status s;
+    if ((s = check_layer(layer)) != Q8_OK) return s;
+    if ((s = check_batch(batch, layer)) != Q8_OK) return s;
+    if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
+    if (nparts < 0) return Q8_EINVAL;
+    if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
+    const q8kv::DecodePlan pl = q8kv::make_plan(*layer, *batch, nq_heads, nparts);
+    const size_t need = q8kv::step_plan_bytes(*batch, pl.nparts);
+    if (need > (size_t)0x7fffffff * 4) return Q8_EUNSUPPORTED;   // word offsets stay in int32 range
+    if (!plan || !aligned(plan, 64) || plan_bytes < need) return Q8_EWORKSPACE;
+    hipError_t e = q8kv::launch_step_plan(*layer, *batch, nq_heads, pl, plan, dev_status,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_decode_plan");
 }
 
 q8_status q8_decode_attn_partial(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,

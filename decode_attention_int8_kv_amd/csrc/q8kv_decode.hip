@@ -38,7 +38,7 @@ template <int G> struct PipeDepth { static constexpr int value = 2; };
 template <int G, bool Big>
 __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
                                              int lt0, int lt1, int n, bool whole, int part,
-                                             int slot)
+                                             int slot, const TileBlocks *first)
 {
     const int c = lane & 7, tslot = lane >> 3;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
@@ -60,7 +60,10 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
 #pragma unroll
         for (int i = 0; i < 4; ++i) qv[g][i] = qp[i];
     }
-    fetch_blocks_ahead<Big>(bt, log2bs, lt0 * kTile, ne, bl[0]);
+    if (first)   // the block ids a step plan holds for this piece
+        planned_first_blocks<Big>(*first, lt0 * kTile, ne, bl[0]);
+    else
+        fetch_blocks_ahead<Big>(bt, log2bs, lt0 * kTile, ne, bl[0]);
     const LaneOffsets lo = lane_offsets(p.cache, kh, lane);
 #pragma unroll
     for (int d = 0; d < D - 1; ++d) {
@@ -285,7 +288,7 @@ __device__ __forceinline__ float row16_sum(float v)
 }
 
 __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, int kh, int lane, int lt0, int lt1,
-                                                int n, bool whole, int part, int slot)
+                                                int n, bool whole, int part, int slot, const TileBlocks *first)
 {
     constexpr int G = 4;
     const int c = lane & 7, tslot = lane >> 3;
@@ -306,7 +309,10 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
     // tile's loads before the quantization (as in attend_piece)
     float4 qv[8];
     mf_load_query(p.q + ((size_t)b * p.nq + kh * G) * kHeadDim, lane, qv);
-    fetch_blocks_ahead<true>(bt, log2bs, lt0 * kTile, ne, bl[0]);
+    if (first)
+        planned_first_blocks<true>(*first, lt0 * kTile, ne, bl[0]);
+    else
+        fetch_blocks_ahead<true>(bt, log2bs, lt0 * kTile, ne, bl[0]);
     load_tile_mf(p.cache, bl[0], lo, lane, lt0 * kTile, ne, p.dev_status, t[0]);
     fetch_blocks_ahead<true>(bt, log2bs, (lt0 + 1) * kTile, ne, bl[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -448,13 +454,15 @@ template <int G, bool Big>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
     extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
-    walk_ranges(p, lds_batch, lds_batch + p.batch + 1, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
-        // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
-        if constexpr (G == 4 && Big)
-            attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
-        else
-            attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
-    });
+    walk_ranges(p, lds_batch, lds_batch + p.batch + 1,
+                [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
+                    const TileBlocks *first) {
+                    // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
+                    if constexpr (G == 4 && Big)
+                        attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first);
+                    else
+                        attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first);
+                });
 }
 
 // ---------------------------------------------------------------- merge ----
@@ -657,12 +665,13 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
     p.q = q;
     p.out = out;
     char *ws = static_cast<char *>(workspace);
-    p.ws_prefix = reinterpret_cast<int32_t *>(ws + plan.off_prefix);
-    p.ws_ms = reinterpret_cast<float2 *>(ws + plan.off_ms);
-    p.ws_acc = reinterpret_cast<float *>(ws + plan.off_acc);
+    p.ws_prefix = ws ? reinterpret_cast<int32_t *>(ws + plan.off_prefix) : nullptr;
+    p.ws_ms = ws ? reinterpret_cast<float2 *>(ws + plan.off_ms) : nullptr;
+    p.ws_acc = ws ? reinterpret_cast<float *>(ws + plan.off_acc) : nullptr;
     p.dev_status = dev_status;
     p.k_new = nullptr;
     p.v_new = nullptr;
+    p.plan = static_cast<const int32_t *>(batch.plan);
     p.batch = batch.batch;
     p.nq = nq;
     p.max_blocks_per_seq = batch.max_blocks_per_seq;
@@ -696,7 +705,9 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
     if (plan.nparts <= 1) return hipSuccess;
     MergeParams p;
     char *ws = static_cast<char *>(workspace);
-    p.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan.off_prefix);
+    // the cut-axis prefix: written by the partial kernel, or the step plan's
+    p.ws_prefix = batch.plan ? static_cast<const int32_t *>(batch.plan) + step_plan_layout(batch.batch, plan.nparts).pref
+                             : reinterpret_cast<const int32_t *>(ws + plan.off_prefix);
     p.ws_ms = reinterpret_cast<const float2 *>(ws + plan.off_ms);
     p.ws_acc = reinterpret_cast<const float *>(ws + plan.off_acc);
     p.out = out;

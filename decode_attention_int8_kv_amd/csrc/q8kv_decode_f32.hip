@@ -201,9 +201,9 @@ template <int G>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_f32_partial_kernel(DecodeParams p)
 {
     __shared__ int pref[kMaxBatch + 1];
-    walk_ranges(p, pref, nullptr, [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot) {
-        attend_piece_f32<G>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
-    });
+    walk_ranges(p, pref, nullptr,
+                [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
+                    const TileBlocks *) { attend_piece_f32<G>(p, b, kh, lane, lt0, lt1, n, whole, part, slot); });
 }
 
 hipError_t launch_decode_partial_f32(const q8_kv_layer &layer, const q8_batch &batch, int nq,

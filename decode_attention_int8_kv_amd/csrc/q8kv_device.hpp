@@ -29,6 +29,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int32_t kDevBadSeqLen = 0x1;
 constexpr int32_t kDevBadBlockId = 0x2;
 constexpr int32_t kDevBadToken = 0x4;
+constexpr int32_t kDevBadPlan = 0x8;
 
 // ------------------------------------------------------------------ quantizers
 // K/V row: given the row's max-abs a, the stored step d and the reciprocal r.

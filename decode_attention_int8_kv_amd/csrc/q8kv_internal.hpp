@@ -65,6 +65,11 @@ hipError_t launch_qk_partials(const q8_kv_layer &layer, const q8_batch &batch, i
 size_t static_scratch_bytes();
 hipError_t static_scratch(void **ptr);
 
+// The step plan (q8kv_stepplan.hip).
+size_t step_plan_bytes(const q8_batch &batch, int nparts);
+hipError_t launch_step_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, const DecodePlan &plan,
+                            void *plan_buf, int32_t *dev_status, hipStream_t stream);
+
 hipError_t launch_stream_read(const void *buf, size_t bytes, int workgroups, int nontemporal, uint32_t *sink,
                               hipStream_t stream);
 

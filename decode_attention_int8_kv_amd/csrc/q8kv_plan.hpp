@@ -2,6 +2,7 @@
 // shape, workspace layout), shared by the decode kernels and the C-ABI layer.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 
 #include "q8kv.h"
@@ -26,5 +27,50 @@ constexpr int kPieceCost = 2;
 
 DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq);
+
+// ------------------------------------------------------------ step plan --
+// The cut of one decode step, made once by q8_decode_plan (one small kernel)
+// and read by every layer's partial kernel instead of scanning the lengths
+// and looking up block ids at the start of every workgroup.  It lists, per
+// range, its pieces in walk order; per piece the sequence, its tile interval
+// and length, whether it is the whole sequence, its record slot, whether it
+// holds the sequence's newest token, and the block ids a piece starts with.
+// int32 words, in order:
+//   header  [kPlanHeader]                       (kPlanMagic, batch, nparts, ...)
+//   pref    [batch + 1]   cut-axis prefix (the merge kernel reads it)
+//   range   [nparts + 1]  first piece of every range (prefix of piece counts)
+//   empty   [batch]       the sequences of length 0 (their output rows are zeroed)
+//   pieces  [(nparts + batch) * kPieceInts], 64-byte aligned
+// A range holds at most one piece more than the sequences that start inside
+// it, so nparts + batch pieces always suffice.
+constexpr int32_t kPlanMagic = 0x51384B50;   // tag of a finished plan
+constexpr int kPlanHeader = 16;
+constexpr int kPieceInts = 16;
+enum PlanHeader { kPhMagic, kPhBatch, kPhParts, kPhKvBsLog2, kPhPieceCost, kPhTotal, kPhEmpty, kPhMaxSeqLen };
+enum PieceField {
+    kPfSeq,        // sequence b
+    kPfT0,         // first tile (of the sequence's 32-token tiles)
+    kPfT1,         // one past the last tile
+    kPfLen,        // the sequence's length n (>= 1)
+    kPfFlags,      // bit 0: whole sequence; bit 1: record slot 1; bit 2: holds position n - 1
+    kPfAppendBlk,  // block id of position n - 1
+    kPfFirstBlk    // 4 words: block ids of the first tile's 8-token sub-tiles (tokens clamped to n - 1)
+};
+constexpr int kPieceWhole = 1, kPieceSlot1 = 2, kPieceAppend = 4;
+
+struct StepPlanLayout {
+    size_t pref, range, empty, pieces, words;   // word offsets and total
+};
+
+__host__ __device__ inline StepPlanLayout step_plan_layout(int batch, int nparts)
+{
+    StepPlanLayout l;
+    l.pref = kPlanHeader;
+    l.range = l.pref + (size_t)batch + 1;
+    l.empty = l.range + (size_t)nparts + 1;
+    l.pieces = (l.empty + (size_t)batch + 15) / 16 * 16;
+    l.words = l.pieces + ((size_t)nparts + batch) * kPieceInts;
+    return l;
+}
 
 }  // namespace q8kv

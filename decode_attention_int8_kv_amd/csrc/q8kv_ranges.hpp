@@ -36,6 +36,8 @@ struct DecodeParams {
     // sequence, [batch][nkv][128] fp32, quantized into the cache first
     const float *k_new;
     const float *v_new;
+    // the step plan (q8kv_plan.hpp), or null: the cut is then made here
+    const int32_t *plan;
     int32_t batch;
     int32_t nq;
     int32_t max_blocks_per_seq;
@@ -119,18 +121,120 @@ __device__ inline void build_prefix(const DecodeParams &p, int *pref, int *lens,
     __syncthreads();
 }
 
+// The first tile's block ids of a planned piece, masked like
+// fetch_blocks_ahead: sub-tiles at or past ne (the piece's end) get -1.
+template <bool BigBlocks>
+__device__ __forceinline__ void planned_first_blocks(const TileBlocks &raw, int t0, int ne, TileBlocks &b)
+{
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) b.id[kk] = (t0 + kSub * kk < ne) ? raw.id[BigBlocks ? 0 : kk] : -1;
+}
+
+// walk_ranges over a step plan: the same pieces, appends and zeroed rows,
+// read from the plan (every piece's fields with scalar loads) instead of
+// found by a length scan and lookups.  A plan made for another batch size,
+// partition count, block size, cost or length bound sets Q8_DEV_BAD_PLAN
+// and the workgroup does nothing.
+template <class Attend>
+__device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend)
+{
+    const_i32 *pl = (const_i32 *)p.plan;
+    const int part = blockIdx.x / p.head_groups;
+    const int hg = blockIdx.x - part * p.head_groups;
+    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int kh = hg * (int)(blockDim.x >> 6) + wave;
+    const bool ok = pl[kPhMagic] == kPlanMagic && pl[kPhBatch] == p.batch && pl[kPhParts] == p.nparts &&
+                    pl[kPhKvBsLog2] == p.cache.kv_bs_log2 && pl[kPhPieceCost] == p.piece_cost &&
+                    pl[kPhMaxSeqLen] == p.max_seq_len;
+    if (!ok) {
+        if (threadIdx.x == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadPlan);
+        return;
+    }
+    const StepPlanLayout L = step_plan_layout(p.batch, p.nparts);
+    const int r0 = pl[L.range + part], r1 = pl[L.range + part + 1];
+    const int bs_mask = (1 << p.cache.kv_bs_log2) - 1;
+
+    if (p.k_new && kh < p.cache.nkv) {
+        // fused append: the newest token of every sequence whose last tile
+        // lies in this range, before any tile is loaded (ordering as in
+        // walk_ranges); four rows' loads in flight at a time
+        bool wrote = false;
+        for (int j0 = r0; j0 < r1; j0 += 4) {
+            float2 k[4], v[4];
+            int seq[4], blk[4], row[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u;
+                seq[u] = -1;
+                if (j < r1) {
+                    const_i32 *pc = pl + L.pieces + (size_t)j * kPieceInts;
+                    if (pc[kPfFlags] & kPieceAppend) {
+                        seq[u] = pc[kPfSeq];
+                        blk[u] = pc[kPfAppendBlk];
+                        row[u] = (pc[kPfLen] - 1) & bs_mask;
+                        const size_t src = ((size_t)seq[u] * p.cache.nkv + kh) * kHeadDim + 2 * lane;
+                        k[u] = *reinterpret_cast<const float2 *>(p.k_new + src);
+                        v[u] = *reinterpret_cast<const float2 *>(p.v_new + src);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (seq[u] < 0) continue;
+                if ((unsigned)blk[u] >= (unsigned)p.cache.num_blocks) {
+                    if (lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
+                    continue;
+                }
+                append_row_vals(const_cast<int8_t *>(p.cache.k_codes), const_cast<int8_t *>(p.cache.v_codes),
+                                const_cast<float *>(p.cache.k_scale), const_cast<float *>(p.cache.v_scale),
+                                const_cast<float *>(p.k_f32), const_cast<float *>(p.v_f32), p.cache.nkv,
+                                p.cache.kv_bs_log2, blk[u], row[u], kh, k[u], v[u], lane);
+                wrote = true;
+            }
+        }
+        if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+
+    if (kh < p.cache.nkv) {
+        for (int j = r0; j < r1; ++j) {
+            const_i32 *pc = pl + L.pieces + (size_t)j * kPieceInts;
+            const int b = pc[kPfSeq], lt0 = pc[kPfT0], lt1 = pc[kPfT1], n = pc[kPfLen], fl = pc[kPfFlags];
+            TileBlocks first;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) first.id[kk] = pc[kPfFirstBlk + kk];
+            attend(b, kh, lane, lt0, lt1, n, (fl & kPieceWhole) != 0, part, (fl & kPieceSlot1) ? 1 : 0, &first);
+        }
+    }
+
+    if (hg == 0) {
+        const int n_empty = pl[kPhEmpty];
+        for (int e = part; e < n_empty; e += p.nparts) {
+            const int b = pl[L.empty + e];
+            float4 *o = reinterpret_cast<float4 *>(p.out + (size_t)b * p.nq * kHeadDim);
+            for (int i = threadIdx.x; i < p.nq * (kHeadDim / 4); i += blockDim.x)
+                o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
 // The whole job of one workgroup of a partial kernel: range blockIdx.x /
 // head_groups, KV heads hg * waves + wave.  attend(b, kh, lane, lt0, lt1, n,
-// whole, part, slot) runs one wave over tiles [lt0, lt1) of sequence b
+// whole, part, slot, first) runs one wave over tiles [lt0, lt1) of sequence b
 // (length n); `whole` says the piece is the whole sequence, else its state
 // goes to slot `slot` (0: first piece of the range, 1: later) of record
-// `part`.  Afterwards the output rows of empty sequences whose tile position
-// falls in this range are zeroed (the last range also takes those at the
-// very end).  With p.k_new set, `lens` (LDS, batch entries) is required and
-// the range's new tokens are appended first.
+// `part`; `first` holds the raw block ids of the first tile (from a step
+// plan), or is null.  Afterwards the output rows of empty sequences whose
+// tile position falls in this range are zeroed (the last range also takes
+// those at the very end).  With p.k_new set, `lens` (LDS, batch entries) is
+// required and the range's new tokens are appended first.  With a step plan
+// (p.plan) the same work is read from it (walk_plan).
 template <class Attend>
 __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
 {
+    if (p.plan) {
+        walk_plan(p, attend);
+        return;
+    }
     const int part = blockIdx.x / p.head_groups;
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -221,7 +325,7 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
                 const int slot = (start >= a0) ? 0 : 1;
                 int n = lens ? lens[b] : p.seq_lens[b];
                 n = uniform(n);
-                attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot);
+                attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot, static_cast<const TileBlocks *>(nullptr));
             }
             x = x1;
         }

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 5
+#define Q8KV_ABI_VERSION 6
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -72,6 +72,7 @@ typedef enum q8_status {
 #define Q8_DEV_BAD_SEQ_LEN  0x1  /* seq_lens[b] < 0 or > max_seq_len */
 #define Q8_DEV_BAD_BLOCK_ID 0x2  /* block_table entry outside [0, num_blocks) */
 #define Q8_DEV_BAD_TOKEN    0x4  /* append: tok_seq outside [0, batch) or tok_pos outside [0, seq_lens[seq]) */
+#define Q8_DEV_BAD_PLAN     0x8  /* decode: batch->plan was not made by q8_decode_plan for this call's shape */
 
 /* One layer's physical block pool (pointers to device memory).
  * Alignment: k_codes and v_codes 16 bytes, k_scale and v_scale 4 bytes.
@@ -95,13 +96,24 @@ typedef struct q8_kv_layer {
 
 /* Per-step batch metadata, shared by all layers.  batch, max_blocks_per_seq
  * and max_seq_len are host values; the arrays are device memory.
- * max_seq_len must not exceed max_blocks_per_seq * kv_bs. */
+ * max_seq_len must not exceed max_blocks_per_seq * kv_bs.
+ * plan: NULL, or a step plan made by q8_decode_plan for these arrays (with
+ * their current contents), the decode call's nq_heads and nparts and the
+ * layer's nkv_heads and kv_bs (64-byte aligned device memory).  The decode
+ * entry points (q8_decode_attn and its phases, q8_decode_step and its
+ * partial, q8_decode_step_static, q8_decode_attn_f32 and its partial) then
+ * read the cut from it instead of making it in every workgroup, with
+ * bit-identical results; the other entry points ignore it.  A plan made for
+ * another batch size, partition count, kv_bs or max_seq_len is detected on
+ * the device (Q8_DEV_BAD_PLAN, no output written); one made before the
+ * arrays changed is not -- make a new plan whenever they change. */
 typedef struct q8_batch {
     int32_t batch;
     int32_t max_blocks_per_seq;
     int32_t max_seq_len;
     const int32_t *block_table;
     const int32_t *seq_lens;
+    const void *plan;
 } q8_batch;
 
 /* kv_quantize_per_head append ("9-3" §2; stored layout "9-2" §2 segment 2).
@@ -131,6 +143,23 @@ int32_t q8_decode_attn_auto_parts(const q8_kv_layer *layer, const q8_batch *batc
  * (nparts = 0: the automatic count above).  Returns 0 on invalid arguments. */
 size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *batch,
                                       int32_t nq_heads, int32_t nparts);
+
+/* The step plan (see q8_batch.plan): the cut of the batch into ranges and
+ * pieces that every decode call of this step would otherwise make at the
+ * start of every workgroup -- the length prefix, the ranges' pieces and the
+ * block ids each piece starts with -- made once by one small kernel and
+ * shared by all layers of the step.  The plan depends on the batch arrays'
+ * contents, nq_heads (through the automatic partition count), nparts, and
+ * the layer's nkv_heads and kv_bs; make it after the step's seq_lens and
+ * block_table are final (after the appends' positions are counted in
+ * seq_lens) and before the first decode of the step.  plan: device memory of
+ * at least q8_decode_plan_bytes() bytes, 64-byte aligned; batch->plan is
+ * ignored.  Bad lengths set Q8_DEV_BAD_SEQ_LEN here (the planned decode calls
+ * then treat those sequences as empty without reporting again). */
+size_t q8_decode_plan_bytes(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
+                            int32_t nparts);
+q8_status q8_decode_plan(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, int32_t nparts,
+                         void *plan, size_t plan_bytes, int32_t *dev_status, void *stream);
 
 /* Decode attention ("9-2" §2, all three segments) for every sequence b and
  * query head h of the batch:

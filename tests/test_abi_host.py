@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 5
+    assert q8.abi_version() == 6
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
