@@ -266,9 +266,14 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
             attend(li)
             merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
 
-    # ---- timed region 1: whole steps (one HIP graph per step unless eager)
+    # ---- timed region 1: whole steps (HIP graph replays unless eager).  A
+    # graph holds graph_steps consecutive steps: a step of one small layer
+    # takes less GPU time than the host needs to launch a replay, and one
+    # step per replay would time the host instead of the GPU.
     graph = None
+    copies = 1
     if not eager:
+        copies = graph_steps(layers)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -276,7 +281,8 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step_plain()
+            for _ in range(copies):
+                step_plain()
     run = graph.replay if graph is not None else step_plain
     for _ in range(warmup):
         run()
@@ -286,6 +292,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    steps_timed = steps * copies
     assert int(status.item()) == 0, "device status set during timing"
 
     # ---- timed region 2: eager launches with HIP events around each kernel on
@@ -311,14 +318,19 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     t_layer = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
 
     attn_b, app_b = algorithmic_bytes(w, lens, kv_bs, path, topk)
-    ms_per_step = wall * 1e3 / steps
+    ms_per_step = wall * 1e3 / steps_timed
     del pools, outs, qs, new_k, new_v, ws, plan
     return {
         "lens": lens, "table": table, "nblocks": nblocks, "nparts": nparts, "layers": layers,
         "ms_per_step": ms_per_step, "attn_bytes": attn_b, "append_bytes": app_b,
         "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
-        "graph": graph is not None, "setup_s": setup_s, "fused": fused, "planned": planned,
+        "graph": graph is not None, "graph_steps": copies, "setup_s": setup_s, "fused": fused, "planned": planned,
     }
+
+
+def graph_steps(layers: int) -> int:
+    """Decode steps per captured graph: 32 layer-steps or more per replay."""
+    return max(1, 32 // max(1, layers))
 
 
 def prefill_flops(w: workloads.Workload, lens: np.ndarray) -> int:
@@ -597,7 +609,7 @@ def main():
             "us_append": None if fused else round(float(np.median(t_append)), 2),
             "us_decode_partial": round(float(np.median(t_partial)), 2),
             "us_decode_merge": round(float(np.median(t_merge)), 2),
-            "graph": m["graph"],
+            "graph": m["graph"], "graph_steps": m["graph_steps"],
             "bytes_per_layer_step": int(attn_b + app_b), "setup_s": round(m["setup_s"], 1),
             "sweep": sweep,
         },

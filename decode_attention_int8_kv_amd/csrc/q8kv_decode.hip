@@ -478,18 +478,65 @@ struct MergeParams {
 };
 
 constexpr int kMaxMergeWaves = 16;
-constexpr int kMergeBatch = 16;  // pieces whose loads a wave has in flight together
+constexpr int kMergeBatch = 16;  // loads a lane has in flight together
 
-// One workgroup per (sequence, query head) whose tiles span several ranges:
-// combines the pieces' (M, S, acc) with the online-softmax rescale rule
-// ("9-2" §2 segment 2 applied to whole partial states).  Wave w takes pieces
-// w, w + waves, ..., kMergeBatch of them per round with all their loads
-// issued before any is used, and keeps its own running max; the waves' states
-// are then combined in wave order, so the result does not depend on timing.
-// A batch with fewer pieces than waves * kMergeBatch costs one round trip.
+// Two partial states combined with the rescale rule of "9-2" §2 segment 2
+// (M the larger, S and the accumulators rescaled to it and summed).  Every
+// operation is symmetric in the two states (max, and sums of two products --
+// IEEE addition is commutative), so the two lanes of a swapped pair end with
+// the same bits whichever of them holds which state.
+__device__ __forceinline__ void merge_states(float &m, float &s, float &ax, float &ay, float m2, float s2, float ax2,
+                                             float ay2)
+{
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;   // neither has seen a token
+    const float f1 = __builtin_amdgcn_exp2f(m - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);   // 0 for -inf
+    m = mn;
+    s = s * f1 + s2 * f2;
+    ax = ax * f1 + ax2 * f2;
+    ay = ay * f1 + ay2 * f2;
+}
+
+// The state of the lane 16 (Rows = 16) or 32 (Rows = 32) lanes away,
+// combined into this lane's: a v_permlane16/32_swap of a register with itself
+// leaves this lane's value and the partner's in the two results.
+template <int Rows>
+__device__ __forceinline__ void merge_across_rows(float &m, float &s, float &ax, float &ay)
+{
+    auto swap = [](float v) {
+        if constexpr (Rows == 16)
+            return __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        else
+            return __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    };
+    const auto rm = swap(m), rs = swap(s), rx = swap(ax), ry = swap(ay);
+    float m0 = __uint_as_float(rm[0]), s0 = __uint_as_float(rs[0]);
+    float x0 = __uint_as_float(rx[0]), y0 = __uint_as_float(ry[0]);
+    merge_states(m0, s0, x0, y0, __uint_as_float(rm[1]), __uint_as_float(rs[1]), __uint_as_float(rx[1]),
+                 __uint_as_float(ry[1]));
+    m = m0;
+    s = s0;
+    ax = x0;
+    ay = y0;
+}
+
+// Merge of the pieces of every (sequence, query head) whose tiles span
+// several ranges: their (M, S, acc) records combined with the online-softmax
+// rescale rule ("9-2" §2 segment 2 applied to whole partial states) and one
+// division.  Workgroup = (sequence b, query head h, slice of 128 / Slices
+// dims); a lane holds two dims of one piece, so a wave reads 64 / (64 /
+// Slices) = Slices pieces per load and each lane has kMergeBatch loads in
+// flight.  Wave w takes piece groups w, w + waves, ...; the lanes' states are
+// combined across the lane rows (permlane swaps) and then the waves' states
+// in wave order through LDS, so the result does not depend on timing.  More
+// slices give small batches more workgroups (a batch-1 128K sequence has 32
+// (sequence, head) rows of 256 pieces each).
+template <int Slices>
 __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(MergeParams p)
 {
-    const int b = blockIdx.x / p.nq, h = blockIdx.x - b * p.nq;
+    constexpr int kLanesPerPiece = 64 / Slices;   // 64, 32, 16
+    const int row = blockIdx.x / Slices, sl = blockIdx.x - row * Slices;
+    const int b = row / p.nq, h = row - b * p.nq;
     const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1], total = p.ws_prefix[p.batch];
     if (e0 == a0) return;
     // ranges of the first and the last tile (before the first tile of a
@@ -501,6 +548,8 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
     const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+    const int pg = lane / kLanesPerPiece, dl = lane - pg * kLanesPerPiece;
+    const int dim2 = sl * kLanesPerPiece + dl;   // this lane's float2 of the 64 in a row
     // a range can be empty (and write no record) only when there are more
     // ranges than cut-axis units; otherwise skip the two divisions per
     // record (a range strictly between the first and the last tile's holds
@@ -508,17 +557,18 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     const bool may_be_empty = p.nparts > total;
 
     float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
-    for (int j0 = wave; j0 < np; j0 += kMergeBatch * waves) {
+    const int stride = waves * Slices;   // piece groups per round of one load
+    for (int j0 = wave * Slices + pg; j0 < np; j0 += kMergeBatch * stride) {
         float2 ms[kMergeBatch], av[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
-            const int j = j0 + u * waves, i = i0 + j;
+            const int j = j0 + u * stride, i = i0 + j;
             const bool have = j < np && (!may_be_empty || part_start(i, total, p.nparts) !=
                                                               part_start(i + 1, total, p.nparts));
             if (have) {
                 const size_t r = ((size_t)i * 2 + (j == 0 ? slot0 : 0)) * p.nq + h;
                 ms[u] = p.ws_ms[r];
-                av[u] = reinterpret_cast<const float2 *>(p.ws_acc + r * kHeadDim)[lane];
+                av[u] = reinterpret_cast<const float2 *>(p.ws_acc + r * kHeadDim)[dim2];
             } else {
                 ms[u] = make_float2(-INFINITY, 0.0f);
                 av[u] = make_float2(0.0f, 0.0f);
@@ -541,6 +591,9 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
         }
         m = mn;
     }
+    // the wave's piece groups: rows of 16 lanes (Slices = 4) or halves (2)
+    if constexpr (Slices == 4) merge_across_rows<16>(m, s, ax, ay);
+    if constexpr (Slices >= 2) merge_across_rows<32>(m, s, ax, ay);
 
     __shared__ float sh_m[kMaxMergeWaves], sh_s[kMaxMergeWaves];
     __shared__ float2 sh_a[kMaxMergeWaves][64];
@@ -550,7 +603,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     }
     sh_a[wave][lane] = make_float2(ax, ay);
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0 || pg != 0) return;
     float mx = -INFINITY;
     for (int w = 0; w < waves; ++w) mx = fmaxf(mx, sh_m[w]);
     s = 0.0f;
@@ -565,7 +618,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
         }
     }
     float2 *o = reinterpret_cast<float2 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim);
-    o[lane] = s > 0.0f ? make_float2(ax / s, ay / s) : make_float2(0.0f, 0.0f);
+    o[dim2] = s > 0.0f ? make_float2(ax / s, ay / s) : make_float2(0.0f, 0.0f);
 }
 
 // ----------------------------------------------------------------- host ----
@@ -632,12 +685,16 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
     pl.piece_cost = kPieceCost;
     choose_width(layer.nkv_heads, nq / layer.nkv_heads, pl.waves, pl.head_groups);
-    // merge waves: enough that a sequence cut into about twice the average
-    // number of pieces is read in one round (kMergeBatch pieces per wave);
-    // more pieces take more rounds
+    // merge: few (sequence, query head) rows get each row's dims split over
+    // up to four workgroups, so a small batch still spreads its merge over
+    // many CUs; waves: enough that a sequence cut into about twice the average
+    // number of pieces is read in one round (kMergeBatch loads per lane, a
+    // wave reading `slices` pieces per load); more pieces take more rounds
+    const long long rows = (long long)batch.batch * nq;
+    pl.merge_slices = rows >= 256 ? 1 : rows >= 64 ? 2 : 4;
     const long long per_seq = 2LL * pl.nparts / (batch.batch > 0 ? batch.batch : 1) + 2;
     int mw = 1;
-    while (mw < kMaxMergeWaves && (long long)mw * kMergeBatch < per_seq) mw <<= 1;
+    while (mw < kMaxMergeWaves && (long long)mw * kMergeBatch * pl.merge_slices < per_seq) mw <<= 1;
     pl.merge_waves = mw;
     pl.off_prefix = 0;
     pl.off_ms = align_up(sizeof(int32_t) * ((size_t)batch.batch + 1), 256);
@@ -715,8 +772,13 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
     p.nq = nq;
     p.nparts = plan.nparts;
     p.piece_cost = plan.piece_cost;
-    hipLaunchKernelGGL(q8_attn_merge_kernel, dim3(batch.batch * nq), dim3(plan.merge_waves * 64), 0,
-                       stream, p);
+    const dim3 grid((unsigned)((long long)batch.batch * nq * plan.merge_slices)), block(plan.merge_waves * 64);
+    if (plan.merge_slices == 4)
+        hipLaunchKernelGGL(q8_attn_merge_kernel<4>, grid, block, 0, stream, p);
+    else if (plan.merge_slices == 2)
+        hipLaunchKernelGGL(q8_attn_merge_kernel<2>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(q8_attn_merge_kernel<1>, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct DecodePlan {
     int head_groups;     // workgroups per range (8 KV heads each)
     int waves;           // waves per decode workgroup
     int merge_waves;     // waves per merge workgroup
+    int merge_slices;    // merge workgroups per (sequence, query head): dim slices 1, 2 or 4
     int piece_cost;      // cut-axis units charged per non-empty sequence (see q8kv_ranges.hpp)
     size_t off_prefix, off_ms, off_acc, bytes;
 };
