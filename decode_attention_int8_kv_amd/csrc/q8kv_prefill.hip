@@ -78,10 +78,11 @@ struct PrefillParams {
 // Partial states of the key segments other than the first, per lane:
 // [slot][set][32 accumulators, M, S][lane].
 constexpr int kCombVals = 8 * 4 + 2;
-#ifndef Q8KV_PREFILL_SPLIT
-#define Q8KV_PREFILL_SPLIT 4
-#endif
-constexpr int kPrefillSplit = Q8KV_PREFILL_SPLIT;   // 1, 2 or 4
+// Waves that split one query tile's keys when at least half of them are new
+// (prefill_segments).  The launch halves it (to 2, then 1) only while the
+// grid would exceed 65535 rows of workgroups, i.e. for prompts of more than
+// 2^21 query rows; chunks after a long history use 1.
+constexpr int kPrefillSplit = 4;
 
 // 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
 __device__ __forceinline__ v4s_t codes_to_bf16(uint32_t w)
