@@ -54,7 +54,8 @@ def parse():
                          "(q8_decode_step) or by q8_kv_append before it")
     ap.add_argument("--no-plan", action="store_true",
                     help="decode without a step plan: every layer's partial kernel makes the cut itself "
-                         "(default: q8_decode_plan once per step, read by every layer)")
+                         "(default: q8_decode_plan once per step, read by every layer, when a step has "
+                         "more than one layer)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the other batch x context configurations (reported under config.sweep)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -235,7 +236,9 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     if path == "sparse":
         ws_bytes = max(ws_bytes, q8.decode_attn_sparse_workspace_bytes(pools[0], batch, nq, topk))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    planned = planned and path in ("q8", "f32")
+    # a plan is made once per step and pays for itself over the step's layers;
+    # a one-layer step does not plan
+    planned = planned and path in ("q8", "f32") and layers > 1
     plan = None
     if planned:
         plan = torch.empty(q8.decode_plan_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
