@@ -456,7 +456,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
     extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
     walk_ranges(p, lds_batch, lds_batch + p.batch + 1,
                 [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
-                    const TileBlocks *first) {
+                    const TileBlocks *first) __attribute__((always_inline)) {
                     // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
                     if constexpr (G == 4 && Big)
                         attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first);
