@@ -231,8 +231,11 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     new_v = torch.randn((layers, B, nkv, hd), generator=gen, device=dev)
     qs = torch.randn((layers, B, nq, hd), generator=gen, device=dev)
     outs = torch.empty((layers, B, nq, hd), dtype=torch.float32, device=dev)
+    # the calls get the requested count (0: the library's automatic cut, which
+    # may also choose the workgroup shape); the JSON reports the resolved count
     nparts = nparts_arg or q8.decode_attn_auto_parts(pools[0], batch, nq)
-    ws_bytes = q8.decode_attn_workspace_bytes(pools[0], batch, nq, nparts)
+    call_parts = nparts_arg
+    ws_bytes = q8.decode_attn_workspace_bytes(pools[0], batch, nq, call_parts)
     if path == "sparse":
         ws_bytes = max(ws_bytes, q8.decode_attn_sparse_workspace_bytes(pools[0], batch, nq, topk))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -241,7 +244,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     planned = planned and path in ("q8", "f32") and layers > 1
     plan = None
     if planned:
-        plan = torch.empty(q8.decode_plan_bytes(pools[0], batch, nq, nparts), dtype=torch.uint8, device=dev)
+        plan = torch.empty(q8.decode_plan_bytes(pools[0], batch, nq, call_parts), dtype=torch.uint8, device=dev)
     batch_p = batch.with_plan(plan)   # the decode calls' batch (the appends and the plan itself ignore it)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status set during fill"
@@ -249,7 +252,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
 
     def make_plan():
         if planned:
-            q8.decode_plan(pools[0], batch, nq, plan, nparts=nparts, dev_status=status)
+            q8.decode_plan(pools[0], batch, nq, plan, nparts=call_parts, dev_status=status)
 
     def append(li):
         if not fused:
@@ -258,16 +261,16 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     def attend(li):
         if fused:
             q8.decode_step_partial(pools[li], batch_p, nq, new_k[li], new_v[li], qs[li], scale, outs[li], ws,
-                                   nparts=nparts, dev_status=status)
+                                   nparts=call_parts, dev_status=status)
         else:
-            partial(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            partial(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=call_parts, dev_status=status)
 
     def step_plain():
         make_plan()
         for li in range(layers):
             append(li)
             attend(li)
-            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=call_parts, dev_status=status)
 
     # ---- timed region 1: whole steps (HIP graph replays unless eager).  A
     # graph holds graph_steps consecutive steps: a step of one small layer
@@ -312,7 +315,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
             if e: e[1].record(stream)
             attend(li)
             if e: e[2].record(stream)
-            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=nparts, dev_status=status)
+            merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=call_parts, dev_status=status)
             if e: e[3].record(stream)
     torch.cuda.synchronize()
     t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
