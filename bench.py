@@ -306,7 +306,9 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     stream = torch.cuda.current_stream()
     ev_steps = max(2, min(steps, 5))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ev_steps * layers)]
+    ahead = HostAhead(torch)
     for s_ in range(ev_steps + 1):
+        ahead.start(s_ > 0)
         make_plan()
         for li in range(layers):
             e = ev[(s_ - 1) * layers + li] if s_ > 0 else None   # first pass is a warm-up
@@ -317,6 +319,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
             if e: e[2].record(stream)
             merge(pools[li], batch_p, nq, qs[li], scale, outs[li], ws, nparts=call_parts, dev_status=status)
             if e: e[3].record(stream)
+        ahead.stop()
     torch.cuda.synchronize()
     t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
     t_partial = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
@@ -332,6 +335,37 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
         "graph": graph is not None, "graph_steps": copies, "setup_s": setup_s, "fused": fused, "planned": planned,
     }
+
+
+class HostAhead:
+    """Keeps the GPU on a bounded spin kernel (torch.cuda._sleep) while the
+    host enqueues one event-timed step, so the events around each kernel
+    bracket GPU time only: for a small kernel the host's per-call argument
+    checks and launch take longer than the kernel itself, and without a head
+    start the GPU would wait for the host between two events.  The spin is
+    sized from the host's enqueue time of the untimed first pass."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 2_000_000
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        self.cycles_per_us = n / max(1e-3, e0.elapsed_time(e1) * 1e3)
+        self.host_us = 0.0
+        self.t = 0.0
+
+    def start(self, timed: bool):
+        if timed and self.host_us > 0:
+            self.torch.cuda._sleep(int(min(1.5 * self.host_us + 50.0, 200_000.0) * self.cycles_per_us))
+        self.t = time.perf_counter()
+
+    def stop(self):
+        self.host_us = max(self.host_us, (time.perf_counter() - self.t) * 1e6)
 
 
 def graph_steps(layers: int) -> int:
@@ -425,7 +459,9 @@ def measure_prefill(torch, q8, dev, w, layers, steps, warmup, eager=False):
     stream = torch.cuda.current_stream()
     ev_steps = max(2, min(steps, 5))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_steps * layers)]
+    ahead = HostAhead(torch)
     for s_ in range(ev_steps + 1):
+        ahead.start(s_ > 0)
         for li in range(layers):
             e = ev[(s_ - 1) * layers + li] if s_ > 0 else None
             if e: e[0].record(stream)
@@ -433,6 +469,7 @@ def measure_prefill(torch, q8, dev, w, layers, steps, warmup, eager=False):
             if e: e[1].record(stream)
             q8.prefill_attn(pools[li], batch, nq, q_start, nb, qs[li], scale, outs[li], dev_status=status)
             if e: e[2].record(stream)
+        ahead.stop()
     torch.cuda.synchronize()
     t_append = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
     t_prefill = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
