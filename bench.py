@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--append", choices=("fused", "separate"), default="fused",
                     help="--path q8: the new tokens appended inside the decode's partial kernel "
                          "(q8_decode_step) or by q8_kv_append before it")
+    ap.add_argument("--invariant", action="store_true",
+                    help="decode with the batch-invariant cut (Q8_BATCH_INVARIANT: a sequence's bits independent "
+                         "of the rest of the batch; no step plan)")
     ap.add_argument("--no-plan", action="store_true",
                     help="decode without a step plan: every layer's partial kernel makes the cut itself "
                          "(default: q8_decode_plan once per step, read by every layer, when a step has "
@@ -175,7 +178,7 @@ SWEEP = ("single_head_256", "qwen2b_b1_n506", "qwen2b_b1_n2046", "qwen2b_b1_n405
 
 
 def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False, path="q8", topk=32,
-            fused=True, planned=True):
+            fused=True, planned=True, invariant=False):
     """One workload: fill `layers` cache pools, then time whole decode steps
     (graph replay unless eager) and, in an eager pass with HIP events on the
     library's stream, each kernel.  With `planned` (the q8 and f32 paths), a
@@ -191,7 +194,8 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     table, nblocks = workloads.block_table(lens, kv_bs, w.seed)
     table_t = torch.from_numpy(table).to(dev)
     lens_t = torch.from_numpy(lens).to(dev)
-    batch = q8.make_batch(table_t, lens_t, int(max(1, lens.max())))
+    invariant = invariant and path in ("q8", "f32")
+    batch = q8.make_batch(table_t, lens_t, int(max(1, lens.max())), invariant=invariant)
     pools = [q8.alloc_layer(nblocks, kv_bs, nkv, dev, mirror=(path == "f32")) for _ in range(layers)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     partial = q8.decode_attn_f32_partial if path == "f32" else q8.decode_attn_partial
@@ -241,7 +245,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     # a plan is made once per step and pays for itself over the step's layers;
     # a one-layer step does not plan
-    planned = planned and path in ("q8", "f32") and layers > 1
+    planned = planned and path in ("q8", "f32") and layers > 1 and not invariant
     plan = None
     if planned:
         plan = torch.empty(q8.decode_plan_bytes(pools[0], batch, nq, call_parts), dtype=torch.uint8, device=dev)
@@ -334,6 +338,7 @@ def measure(torch, q8, dev, w, layers, steps, warmup, nparts_arg=0, eager=False,
         "ms_per_step": ms_per_step, "attn_bytes": attn_b, "append_bytes": app_b,
         "t_append": t_append, "t_partial": t_partial, "t_merge": t_merge, "t_layer": t_layer,
         "graph": graph is not None, "graph_steps": copies, "setup_s": setup_s, "fused": fused, "planned": planned,
+        "invariant": invariant,
     }
 
 
@@ -592,7 +597,7 @@ def main():
     layers = args.layers or w.layers
     fused = args.append == "fused" and args.path == "q8"
     m = measure(torch, q8, dev, w, layers, args.steps, args.warmup, args.nparts, args.eager, args.path, args.topk,
-                fused, not args.no_plan)
+                fused, not args.no_plan, args.invariant)
     lens = m["lens"]
     B, nq, nkv, hd, kv_bs = w.batch, w.nq, w.nkv, w.head_dim, w.kv_bs
     attn_b, app_b = m["attn_bytes"], m["append_bytes"]
@@ -628,7 +633,7 @@ def main():
                 continue
             ws_ = workloads.WORKLOADS[name]
             sweep.append(sweep_entry(ws_, measure(torch, q8, dev, ws_, ws_.layers, 10, 2, 0, args.eager,
-                                                  fused=fused, planned=not args.no_plan)))
+                                                  fused=fused, planned=not args.no_plan, invariant=args.invariant)))
             torch.cuda.empty_cache()
             print(f"[sweep] {name} done", file=sys.stderr, flush=True)
 
@@ -643,7 +648,7 @@ def main():
         "vs_baseline": None, "dtype": "fp32" if args.path == "f32" else "int8/fp32", "data": "synthetic",
         "config": {
             "workload": w.name, "path": args.path, "topk": args.topk if args.path == "sparse" else None,
-            "append": "fused" if fused else "separate", "step_plan": m["planned"],
+            "append": "fused" if fused else "separate", "step_plan": m["planned"], "batch_invariant": m["invariant"],
             "batch": B, "nq_heads": nq, "nkv_heads": nkv, "head_dim": hd, "kv_bs": kv_bs,
             "layers": layers, "ctx": list(w.lens), "ctx_mean": float(lens.mean()), "nparts": m["nparts"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

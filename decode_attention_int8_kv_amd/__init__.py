@@ -28,6 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libq8kv.so")
 
 Q8_OK, Q8_EINVAL, Q8_EUNSUPPORTED, Q8_EWORKSPACE, Q8_EHIP = 0, -1, -2, -3, -4
 DEV_BAD_PLAN = 0x8
+BATCH_INVARIANT = 0x1           # q8_batch.flags: Q8_BATCH_INVARIANT
+ABI_VERSION = 7                 # the q8_batch / entry-point layout these bindings marshal
 QPATH_VALU, QPATH_MFMA = 0, 1   # q8_quantize_q: two lanes or one lane per 32-block
 DEV_BAD_SEQ_LEN, DEV_BAD_BLOCK_ID, DEV_BAD_TOKEN = 0x1, 0x2, 0x4
 HEAD_DIM = 128
@@ -53,7 +55,7 @@ class _Layer(ctypes.Structure):
 class _Batch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p), ("plan", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -106,6 +108,8 @@ def _load():
     lib.q8_status_string.restype = ctypes.c_char_p
     lib.q8_last_error.restype = ctypes.c_char_p
     lib.q8_abi_version.restype = I32
+    if lib.q8_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH}: ABI {lib.q8_abi_version()}, these bindings need {ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 
@@ -237,18 +241,22 @@ class KVLayer:
 @dataclasses.dataclass
 class Batch:
     """Per-step batch metadata: block_table int32 [batch, max_blocks_per_seq],
-    seq_lens int32 [batch] (device tensors), host-side max_seq_len, and an
-    optional step plan (a device tensor filled by decode_plan)."""
+    seq_lens int32 [batch] (device tensors), host-side max_seq_len, an
+    optional step plan (a device tensor filled by decode_plan), and whether
+    the decode calls cut it batch-invariantly (Q8_BATCH_INVARIANT: a
+    sequence's bits independent of the rest of the batch; no plan)."""
     block_table: object
     seq_lens: object
     batch: int
     max_blocks_per_seq: int
     max_seq_len: int
     plan: object = None
+    invariant: bool = False
 
     def c(self) -> _Batch:
         return _Batch(self.batch, self.max_blocks_per_seq, self.max_seq_len,
-                      _ptr(self.block_table), _ptr(self.seq_lens), _ptr(self.plan))
+                      _ptr(self.block_table), _ptr(self.seq_lens), _ptr(self.plan),
+                      BATCH_INVARIANT if self.invariant else 0)
 
     def with_plan(self, plan) -> "Batch":
         """The same batch with a step plan (or None)."""
@@ -272,16 +280,17 @@ def alloc_layer(num_blocks: int, kv_bs: int, nkv_heads: int, device="cuda", head
     return KVLayer(kc, vc, ks, vs, nkv_heads, kv_bs, num_blocks, head_dim, kf, vf)
 
 
-def make_batch(block_table, seq_lens, max_seq_len: int) -> Batch:
+def make_batch(block_table, seq_lens, max_seq_len: int, invariant: bool = False) -> Batch:
     """Batch from block_table int32 [batch, max_blocks_per_seq] and seq_lens
-    int32 [batch] (contiguous GPU tensors on one device)."""
+    int32 [batch] (contiguous GPU tensors on one device); invariant=True asks
+    the decode calls for the batch-invariant cut."""
     import torch
     if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
         raise ValueError("block_table: expected a 2-D torch tensor [batch, max_blocks_per_seq]")
     b, mb = int(block_table.shape[0]), int(block_table.shape[1])
     (_Args().need(block_table, "block_table", torch.int32, b * mb, exact=True)
             .need(seq_lens, "seq_lens", torch.int32, b, exact=True).done())
-    return Batch(block_table, seq_lens, b, mb, int(max_seq_len))
+    return Batch(block_table, seq_lens, b, mb, int(max_seq_len), invariant=bool(invariant))
 
 
 # ------------------------------------------------------------- entry points --

@@ -53,6 +53,8 @@ q8_status check_batch(const q8_batch *b, const q8_kv_layer *l)
     if (!b->block_table || !b->seq_lens) return Q8_EINVAL;
     if (!aligned(b->block_table, 4) || !aligned(b->seq_lens, 4)) return Q8_EINVAL;
     if (b->plan && !aligned(b->plan, 64)) return Q8_EINVAL;
+    if (b->flags & ~Q8_BATCH_INVARIANT) return Q8_EINVAL;
+    if ((b->flags & Q8_BATCH_INVARIANT) && b->plan) return Q8_EINVAL;   // an invariant batch is not planned
     return Q8_OK;
 }
 
@@ -121,7 +123,7 @@ size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *
 size_t q8_decode_plan_bytes(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, int32_t nparts)
 {
     if (check_layer(layer) != Q8_OK || check_batch(batch, layer) != Q8_OK ||
-        check_heads(layer, nq_heads) != Q8_OK || nparts < 0)
+        check_heads(layer, nq_heads) != Q8_OK || nparts < 0 || (batch->flags & Q8_BATCH_INVARIANT))
         return 0;
     return q8kv::step_plan_bytes(*batch, q8kv::make_plan(*layer, *batch, nq_heads, nparts).nparts);
 }
@@ -133,7 +135,7 @@ q8_status q8_decode_plan(const q8_kv_layer *layer, const q8_batch *batch, int32_
     if ((s = check_layer(layer)) != Q8_OK) return s;
     if ((s = check_batch(batch, layer)) != Q8_OK) return s;
     if ((s = check_heads(layer, nq_heads)) != Q8_OK) return s;
-    if (nparts < 0) return Q8_EINVAL;
+    if (nparts < 0 || (batch->flags & Q8_BATCH_INVARIANT)) return Q8_EINVAL;
     if (dev_status && !aligned(dev_status, 4)) return Q8_EINVAL;
     const q8kv::DecodePlan pl = q8kv::make_plan(*layer, *batch, nq_heads, nparts);
     const size_t need = q8kv::step_plan_bytes(*batch, pl.nparts);

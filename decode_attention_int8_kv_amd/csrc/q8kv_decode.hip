@@ -476,6 +476,12 @@ struct MergeParams {
     int32_t nq;
     int32_t nparts;
     int32_t piece_cost;
+    // batch-invariant cut (walk_chunks), or 0: tiles per chunk and records per
+    // sequence; the chunk count comes from seq_lens
+    int32_t chunk_tiles;
+    int32_t max_chunks;
+    const int32_t *seq_lens;
+    int32_t max_seq_len;
 };
 
 constexpr int kMaxMergeWaves = 16;
@@ -543,24 +549,44 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     if (p.plan && !(p.plan[kPhMagic] == kPlanMagic && p.plan[kPhBatch] == p.batch && p.plan[kPhParts] == p.nparts &&
                     p.plan[kPhPieceCost] == p.piece_cost))
         return;
-    const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1], total = p.ws_prefix[p.batch];
-    if (e0 == a0) return;
-    // ranges of the first and the last tile (before the first tile of a
-    // sequence other than 0 lie piece_cost units that hold none)
-    const int first = a0 + (b > 0 ? p.piece_cost : 0);
-    const int i0 = part_of(first, total, p.nparts), i1 = part_of(e0 - 1, total, p.nparts);
-    if (i0 == i1) return;
-    const int np = i1 - i0 + 1;
-    // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
-    const int slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
+    int np, i0 = 0, slot0 = 0, total = 0;
+    bool may_be_empty = false;
+    if (p.chunk_tiles > 0) {
+        // batch-invariant cut: the sequence's chunks, records b * max_chunks + c
+        int n = p.seq_lens[b];
+        if (n < 0 || n > p.max_seq_len) n = 0;   // reported by the partial kernel
+        const int tiles = (n + kTile - 1) / kTile, L = chunk_tiles_of(tiles, p.chunk_tiles);
+        np = (tiles + L - 1) / L;
+        if (np <= 1) return;   // one chunk: finished in place
+        i0 = b * p.max_chunks;
+    } else {
+        const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1];
+        total = p.ws_prefix[p.batch];
+        if (e0 == a0) return;
+        // ranges of the first and the last tile (before the first tile of a
+        // sequence other than 0 lie piece_cost units that hold none)
+        const int first = a0 + (b > 0 ? p.piece_cost : 0);
+        i0 = part_of(first, total, p.nparts);
+        const int i1 = part_of(e0 - 1, total, p.nparts);
+        if (i0 == i1) return;
+        np = i1 - i0 + 1;
+        // the first piece sits in slot 1 of its range when the range starts in an earlier sequence
+        slot0 = part_start(i0, total, p.nparts) < a0 ? 1 : 0;
+        // a range can be empty (and write no record) only when there are more
+        // ranges than cut-axis units; otherwise skip the two divisions per
+        // record (a range strictly between the first and the last tile's holds
+        // only tiles of this sequence)
+        may_be_empty = p.nparts > total;
+    }
+    // record of piece j: (range i0 + j, slot) = index (2 (i0 + j) + slot) nq + h,
+    // or chunk record i0 + j = index (i0 + j) nq + h
+    const bool chunked = p.chunk_tiles > 0;
+    auto record = [&](int j) {
+        return chunked ? (size_t)(i0 + j) * p.nq + h : ((size_t)(i0 + j) * 2 + (j == 0 ? slot0 : 0)) * p.nq + h;
+    };
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, waves = blockDim.x >> 6;
     const int pg = lane / kLanesPerPiece, dl = lane - pg * kLanesPerPiece;
     const int dim2 = sl * kLanesPerPiece + dl;   // this lane's float2 of the 64 in a row
-    // a range can be empty (and write no record) only when there are more
-    // ranges than cut-axis units; otherwise skip the two divisions per
-    // record (a range strictly between the first and the last tile's holds
-    // only tiles of this sequence)
-    const bool may_be_empty = p.nparts > total;
 
     float m = -INFINITY, s = 0.0f, ax = 0.0f, ay = 0.0f;
     const int stride = waves * Slices;   // piece groups per round of one load
@@ -572,7 +598,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
             const bool have = j < np && (!may_be_empty || part_start(i, total, p.nparts) !=
                                                               part_start(i + 1, total, p.nparts));
             if (have) {
-                const size_t r = ((size_t)i * 2 + (j == 0 ? slot0 : 0)) * p.nq + h;
+                const size_t r = record(j);
                 ms[u] = p.ws_ms[r];
                 av[u] = reinterpret_cast<const float2 *>(p.ws_acc + r * kHeadDim)[dim2];
             } else {
@@ -702,10 +728,32 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     int mw = 1;
     while (mw < kMaxMergeWaves && (long long)mw * kMergeBatch * pl.merge_slices < per_seq) mw <<= 1;
     pl.merge_waves = mw;
+    pl.chunk_tiles = 0;
+    pl.max_chunks = 0;
+    size_t records = 2 * (size_t)pl.nparts;   // (range, slot) records per query head
+    if (batch.flags & Q8_BATCH_INVARIANT) {
+        // chunks counted from each sequence's start, no units charged per
+        // sequence, one record per chunk; the merge's shape is fixed, so the
+        // order in which it combines a sequence's chunk states depends on
+        // their number only
+        pl.piece_cost = 0;
+        pl.chunk_tiles = kInvariantChunkTiles;
+        // the most chunks a sequence of at most max_seq_len positions has
+        const int tiles_ub = (batch.max_seq_len + kTile - 1) / kTile;
+        const int short_ub = tiles_ub < 64 * kInvariantChunkTiles ? tiles_ub : 64 * kInvariantChunkTiles - 1;
+        const int long_chunks = tiles_ub >= 64 * kInvariantChunkTiles
+                                    ? (tiles_ub + 2 * kInvariantChunkTiles - 1) / (2 * kInvariantChunkTiles) : 0;
+        const int short_chunks = (short_ub + kInvariantChunkTiles - 1) / kInvariantChunkTiles;
+        pl.max_chunks = long_chunks > short_chunks ? long_chunks : short_chunks;
+        if (pl.max_chunks < 1) pl.max_chunks = 1;
+        pl.merge_slices = 1;
+        pl.merge_waves = 4;
+        records = (size_t)batch.batch * pl.max_chunks;
+    }
     pl.off_prefix = 0;
     pl.off_ms = align_up(sizeof(int32_t) * ((size_t)batch.batch + 1), 256);
-    pl.off_acc = pl.off_ms + align_up(sizeof(float) * 2 * 2 * (size_t)pl.nparts * nq, 256);
-    pl.bytes = pl.off_acc + sizeof(float) * 2 * (size_t)pl.nparts * nq * kHeadDim;
+    pl.off_acc = pl.off_ms + align_up(sizeof(float) * 2 * records * nq, 256);
+    pl.bytes = pl.off_acc + sizeof(float) * records * nq * kHeadDim;
     return pl;
 }
 
@@ -742,6 +790,8 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
     p.nparts = plan.nparts;
     p.head_groups = plan.head_groups;
     p.piece_cost = plan.piece_cost;
+    p.chunk_tiles = plan.chunk_tiles;
+    p.max_chunks = plan.max_chunks;
     p.sc = (float)((double)scale * 1.4426950408889634);
     return p;
 }
@@ -765,7 +815,7 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
                                const DecodePlan &plan, void *workspace, hipStream_t stream)
 {
     (void)layer;
-    if (plan.nparts <= 1) return hipSuccess;
+    if (plan.nparts <= 1 && plan.chunk_tiles == 0) return hipSuccess;
     MergeParams p;
     char *ws = static_cast<char *>(workspace);
     // the cut-axis prefix: written by the partial kernel, or the step plan's
@@ -779,6 +829,10 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
     p.nq = nq;
     p.nparts = plan.nparts;
     p.piece_cost = plan.piece_cost;
+    p.chunk_tiles = plan.chunk_tiles;
+    p.max_chunks = plan.max_chunks;
+    p.seq_lens = batch.seq_lens;
+    p.max_seq_len = batch.max_seq_len;
     const dim3 grid((unsigned)((long long)batch.batch * nq * plan.merge_slices)), block(plan.merge_waves * 64);
     if (plan.merge_slices == 4)
         hipLaunchKernelGGL(q8_attn_merge_kernel<4>, grid, block, 0, stream, p);

@@ -17,6 +17,8 @@ struct DecodePlan {
     int merge_waves;     // waves per merge workgroup
     int merge_slices;    // merge workgroups per (sequence, query head): dim slices 1, 2 or 4
     int piece_cost;      // cut-axis units charged per non-empty sequence (see q8kv_ranges.hpp)
+    int chunk_tiles;     // batch-invariant cut: tiles per chunk (walk_chunks), or 0
+    int max_chunks;      // batch-invariant cut: chunk records per sequence
     size_t off_prefix, off_ms, off_acc, bytes;
 };
 
@@ -25,6 +27,22 @@ struct DecodePlan {
 // loads are dependent round trips), so ranges that start many sequences get
 // fewer tiles.
 constexpr int kPieceCost = 2;
+
+// The batch-invariant cut (Q8_BATCH_INVARIANT): chunks of this many 32-token
+// tiles counted from each sequence's start (Q8_INVARIANT_CHUNK_TOKENS
+// positions); about four chunks per range on a batched step keep the ranges'
+// work within a chunk of each other.  A sequence of 64 chunks or more uses
+// chunks twice as long (chunk_tiles_of): half the chunk starts and records
+// where they cost most, and still at least 32 chunks to spread.
+constexpr int kInvariantChunkTiles = 8;
+
+// Tiles per chunk of a sequence of `tiles` tiles under the batch-invariant
+// cut with base chunk length `base` (a function of the sequence's own length
+// only).
+__host__ __device__ inline int chunk_tiles_of(int tiles, int base)
+{
+    return tiles >= 64 * base ? 2 * base : base;
+}
 
 DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq);

@@ -45,6 +45,10 @@ struct DecodeParams {
     int32_t nparts;
     int32_t head_groups;
     int32_t piece_cost;   // cut-axis units in front of every non-empty sequence's tiles
+    // batch-invariant cut (walk_chunks), or 0: tiles per chunk, and the chunk
+    // records per sequence (record of chunk c of sequence b: b * max_chunks + c)
+    int32_t chunk_tiles;
+    int32_t max_chunks;
     float sc;             // softmax scale * log2(e)
 };
 
@@ -217,6 +221,142 @@ __device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend
     }
 }
 
+// Fused append of walk_ranges / walk_chunks: the new token of every
+// sequence b >= lo with owns(b), for this wave's KV head kh, before the wave
+// loads any tile; groups of 64 sequences from lo until past(first of the
+// group).  The owning range is the one whose wave reads the token's tile, so
+// the wave reads back only rows it wrote itself.  Lane i looks up sequence
+// b0 + i's block while the rows of the first four owned sequences are read;
+// rows are written four at a time.  A wave's vector memory operations are
+// performed in order, so a wavefront-scope fence (no wait; it keeps the
+// compiler from moving the tile loads above the stores) is all the ordering
+// needed.  An agent-scope fence would write back and invalidate L2 in every
+// workgroup.
+template <class Owns, class Past>
+__device__ __forceinline__ void append_rows(const DecodeParams &p, const int *lens, int kh, int lane, int lo,
+                                            Owns &&owns, Past &&past)
+{
+    bool wrote = false;
+    for (int b0 = lo; b0 < p.batch && !past(b0); b0 += 64) {
+        const int b = b0 + lane;
+        const bool own = b < p.batch && owns(b);
+        const int pos = own ? lens[b] - 1 : 0;
+        int blk = 0;
+        if (own) blk = p.block_table[(size_t)b * p.max_blocks_per_seq + (pos >> p.cache.kv_bs_log2)];
+        uint64_t todo = __builtin_amdgcn_ballot_w64(own);
+        int idx[4];
+        float2 k[4], v[4];
+        auto load_group = [&]() {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                idx[j] = todo ? __builtin_ctzll(todo) : -1;
+                todo &= todo - 1;
+                if (idx[j] >= 0) {
+                    const size_t src = ((size_t)(b0 + idx[j]) * p.cache.nkv + kh) * kHeadDim + 2 * lane;
+                    k[j] = *reinterpret_cast<const float2 *>(p.k_new + src);
+                    v[j] = *reinterpret_cast<const float2 *>(p.v_new + src);
+                }
+            }
+        };
+        if (!todo) continue;
+        load_group();
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(own && (unsigned)blk >= (unsigned)p.cache.num_blocks);
+        if (bad != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
+        for (;;) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (idx[j] < 0) break;
+                if ((bad >> idx[j]) & 1) continue;
+                const int ps = __builtin_amdgcn_readlane(pos, idx[j]);
+                const int bk = __builtin_amdgcn_readlane(blk, idx[j]);
+                append_row_vals(const_cast<int8_t *>(p.cache.k_codes), const_cast<int8_t *>(p.cache.v_codes),
+                                const_cast<float *>(p.cache.k_scale), const_cast<float *>(p.cache.v_scale),
+                                const_cast<float *>(p.k_f32), const_cast<float *>(p.v_f32), p.cache.nkv,
+                                p.cache.kv_bs_log2, bk, ps & ((1 << p.cache.kv_bs_log2) - 1), kh, k[j], v[j],
+                                lane);
+                wrote = true;
+            }
+            if (!todo) break;
+            load_group();
+        }
+    }
+    if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Output rows of the empty sequences whose cut-axis position falls in units
+// [start, end) of range `part` (the last range also takes those at the very
+// end), zeroed by the whole workgroup.
+__device__ __forceinline__ void zero_empty_rows(const DecodeParams &p, const int *pref, int part, int start, int end,
+                                                int lane)
+{
+    const int total = pref[p.batch];
+    // first b with pref[b] >= start (start <= total = pref[batch])
+    const int lo = p.batch == 1 ? (start > 0 ? 1 : 0) : count_le(pref, p.batch + 1, start - 1, lane);
+    const bool last = (part == p.nparts - 1);
+    for (int b = lo; b < p.batch && (pref[b] < end || (last && pref[b] <= total)); ++b) {
+        if (pref[b + 1] != pref[b]) continue;
+        float4 *o = reinterpret_cast<float4 *>(p.out + (size_t)b * p.nq * kHeadDim);
+        for (int i = threadIdx.x; i < p.nq * (kHeadDim / 4); i += blockDim.x)
+            o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// The batch-invariant walk (p.chunk_tiles > 0): every sequence is cut into
+// chunks of chunk_tiles_of(its tiles, chunk_tiles) tiles counted from its own
+// start, and a range takes
+// the chunks whose first tile lies in it (units [start, end) of the tile
+// prefix, which here charges no units per sequence).  Each chunk is walked as
+// a piece of its own: a sequence of one chunk is finished in place, the
+// chunks of a longer one leave their states in records b * max_chunks + c,
+// which the merge kernel combines in chunk order.  Nothing of this depends on
+// the other sequences or the partition count, so neither do the bits.  The
+// fused append is done by the range that walks the sequence's last chunk.
+template <class Attend>
+__device__ __forceinline__ void walk_chunks(const DecodeParams &p, int *pref, int *lens, int part, int hg, int kh,
+                                            int lane, Attend &&attend)
+{
+    build_prefix(p, pref, lens, blockIdx.x == 0);
+    const int total = pref[p.batch];
+    const int start = part_start(part, total, p.nparts);
+    const int end = part_start(part + 1, total, p.nparts);
+    // first tile of sequence b's last chunk (tiles > 0)
+    auto last_chunk = [&](int b) {
+        const int tiles = pref[b + 1] - pref[b], L = chunk_tiles_of(tiles, p.chunk_tiles);
+        return pref[b] + ((tiles - 1) / L) * L;
+    };
+
+    if (p.k_new && lens && kh < p.cache.nkv && start < end) {
+        const int lo = p.batch == 1 ? 0 : count_le(pref + 1, p.batch, start, lane);
+        append_rows(p, lens, kh, lane, lo,
+                    [&](int b) {
+                        if (pref[b + 1] == pref[b]) return false;
+                        const int c = last_chunk(b);
+                        return start <= c && c < end;
+                    },
+                    [&](int b0) { return pref[b0] >= end; });
+    }
+
+    if (kh < p.cache.nkv && start < end) {
+        // the sequence holding tile `start`, then every later one that starts before `end`
+        int b = p.batch == 1 ? 0 : count_le(pref, p.batch, start, lane) - 1;
+        for (; b < p.batch && pref[b] < end; ++b) {
+            b = uniform(b);
+            const int a0 = uniform(pref[b]), tiles = uniform(pref[b + 1]) - a0;
+            if (tiles == 0) continue;
+            const int L = chunk_tiles_of(tiles, p.chunk_tiles);
+            const int nch = (tiles + L - 1) / L;
+            const int n = uniform(lens ? lens[b] : p.seq_lens[b]);
+            for (int c = a0 >= start ? 0 : (start - a0 + L - 1) / L; c < nch && a0 + c * L < end; ++c) {
+                const int rec = b * p.max_chunks + c;
+                attend(b, kh, lane, c * L, min(tiles, (c + 1) * L), n, nch == 1, rec >> 1, rec & 1,
+                       static_cast<const TileBlocks *>(nullptr));
+            }
+        }
+    }
+
+    if (hg == 0) zero_empty_rows(p, pref, part, start, end, lane);
+}
+
 // The whole job of one workgroup of a partial kernel: range blockIdx.x /
 // head_groups, KV heads hg * waves + wave.  attend(b, kh, lane, lt0, lt1, n,
 // whole, part, slot, first) runs one wave over tiles [lt0, lt1) of sequence b
@@ -239,6 +379,10 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int kh = hg * (int)(blockDim.x >> 6) + wave;
+    if (p.chunk_tiles > 0) {
+        walk_chunks(p, pref, lens, part, hg, kh, lane, attend);
+        return;
+    }
 
     build_prefix(p, pref, lens, blockIdx.x == 0);
     if (blockIdx.x == 0)
@@ -249,63 +393,14 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
     const int end = part_start(part + 1, total, p.nparts);
 
     if (p.k_new && lens && kh < p.cache.nkv && start < end) {
-        // Fused append: the new token of every sequence whose last tile lies
-        // in this range (its position n - 1 is in that tile, which no other
-        // range reads), for this wave's KV head, before any tile is loaded.
-        // Lane i looks up sequence lo + i's block while the rows of the first
-        // four such sequences are read; rows are written four at a time.  The
-        // wave reads back only rows it wrote itself, and a wave's vector
-        // memory operations are performed in order, so a wavefront-scope
-        // fence (no wait; it keeps the compiler from moving the tile loads
-        // above the stores) is all the ordering needed.  An agent-scope fence
-        // would write back and invalidate L2 in every workgroup.
-        // the first sequence whose tiles end after `start` (one exists: start < total)
+        // the sequences whose last tile lies in this range (their position
+        // n - 1 is in that tile, which no other range reads), starting with
+        // the first sequence whose tiles end after `start` (one exists:
+        // start < total)
         const int lo = p.batch == 1 ? 0 : count_le(pref + 1, p.batch, start, lane);
-        bool wrote = false;
-        for (int b0 = lo; b0 < p.batch && pref[b0 + 1] <= end; b0 += 64) {
-            const int b = b0 + lane;
-            const bool own = b < p.batch && pref[b + 1] <= end && pref[b + 1] > pref[b];
-            const int pos = own ? lens[b] - 1 : 0;
-            int blk = 0;
-            if (own) blk = p.block_table[(size_t)b * p.max_blocks_per_seq + (pos >> p.cache.kv_bs_log2)];
-            uint64_t todo = __builtin_amdgcn_ballot_w64(own);
-            int idx[4];
-            float2 k[4], v[4];
-            auto load_group = [&]() {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    idx[j] = todo ? __builtin_ctzll(todo) : -1;
-                    todo &= todo - 1;
-                    if (idx[j] >= 0) {
-                        const size_t src = ((size_t)(b0 + idx[j]) * p.cache.nkv + kh) * kHeadDim + 2 * lane;
-                        k[j] = *reinterpret_cast<const float2 *>(p.k_new + src);
-                        v[j] = *reinterpret_cast<const float2 *>(p.v_new + src);
-                    }
-                }
-            };
-            if (!todo) continue;
-            load_group();
-            const uint64_t bad = __builtin_amdgcn_ballot_w64(own && (unsigned)blk >= (unsigned)p.cache.num_blocks);
-            if (bad != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
-            for (;;) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (idx[j] < 0) break;
-                    if ((bad >> idx[j]) & 1) continue;
-                    const int ps = __builtin_amdgcn_readlane(pos, idx[j]);
-                    const int bk = __builtin_amdgcn_readlane(blk, idx[j]);
-                    append_row_vals(const_cast<int8_t *>(p.cache.k_codes), const_cast<int8_t *>(p.cache.v_codes),
-                                    const_cast<float *>(p.cache.k_scale), const_cast<float *>(p.cache.v_scale),
-                                    const_cast<float *>(p.k_f32), const_cast<float *>(p.v_f32), p.cache.nkv,
-                                    p.cache.kv_bs_log2, bk, ps & ((1 << p.cache.kv_bs_log2) - 1), kh, k[j], v[j],
-                                    lane);
-                    wrote = true;
-                }
-                if (!todo) break;
-                load_group();
-            }
-        }
-        if (wrote) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        append_rows(p, lens, kh, lane, lo,
+                    [&](int b) { return pref[b + 1] <= end && pref[b + 1] > pref[b]; },
+                    [&](int b0) { return pref[b0 + 1] > end; });
     }
 
     if (kh < p.cache.nkv && start < end) {
@@ -331,17 +426,7 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
         }
     }
 
-    if (hg == 0) {
-        // first b with pref[b] >= start (start <= total = pref[batch])
-        const int lo = p.batch == 1 ? (start > 0 ? 1 : 0) : count_le(pref, p.batch + 1, start - 1, lane);
-        const bool last = (part == p.nparts - 1);
-        for (int b = lo; b < p.batch && (pref[b] < end || (last && pref[b] <= total)); ++b) {
-            if (pref[b + 1] != pref[b]) continue;
-            float4 *o = reinterpret_cast<float4 *>(p.out + (size_t)b * p.nq * kHeadDim);
-            for (int i = threadIdx.x; i < p.nq * (kHeadDim / 4); i += blockDim.x)
-                o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
+    if (hg == 0) zero_empty_rows(p, pref, part, start, end, lane);
 }
 
 // Host: the kernel arguments of one decode call.

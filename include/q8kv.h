@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define Q8KV_ABI_VERSION 6
+#define Q8KV_ABI_VERSION 7
 
 typedef enum q8_status {
     Q8_OK = 0,
@@ -106,7 +106,22 @@ typedef struct q8_kv_layer {
  * bit-identical results; the other entry points ignore it.  A plan made for
  * another batch size, partition count, kv_bs or max_seq_len is detected on
  * the device (Q8_DEV_BAD_PLAN, no output written); one made before the
- * arrays changed is not -- make a new plan whenever they change. */
+ * arrays changed is not -- make a new plan whenever they change.
+ * flags: 0, or Q8_BATCH_INVARIANT: the decode entry points then cut every
+ * sequence into chunks of Q8_INVARIANT_CHUNK_TOKENS positions counted from its
+ * start (twice that for a sequence of 64 such chunks or more; the last chunk
+ * shorter), give every chunk its own partial state and
+ * combine a sequence's chunk states in chunk order with a fixed association
+ * -- the online-softmax rescale rule of "9-2 flash_attn_single_q_q8_neon"
+ * §2 segment 2 applied to partial states, one division at the end -- so a
+ * sequence's output bits depend on nothing but its own length, K, V and q:
+ * not on the other sequences of the batch, their order, the partition count
+ * or the placement of its blocks.  Chunks are shared out over the ranges by
+ * their first position, which balances the work less evenly than the default
+ * cut.  The workspace holds up to batch * ceil(max_seq_len / 256) records per
+ * query head.  Such a batch carries no step plan (Q8_EINVAL). */
+#define Q8_BATCH_INVARIANT 0x1
+#define Q8_INVARIANT_CHUNK_TOKENS 256
 typedef struct q8_batch {
     int32_t batch;
     int32_t max_blocks_per_seq;
@@ -114,6 +129,7 @@ typedef struct q8_batch {
     const int32_t *block_table;
     const int32_t *seq_lens;
     const void *plan;
+    int32_t flags;
 } q8_batch;
 
 /* kv_quantize_per_head append ("9-3" §2; stored layout "9-2" §2 segment 2).
@@ -155,7 +171,8 @@ size_t q8_decode_attn_workspace_bytes(const q8_kv_layer *layer, const q8_batch *
  * seq_lens) and before the first decode of the step.  plan: device memory of
  * at least q8_decode_plan_bytes() bytes, 64-byte aligned; batch->plan is
  * ignored.  Bad lengths set Q8_DEV_BAD_SEQ_LEN here (the planned decode calls
- * then treat those sequences as empty without reporting again). */
+ * then treat those sequences as empty without reporting again).  A batch with
+ * Q8_BATCH_INVARIANT has no plan: Q8_EINVAL (and 0 bytes). */
 size_t q8_decode_plan_bytes(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads,
                             int32_t nparts);
 q8_status q8_decode_plan(const q8_kv_layer *layer, const q8_batch *batch, int32_t nq_heads, int32_t nparts,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(q8):
 
 
 def test_version_and_status_strings(q8):
-    assert q8.abi_version() == 6
+    assert q8.abi_version() == 7 == q8.ABI_VERSION
     assert q8.status_string(0) == "ok"
     assert q8.status_string(-3).startswith("workspace")
     assert q8.last_error() == ""
@@ -314,3 +314,26 @@ def test_binding_rejects_wrong_tensors_before_any_call(q8):
         q8.prefill_attn(L, B, 4, torch.zeros(2, dtype=torch.int32), 1, q, 0.1, out)
     with pytest.raises(ValueError, match="partials: .*elements"):
         q8.qk_block_partials(L, B, 4, q, torch.zeros(10, dtype=torch.int32))
+
+
+def test_batch_flags_and_the_invariant_cut(q8):
+    L = layer(q8)
+    lib = q8.lib()
+    # unknown flag bits are refused; the invariant flag is accepted
+    bad = batch(q8)
+    c = bad.c()
+    c.flags = 0x2
+    assert lib.q8_decode_attn(ctypes.byref(L.c()), ctypes.byref(c), 16, FAKE, 0.088, FAKE, 4, FAKE, 1 << 30,
+                              None, None) == -1
+    inv = batch(q8, invariant=True)
+    assert inv.c().flags == q8.BATCH_INVARIANT
+    # an invariant batch carries no step plan and cannot be planned
+    assert call_decode(q8, L, batch(q8, invariant=True, plan=FAKE)) == -1
+    assert lib.q8_decode_plan_bytes(ctypes.byref(L.c()), ctypes.byref(inv.c()), 16, 0) == 0
+    assert lib.q8_decode_plan(ctypes.byref(L.c()), ctypes.byref(inv.c()), 16, 0, FAKE, 1 << 20, None, None) == -1
+    # one record per chunk of 256 positions per sequence and query head, for any partition count
+    for nparts in (0, 1, 4, 1000):
+        need = q8.decode_attn_workspace_bytes(L, inv, 16, nparts)
+        chunks = 4 * ((300 + 255) // 256)
+        assert need >= chunks * 16 * (128 + 2) * 4
+        assert call_decode(q8, L, inv, ws_bytes=need - 1, nparts=nparts) == -3
