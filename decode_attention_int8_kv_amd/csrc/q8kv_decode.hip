@@ -34,11 +34,17 @@ namespace q8kv {
 template <int G> struct PipeDepth { static constexpr int value = 2; };
 
 // One wave: attention of the G query heads of KV head kh over tiles
-// [lt0, lt1) of sequence b (length n).
-template <int G, bool Big>
+// [lt0, lt1) of sequence b (length n).  The state goes to the output rows
+// (whole) or to slot `slot` of record `part`, i.e. to record 2 part + slot.
+// With Runs, [lt0, lt1) is a run of chunks of `chunk` tiles each (lt0 a
+// multiple of chunk): the state is written to record 2 part + slot + i at the
+// end of the run's chunk i and started afresh, while the next chunk's first
+// tile loads are already in flight, so each chunk's record is the one a piece
+// of that chunk alone would leave.
+template <int G, bool Big, bool Runs>
 __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
                                              int lt0, int lt1, int n, bool whole, int part,
-                                             int slot, const TileBlocks *first)
+                                             int slot, const TileBlocks *first, int chunk)
 {
     const int c = lane & 7, tslot = lane >> 3;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
@@ -91,21 +97,24 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     constexpr int NQ = kPvMfma ? G / 4 : 1;
     float M[G], S[G], acc[G][16];
     v4f accm[NQ][16];
+    auto fresh = [&]() {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        M[g] = -INFINITY;
-        S[g] = 0.0f;
-        if constexpr (!kPvMfma) {
+        for (int g = 0; g < G; ++g) {
+            M[g] = -INFINITY;
+            S[g] = 0.0f;
+            if constexpr (!kPvMfma) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+                for (int j = 0; j < 16; ++j) acc[g][j] = 0.0f;
+            }
         }
-    }
-    if constexpr (kPvMfma) {
+        if constexpr (kPvMfma) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
+            for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) accm[q][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+                for (int j = 0; j < 16; ++j) accm[q][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    fresh();
 
     auto process = [&](const Tile &t) {
         float ks[4], vs[4];
@@ -199,66 +208,76 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
         }
     };
 
+    // The state (M, S, acc) to the output rows or to record `rec`.  The 16 G
+    // accumulators of every lane are summed over the token slots scattered
+    // (slot_reduce_scatter): token slot s ends with 2 G consecutive dims of
+    // head s G / 8, which its 8 lanes write.
+    auto finish = [&](bool to_out, int rec) {
+        constexpr int N = 16 * G, P = N / 8;
+        float v[N];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if constexpr (kPvMfma)
+                    v[16 * g + j] = accm[g >> 2][j][g & 3];
+                else
+                    v[16 * g + j] = acc[g][j];
+            }
+        float z[P];
+        slot_reduce_scatter<N>(v, z, lane);
+        const int gh = (tslot * G) >> 3, j0 = (tslot * P) & 15;
+        float sr = 0.0f, mr = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float sg = sum_over_slots(S[g]);
+            sr = gh == g ? sg : sr;
+            mr = gh == g ? M[g] : mr;
+        }
+        const int h = kh * G + gh;
+        if (to_out) {
+            // one division at the end ("9-2" §2 segment 3)
+#pragma unroll
+            for (int k = 0; k < P; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
+            store_floats<P>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c + j0, z);
+        } else {
+            const size_t idx = (size_t)rec * p.nq + h;
+            store_floats<P>(p.ws_acc + idx * kHeadDim + 16 * c + j0, z);
+            if (c == 0 && j0 == 0) p.ws_ms[idx] = make_float2(mr, sr);
+        }
+    };
+
     // D register tiles (the first D - 1 loaded above): while tile i is
     // processed, the loads of tiles i + 1 .. i + D - 1 are in flight and the
     // block ids of tile i + D are being read.  Tile i lives in t[i % D].
     // Tokens past the piece count as past the end, so the tiles loaded
-    // beyond the piece cost no HBM traffic.
-    int lt = lt0;
-    while (true) {
+    // beyond the piece cost no HBM traffic.  Rounds of D tiles, the last one
+    // possibly short: the loop's only exit is its count, and a chunk
+    // boundary of a run (after a whole round: D divides the chunk length) is
+    // handled inside the round's last step, so no path that leaves the loop
+    // or skips a step runs into the flush (the compiler would make the flush
+    // wait there for loads still in flight).
+    int lt = lt0, rec = 2 * part + slot, cut = Runs ? lt0 + chunk : lt1;
+    for (int r = (lt1 - lt0 + D - 1) / D; r > 0; --r) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if (d > 0 && lt >= lt1) continue;   // the last round may be short
             // here lt % D == (lt0 + d) % D relative to the prologue's slots
             const int nxt = (d + D - 1) % D;
             load_tile<true, Big>(p.cache, bl[nxt], lo, lane, (lt + D - 1) * kTile, ne, p.dev_status, t[nxt]);
             fetch_blocks_ahead<Big>(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
             process(t[d]);
-            if (++lt >= lt1) goto piece_done;
-        }
-    }
-piece_done:
-
-    if constexpr (kPvMfma) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[g][j] = accm[g >> 2][j][g & 3];
-    }
-
-    // Sum the 8 token slots of the wave.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        S[g] = sum_over_slots(S[g]);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[g][j] = sum_over_slots(acc[g][j]);
-    }
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (tslot != g) continue;
-        const int h = kh * G + g;
-        if (whole) {
-            // one division at the end ("9-2" §2 segment 3)
-            const float sg = S[g];
-            float4 *o = reinterpret_cast<float4 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float4 r;
-                r.x = sg > 0.0f ? acc[g][4 * j + 0] / sg : 0.0f;
-                r.y = sg > 0.0f ? acc[g][4 * j + 1] / sg : 0.0f;
-                r.z = sg > 0.0f ? acc[g][4 * j + 2] / sg : 0.0f;
-                r.w = sg > 0.0f ? acc[g][4 * j + 3] / sg : 0.0f;
-                o[j] = r;
+            ++lt;
+            if constexpr (Runs) {
+                if (d == D - 1 && lt == cut && lt < lt1) {   // a chunk of the run ends
+                    finish(false, rec++);
+                    fresh();
+                    cut += chunk;
+                }
             }
-        } else {
-            const size_t idx = ((size_t)part * 2 + slot) * p.nq + h;
-            float4 *a = reinterpret_cast<float4 *>(p.ws_acc + idx * kHeadDim + 16 * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                a[j] = make_float4(acc[g][4 * j], acc[g][4 * j + 1], acc[g][4 * j + 2], acc[g][4 * j + 3]);
-            if (c == 0) p.ws_ms[idx] = make_float2(M[g], S[g]);
         }
     }
+    finish(whole, rec);
 }
 
 // Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores
@@ -287,8 +306,10 @@ __device__ __forceinline__ float row16_sum(float v)
     return v + dpp_f<kDppRor8>(v);
 }
 
+template <bool Runs>
 __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, int kh, int lane, int lt0, int lt1,
-                                                int n, bool whole, int part, int slot, const TileBlocks *first)
+                                                int n, bool whole, int part, int slot, const TileBlocks *first,
+                                                int chunk)
 {
     constexpr int G = 4;
     const int c = lane & 7, tslot = lane >> 3;
@@ -325,12 +346,16 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
     }
     const float *qs = mq.qs;
 
-    float M[G], Sl = 0.0f;   // M per head (uniform); Sl: this lane's share of head lg's sum
+    float M[G], Sl;   // M per head (uniform); Sl: this lane's share of head lg's sum
     v4f accm[16];
+    auto fresh = [&]() {
+        Sl = 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) M[g] = -INFINITY;
+        for (int g = 0; g < G; ++g) M[g] = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) accm[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int jj = 0; jj < 16; ++jj) accm[jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    fresh();
 
     // ds_bpermute byte addresses of the score lanes holding head c % 4's
     // weight of token slot (+ 8)
@@ -400,69 +425,75 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         (void)m2;
     };
 
-    int lt = lt0;
-    while (true) {
+    // the state to the output rows or to record `rec`, summed over the token
+    // slots scattered (as in attend_piece): slot s holds dims 8 (s & 1) + k of
+    // head s / 2 = lg, whose sum row16_sum(Sl) gives in the same lanes
+    auto finish = [&](bool to_out, int rec) {
+        float v[16 * G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) v[16 * g + jj] = accm[jj][g];
+        float z[2 * G];
+        slot_reduce_scatter<16 * G>(v, z, lane);
+        const float sr = row16_sum(Sl);
+        const float mr = lg == 0 ? M[0] : lg == 1 ? M[1] : lg == 2 ? M[2] : M[3];
+        const int h = kh * G + lg, d0 = 16 * c + 8 * (tslot & 1);
+        if (to_out) {
+            // one division at the end ("9-2" §2 segment 3)
+#pragma unroll
+            for (int k = 0; k < 2 * G; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
+            store_floats<2 * G>(p.out + ((size_t)b * p.nq + h) * kHeadDim + d0, z);
+        } else {
+            const size_t idx = (size_t)rec * p.nq + h;
+            store_floats<2 * G>(p.ws_acc + idx * kHeadDim + d0, z);
+            if (c == 0 && (tslot & 1) == 0) p.ws_ms[idx] = make_float2(mr, sr);
+        }
+    };
+
+    // rounds and the chunk boundaries of a run as in attend_piece
+    int lt = lt0, rec = 2 * part + slot, cut = Runs ? lt0 + chunk : lt1;
+    for (int r = (lt1 - lt0 + D - 1) / D; r > 0; --r) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
+            if (d > 0 && lt >= lt1) continue;
             const int nxt = (d + D - 1) % D;
             load_tile_mf(p.cache, bl[nxt], lo, lane, (lt + D - 1) * kTile, ne, p.dev_status, t[nxt]);
             fetch_blocks_ahead<true>(bt, log2bs, (lt + D) * kTile, ne, bl[d]);
             process(t[d]);
-            if (++lt >= lt1) goto piece_done;
-        }
-    }
-piece_done:
-
-    float S[G], acc[G][16];
-    const float srow = row16_sum(Sl);
-#pragma unroll
-    for (int g = 0; g < G; ++g) S[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srow), 16 * g));
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[g][jj] = sum_over_slots(accm[jj][g]);
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (tslot != g) continue;
-        const int h = kh * G + g;
-        if (whole) {
-            // one division at the end ("9-2" §2 segment 3)
-            const float sg = S[g];
-            float4 *o = reinterpret_cast<float4 *>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float4 r;
-                r.x = sg > 0.0f ? acc[g][4 * q4 + 0] / sg : 0.0f;
-                r.y = sg > 0.0f ? acc[g][4 * q4 + 1] / sg : 0.0f;
-                r.z = sg > 0.0f ? acc[g][4 * q4 + 2] / sg : 0.0f;
-                r.w = sg > 0.0f ? acc[g][4 * q4 + 3] / sg : 0.0f;
-                o[q4] = r;
+            ++lt;
+            if constexpr (Runs) {
+                if (d == D - 1 && lt == cut && lt < lt1) {
+                    finish(false, rec++);
+                    fresh();
+                    cut += chunk;
+                }
             }
-        } else {
-            const size_t idx = ((size_t)part * 2 + slot) * p.nq + h;
-            float4 *a = reinterpret_cast<float4 *>(p.ws_acc + idx * kHeadDim + 16 * c);
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                a[q4] = make_float4(acc[g][4 * q4], acc[g][4 * q4 + 1], acc[g][4 * q4 + 2], acc[g][4 * q4 + 3]);
-            if (c == 0) p.ws_ms[idx] = make_float2(M[g], S[g]);
         }
     }
+    finish(whole, rec);
 }
 
-template <int G, bool Big>
+// The partial kernel of either cut: Chunked walks the invariant cut
+// (p.chunk_tiles > 0) in chunk runs, else the balanced cut or a step plan.
+static_assert(kInvariantChunkTiles % 2 == 0, "a chunk boundary must fall after a whole round of D = 2 tiles");
+
+template <int G, bool Big, bool Chunked>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
     extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
-    walk_ranges(p, lds_batch, lds_batch + p.batch + 1,
-                [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
-                    const TileBlocks *first) __attribute__((always_inline)) {
-                    // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
-                    if constexpr (G == 4 && Big)
-                        attend_piece_mf(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first);
-                    else
-                        attend_piece<G, Big>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first);
-                });
+    auto attend = [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
+                      const TileBlocks *first, int chunk) __attribute__((always_inline)) {
+        // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
+        if constexpr (G == 4 && Big)
+            attend_piece_mf<Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk);
+        else
+            attend_piece<G, Big, Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk);
+    };
+    if constexpr (Chunked)
+        walk_chunks<true>(p, lds_batch, lds_batch + p.batch + 1, attend);
+    else
+        walk_balanced(p, lds_batch, lds_batch + p.batch + 1, attend);
 }
 
 // ---------------------------------------------------------------- merge ----
@@ -657,15 +688,19 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 template <int G, bool Big>
-static const void *partial_fn() { return reinterpret_cast<const void *>(&q8_attn_partial_kernel<G, Big>); }
+static const void *partial_fn(bool chunked)
+{
+    return chunked ? reinterpret_cast<const void *>(&q8_attn_partial_kernel<G, Big, true>)
+                   : reinterpret_cast<const void *>(&q8_attn_partial_kernel<G, Big, false>);
+}
 
-static const void *partial_kernel(int group, bool big)
+static const void *partial_kernel(int group, bool big, bool chunked)
 {
     switch (group) {
-    case 1: return big ? partial_fn<1, true>() : partial_fn<1, false>();
-    case 2: return big ? partial_fn<2, true>() : partial_fn<2, false>();
-    case 4: return big ? partial_fn<4, true>() : partial_fn<4, false>();
-    default: return big ? partial_fn<8, true>() : partial_fn<8, false>();
+    case 1: return big ? partial_fn<1, true>(chunked) : partial_fn<1, false>(chunked);
+    case 2: return big ? partial_fn<2, true>(chunked) : partial_fn<2, false>(chunked);
+    case 4: return big ? partial_fn<4, true>(chunked) : partial_fn<4, false>(chunked);
+    default: return big ? partial_fn<8, true>(chunked) : partial_fn<8, false>(chunked);
     }
 }
 
@@ -675,7 +710,7 @@ static size_t partial_lds_bytes(int batch) { return (size_t)(2 * batch + 1) * si
 int decode_blocks_per_cu(int group, int waves, int batch)
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, true), waves * 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, true, false), waves * 64,
                                                      partial_lds_bytes(batch)) != hipSuccess || nb < 1)
         nb = 1;
     return nb;
@@ -805,7 +840,7 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     p.k_new = k_new;
     p.v_new = v_new;
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
-    const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile);
+    const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile, plan.chunk_tiles > 0);
     void *args[] = {&p};
     const hipError_t e = hipLaunchKernel(fn, grid, block, args, partial_lds_bytes(batch.batch), stream);
     return e != hipSuccess ? e : hipGetLastError();

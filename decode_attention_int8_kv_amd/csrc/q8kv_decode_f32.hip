@@ -201,12 +201,12 @@ template <int G>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_f32_partial_kernel(DecodeParams p)
 {
     __shared__ int pref[kMaxBatch + 1];
-    // walk_ranges calls the lambda from its planned and its unplanned walk;
-    // without always_inline the compiler makes it a real call, with a stack
-    // frame in scratch and twice the VGPRs
+    // walk_ranges calls the lambda from each of its walks (one piece per
+    // call: chunk is always 0 there); without always_inline the compiler
+    // makes it a real call, with a stack frame in scratch and twice the VGPRs
     walk_ranges(p, pref, nullptr,
                 [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
-                    const TileBlocks *) __attribute__((always_inline)) {
+                    const TileBlocks *, int) __attribute__((always_inline)) {
                     attend_piece_f32<G>(p, b, kh, lane, lt0, lt1, n, whole, part, slot);
                 });
 }

@@ -129,6 +129,58 @@ __device__ __forceinline__ float max_rows32(float v)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Sums over the 8 token slots of a wave (lane 8 s + c is slot s) of N values
+// per lane, scattered over the slots: slot s ends with the sums of values
+// [s N / 8, (s + 1) N / 8) in z.  Three halving steps, each pairing a value
+// of the kept half with one of the given-away half: the 32-lane halves
+// (v_permlane32_swap of the pair leaves, in every lane, its own kept value in
+// one result and the partner's in the other), then the 16-lane rows
+// (v_permlane16_swap), then slots s and s ^ 1, 8 lanes apart in a row (DPP
+// row rotation by 8).  N / 2 + N / 4 + N / 8 exchanges, against 3 N for a
+// full sum of every value in every lane.
+template <int N>
+__device__ __forceinline__ void slot_reduce_scatter(const float (&v)[N], float (&z)[N / 8], int lane)
+{
+    static_assert(N % 8 == 0, "eight slots");
+    float w[N / 2], u[N / 4];
+    // lanes 0-31 keep values [0, N/2), lanes 32-63 [N/2, N): the swap moves
+    // the upper lanes of its first operand and the lower lanes of its second
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + N / 2]),
+                                                        false, false);
+        w[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // even rows of a half keep [0, N/4), odd rows [N/4, N/2): the swap moves
+    // the odd rows of its first operand and the even rows of its second
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[k]), __float_as_uint(w[k + N / 4]),
+                                                        false, false);
+        u[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // even slots keep [0, N/8), odd slots [N/8, N/4)
+    const bool odd = (lane >> 3) & 1;
+#pragma unroll
+    for (int k = 0; k < N / 8; ++k) {
+        const float keep = odd ? u[k + N / 8] : u[k], give = odd ? u[k] : u[k + N / 8];
+        z[k] = keep + dpp_f<kDppRor8>(give);
+    }
+}
+
+// P consecutive floats to dst (P = 2, 4, 8 or 16; dst aligned to 4 P bytes).
+template <int P>
+__device__ __forceinline__ void store_floats(float *dst, const float (&x)[P])
+{
+    if constexpr (P == 2) {
+        *reinterpret_cast<float2 *>(dst) = make_float2(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < P / 4; ++i)
+            reinterpret_cast<float4 *>(dst)[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    }
+}
+
 // Sum / max over the 8 token slots of a wave (lanes that share lane % 8).
 __device__ __forceinline__ float sum_over_slots(float v)
 {

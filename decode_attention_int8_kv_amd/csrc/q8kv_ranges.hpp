@@ -134,7 +134,7 @@ __device__ __forceinline__ void planned_first_blocks(const TileBlocks &raw, int 
     for (int kk = 0; kk < 4; ++kk) b.id[kk] = (t0 + kSub * kk < ne) ? raw.id[BigBlocks ? 0 : kk] : -1;
 }
 
-// walk_ranges over a step plan: the same pieces, appends and zeroed rows,
+// walk_balanced over a step plan: the same pieces, appends and zeroed rows,
 // read from the plan (every piece's fields with scalar loads) instead of
 // found by a length scan and lookups.  A plan made for another batch size,
 // partition count, block size, cost or length bound sets Q8_DEV_BAD_PLAN
@@ -161,7 +161,7 @@ __device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend
     if (p.k_new && kh < p.cache.nkv) {
         // fused append: the newest token of every sequence whose last tile
         // lies in this range, before any tile is loaded (ordering as in
-        // walk_ranges); four rows' loads in flight at a time
+        // walk_balanced); four rows' loads in flight at a time
         bool wrote = false;
         for (int j0 = r0; j0 < r1; j0 += 4) {
             float2 k[4], v[4];
@@ -206,7 +206,7 @@ __device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend
             TileBlocks first;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) first.id[kk] = pc[kPfFirstBlk + kk];
-            attend(b, kh, lane, lt0, lt1, n, (fl & kPieceWhole) != 0, part, (fl & kPieceSlot1) ? 1 : 0, &first);
+            attend(b, kh, lane, lt0, lt1, n, (fl & kPieceWhole) != 0, part, (fl & kPieceSlot1) ? 1 : 0, &first, 0);
         }
     }
 
@@ -221,7 +221,7 @@ __device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend
     }
 }
 
-// Fused append of walk_ranges / walk_chunks: the new token of every
+// Fused append of walk_balanced / walk_chunks: the new token of every
 // sequence b >= lo with owns(b), for this wave's KV head kh, before the wave
 // loads any tile; groups of 64 sequences from lo until past(first of the
 // group).  The owning range is the one whose wave reads the token's tile, so
@@ -303,18 +303,24 @@ __device__ __forceinline__ void zero_empty_rows(const DecodeParams &p, const int
 
 // The batch-invariant walk (p.chunk_tiles > 0): every sequence is cut into
 // chunks of chunk_tiles_of(its tiles, chunk_tiles) tiles counted from its own
-// start, and a range takes
-// the chunks whose first tile lies in it (units [start, end) of the tile
-// prefix, which here charges no units per sequence).  Each chunk is walked as
-// a piece of its own: a sequence of one chunk is finished in place, the
-// chunks of a longer one leave their states in records b * max_chunks + c,
-// which the merge kernel combines in chunk order.  Nothing of this depends on
-// the other sequences or the partition count, so neither do the bits.  The
-// fused append is done by the range that walks the sequence's last chunk.
-template <class Attend>
-__device__ __forceinline__ void walk_chunks(const DecodeParams &p, int *pref, int *lens, int part, int hg, int kh,
-                                            int lane, Attend &&attend)
+// start, and a range takes the chunks whose first tile lies in it (units
+// [start, end) of the tile prefix, which here charges no units per
+// sequence).  Every chunk is attended with a fresh state: a sequence of one
+// chunk is finished in place, the chunks of a longer one leave their states
+// in records b * max_chunks + c, which the merge kernel combines in chunk
+// order.  Nothing of this depends on the other sequences or the partition
+// count, so neither do the bits.  The fused append is done by the range that
+// walks the sequence's last chunk.  With Runs, a range's consecutive chunks
+// of one sequence go to one attend call with chunk = their length in tiles
+// (the callee restarts its state at every chunk boundary but keeps its loads
+// in flight across it); without, one call per chunk with chunk = 0.
+template <bool Runs, class Attend>
+__device__ __forceinline__ void walk_chunks(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
 {
+    const int part = blockIdx.x / p.head_groups;
+    const int hg = blockIdx.x - part * p.head_groups;
+    const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int kh = hg * (int)(blockDim.x >> 6) + wave;
     build_prefix(p, pref, lens, blockIdx.x == 0);
     const int total = pref[p.batch];
     const int start = part_start(part, total, p.nparts);
@@ -346,10 +352,21 @@ __device__ __forceinline__ void walk_chunks(const DecodeParams &p, int *pref, in
             const int L = chunk_tiles_of(tiles, p.chunk_tiles);
             const int nch = (tiles + L - 1) / L;
             const int n = uniform(lens ? lens[b] : p.seq_lens[b]);
-            for (int c = a0 >= start ? 0 : (start - a0 + L - 1) / L; c < nch && a0 + c * L < end; ++c) {
-                const int rec = b * p.max_chunks + c;
-                attend(b, kh, lane, c * L, min(tiles, (c + 1) * L), n, nch == 1, rec >> 1, rec & 1,
-                       static_cast<const TileBlocks *>(nullptr));
+            // chunks [c0, c1) start in [start, end) (a0 < end)
+            const int c0 = a0 >= start ? 0 : (start - a0 + L - 1) / L;
+            const int c1 = min(nch, (end - a0 + L - 1) / L);
+            if constexpr (Runs) {
+                if (c0 < c1) {
+                    const int rec = b * p.max_chunks + c0;
+                    attend(b, kh, lane, c0 * L, min(tiles, c1 * L), n, nch == 1, rec >> 1, rec & 1,
+                           static_cast<const TileBlocks *>(nullptr), L);
+                }
+            } else {
+                for (int c = c0; c < c1; ++c) {
+                    const int rec = b * p.max_chunks + c;
+                    attend(b, kh, lane, c * L, min(tiles, (c + 1) * L), n, nch == 1, rec >> 1, rec & 1,
+                           static_cast<const TileBlocks *>(nullptr), 0);
+                }
             }
         }
     }
@@ -357,19 +374,20 @@ __device__ __forceinline__ void walk_chunks(const DecodeParams &p, int *pref, in
     if (hg == 0) zero_empty_rows(p, pref, part, start, end, lane);
 }
 
-// The whole job of one workgroup of a partial kernel: range blockIdx.x /
-// head_groups, KV heads hg * waves + wave.  attend(b, kh, lane, lt0, lt1, n,
-// whole, part, slot, first) runs one wave over tiles [lt0, lt1) of sequence b
-// (length n); `whole` says the piece is the whole sequence, else its state
-// goes to slot `slot` (0: first piece of the range, 1: later) of record
-// `part`; `first` holds the raw block ids of the first tile (from a step
-// plan), or is null.  Afterwards the output rows of empty sequences whose
+// The whole job of one workgroup of a partial kernel under the balanced cut:
+// range blockIdx.x / head_groups, KV heads hg * waves + wave.  attend(b, kh,
+// lane, lt0, lt1, n, whole, part, slot, first, chunk) runs one wave over
+// tiles [lt0, lt1) of sequence b (length n); `whole` says the piece is the
+// whole sequence, else its state goes to slot `slot` (0: first piece of the
+// range, 1: later) of record `part`; `first` holds the raw block ids of the
+// first tile (from a step plan), or is null; chunk is 0 (walk_chunks passes
+// its chunk length).  Afterwards the output rows of empty sequences whose
 // tile position falls in this range are zeroed (the last range also takes
 // those at the very end).  With p.k_new set, `lens` (LDS, batch entries) is
 // required and the range's new tokens are appended first.  With a step plan
 // (p.plan) the same work is read from it (walk_plan).
 template <class Attend>
-__device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
+__device__ __forceinline__ void walk_balanced(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
 {
     if (p.plan) {
         walk_plan(p, attend);
@@ -379,10 +397,6 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int kh = hg * (int)(blockDim.x >> 6) + wave;
-    if (p.chunk_tiles > 0) {
-        walk_chunks(p, pref, lens, part, hg, kh, lane, attend);
-        return;
-    }
 
     build_prefix(p, pref, lens, blockIdx.x == 0);
     if (blockIdx.x == 0)
@@ -420,13 +434,24 @@ __device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, in
                 const int slot = (start >= a0) ? 0 : 1;
                 int n = lens ? lens[b] : p.seq_lens[b];
                 n = uniform(n);
-                attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot, static_cast<const TileBlocks *>(nullptr));
+                attend(b, kh, lane, x0 - f, x1 - f, n, whole, part, slot, static_cast<const TileBlocks *>(nullptr), 0);
             }
             x = x1;
         }
     }
 
     if (hg == 0) zero_empty_rows(p, pref, part, start, end, lane);
+}
+
+// Either cut, chosen at run time from p.chunk_tiles (one attend call per
+// chunk under the invariant cut).
+template <class Attend>
+__device__ __forceinline__ void walk_ranges(const DecodeParams &p, int *pref, int *lens, Attend &&attend)
+{
+    if (p.chunk_tiles > 0)
+        walk_chunks<false>(p, pref, lens, attend);
+    else
+        walk_balanced(p, pref, lens, attend);
 }
 
 // Host: the kernel arguments of one decode call.

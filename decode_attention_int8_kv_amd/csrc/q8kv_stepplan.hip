@@ -17,7 +17,7 @@ namespace q8kv {
 
 constexpr int kPlanThreads = 1024;
 
-// Pieces of range i, in walk order (the loop of walk_ranges); emit(b, x0, x1,
+// Pieces of range i, in walk order (the loop of walk_balanced); emit(b, x0, x1,
 // f, e0, slot) for each.  pref: the cut-axis prefix (LDS).
 template <class Emit>
 __device__ __forceinline__ void range_pieces(const int *pref, int batch, int cost, int start, int end, Emit &&emit)
