@@ -13,7 +13,7 @@
 // GPU organisation (gfx950, wave64):
 //   * The batch's tiles (32 tokens of one sequence) are laid end to end and
 //     cut into `nparts` equal contiguous ranges; one workgroup per range (and
-//     per group of 8 KV heads) walks its range.  Each KV head is one wave, so
+//     per group of up to 8 KV heads) walks its range.  Each KV head is one wave, so
 //     the K/V rows of a head are read once for all of its G = nq/nkv query
 //     heads, and a workgroup's waves together read whole token rows.
 //   * Per tile the rescale is applied once with the tile's max (the online
@@ -24,6 +24,7 @@
 //   * A sequence cut by a range boundary leaves (M, S, acc) partial states
 //     in the workspace; the merge kernel combines them with the same rescale
 //     rule and divides once.  A sequence inside one range is finished in place.
+#include <atomic>
 #include "q8kv_ranges.hpp"
 
 namespace q8kv {
@@ -716,30 +717,59 @@ int decode_blocks_per_cu(int group, int waves, int batch)
     return nb;
 }
 
-// Workgroup width (KV heads per workgroup): one workgroup per token range for
-// up to 8 KV heads, else the heads split evenly over the fewest workgroups.
-// The waves of a workgroup then read whole 1 KB token rows together; on the
-// ragged 2B batch this measured the same time as two 4-wave workgroups with
-// three resident per CU, with half the workgroups to set up.
-static void choose_width(int nkv, int group, int &waves, int &head_groups)
+// Waves per SIMD that the partial kernel for (group, block size, cut) can
+// hold (its registers decide): the resident 4-wave workgroups per CU, one
+// wave per SIMD each.  Cached per device.
+static int partial_waves_per_simd(int group, bool big, bool chunked)
 {
-    (void)group;
-    head_groups = (nkv + kMaxWavesPerWG - 1) / kMaxWavesPerWG;
-    waves = (nkv + head_groups - 1) / head_groups;
+    static std::atomic<int> cache[kMaxDevices][4][2][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+    const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    if (dev >= 0) {
+        const int v = cache[dev][gi][big][chunked].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, partial_kernel(group, big, chunked), 256, 0) != hipSuccess ||
+        nb < 1)
+        nb = 1;
+    if (dev >= 0) cache[dev][gi][big][chunked].store(nb, std::memory_order_relaxed);
+    return nb;
 }
 
+// Workgroup width (KV heads per workgroup, one wave each): at most 8, and at
+// most 4 where the kernel holds three or more waves per SIMD (G <= 2 with
+// blocks of 32 positions or more).  The narrow workgroups spread a range's KV
+// heads over two CUs' worth of slots: A-B-B-A on one box, ragged 2B batch
+// 105.4 -> 101.8-102.3 us per layer-step at 256 ranges (384 ranges: 102.4-102.6,
+// 512: 103.8), 2B batch 1 at n = 4059 12.6 -> 11.2 us; at two waves per SIMD
+// (G = 4) they were slower (stress batch 102.8 -> 106.7 us).
+static void choose_width(const q8_kv_layer &layer, int group, bool chunked, int &waves, int &head_groups)
+{
+    const int maxw =
+        partial_waves_per_simd(group, layer.kv_bs >= kTile, chunked) >= 3 ? kMaxWavesPerWG / 2 : kMaxWavesPerWG;
+    head_groups = (layer.nkv_heads + maxw - 1) / maxw;
+    waves = (layer.nkv_heads + head_groups - 1) / head_groups;
+}
+
+// One range per CU for every whole multiple of the batch's KV heads that the
+// CU's resident waves cover (at least one; fewer ranges than CUs when a
+// range's heads take more than a CU), at most one per tile.
 int auto_parts(const q8_kv_layer &layer, const q8_batch &batch, int nq)
 {
+    const int group = nq / layer.nkv_heads;
     int waves, head_groups;
-    choose_width(layer.nkv_heads, nq / layer.nkv_heads, waves, head_groups);
+    choose_width(layer, group, (batch.flags & Q8_BATCH_INVARIANT) != 0, waves, head_groups);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
             cus = v;
     }
-    const long long slots = (long long)cus * decode_blocks_per_cu(nq / layer.nkv_heads, waves, batch.batch) /
-                            head_groups;
+    const long long resident = (long long)decode_blocks_per_cu(group, waves, batch.batch) * waves;   // per CU
+    const long long slots = resident >= layer.nkv_heads ? (long long)cus * (resident / layer.nkv_heads)
+                                                        : (long long)cus * resident / layer.nkv_heads;
     const long long tiles_ub = (long long)batch.batch * ((batch.max_seq_len + kTile - 1) / kTile);
     long long parts = slots < tiles_ub ? slots : tiles_ub;
     if (parts < 1) parts = 1;
@@ -751,7 +781,7 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     DecodePlan pl;
     pl.nparts = nparts > 0 ? nparts : auto_parts(layer, batch, nq);
     pl.piece_cost = kPieceCost;
-    choose_width(layer.nkv_heads, nq / layer.nkv_heads, pl.waves, pl.head_groups);
+    choose_width(layer, nq / layer.nkv_heads, (batch.flags & Q8_BATCH_INVARIANT) != 0, pl.waves, pl.head_groups);
     // merge: few (sequence, query head) rows get each row's dims split over
     // up to four workgroups, so a small batch still spreads its merge over
     // many CUs; waves: enough that a sequence cut into about twice the average

@@ -45,6 +45,9 @@ hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int n
 hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, int nq, float *out,
                                const DecodePlan &plan, void *workspace, hipStream_t stream);
 
+// Devices a process's per-device tables cover (device ordinals 0 .. 63).
+constexpr int kMaxDevices = 64;
+
 // Resident workgroups per CU of the decode kernel for this group size.
 int decode_blocks_per_cu(int group, int waves, int batch);
 

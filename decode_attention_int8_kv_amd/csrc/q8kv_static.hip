@@ -16,7 +16,6 @@
 namespace q8kv {
 
 constexpr size_t kScratchBytes = 16u << 20;   // 16 MiB per device
-constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
