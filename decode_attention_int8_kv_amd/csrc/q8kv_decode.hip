@@ -499,8 +499,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
 
 // ---------------------------------------------------------------- merge ----
 struct MergeParams {
-    const int32_t *plan;        // the step plan whose prefix ws_prefix points into, or null
-    const int32_t *ws_prefix;
+    const int32_t *ws_prefix;   // [batch + 1] cut-axis prefix (a negative total: no records)
     const float2 *ws_ms;
     const float *ws_acc;
     float *out;
@@ -576,11 +575,6 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     constexpr int kLanesPerPiece = 64 / Slices;   // 64, 32, 16
     const int row = blockIdx.x / Slices, sl = blockIdx.x - row * Slices;
     const int b = row / p.nq, h = row - b * p.nq;
-    // a plan made for another cut (the partial kernel refused it and wrote no
-    // records) or cut short: its prefix is not this call's
-    if (p.plan && !(p.plan[kPhMagic] == kPlanMagic && p.plan[kPhBatch] == p.batch && p.plan[kPhParts] == p.nparts &&
-                    p.plan[kPhPieceCost] == p.piece_cost))
-        return;
     int np, i0 = 0, slot0 = 0, total = 0;
     bool may_be_empty = false;
     if (p.chunk_tiles > 0) {
@@ -594,7 +588,9 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void q8_attn_merge_kernel(Merg
     } else {
         const int a0 = p.ws_prefix[b], e0 = p.ws_prefix[b + 1];
         total = p.ws_prefix[p.batch];
-        if (e0 == a0) return;
+        // a negative total: the partial kernel refused its step plan (made for
+        // another cut) and wrote no records
+        if (e0 == a0 || total < 0) return;
         // ranges of the first and the last tile (before the first tile of a
         // sequence other than 0 lie piece_cost units that hold none)
         const int first = a0 + (b > 0 ? p.piece_cost : 0);
@@ -883,10 +879,9 @@ hipError_t launch_decode_merge(const q8_kv_layer &layer, const q8_batch &batch, 
     if (plan.nparts <= 1 && plan.chunk_tiles == 0) return hipSuccess;
     MergeParams p;
     char *ws = static_cast<char *>(workspace);
-    // the cut-axis prefix: written by the partial kernel, or the step plan's
-    p.plan = static_cast<const int32_t *>(batch.plan);
-    p.ws_prefix = batch.plan ? p.plan + step_plan_layout(batch.batch, plan.nparts).pref
-                             : reinterpret_cast<const int32_t *>(ws + plan.off_prefix);
+    // the cut-axis prefix, which the partial kernel wrote to the workspace
+    // (from its own scan, or copied from the step plan)
+    p.ws_prefix = reinterpret_cast<const int32_t *>(ws + plan.off_prefix);
     p.ws_ms = reinterpret_cast<const float2 *>(ws + plan.off_ms);
     p.ws_acc = reinterpret_cast<const float *>(ws + plan.off_acc);
     p.out = out;

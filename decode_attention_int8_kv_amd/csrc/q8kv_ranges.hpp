@@ -147,14 +147,21 @@ __device__ __forceinline__ void walk_plan(const DecodeParams &p, Attend &&attend
     const int hg = blockIdx.x - part * p.head_groups;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int kh = hg * (int)(blockDim.x >> 6) + wave;
-    const bool ok = pl[kPhMagic] == kPlanMagic && pl[kPhBatch] == p.batch && pl[kPhParts] == p.nparts &&
-                    pl[kPhKvBsLog2] == p.cache.kv_bs_log2 && pl[kPhPieceCost] == p.piece_cost &&
-                    pl[kPhMaxSeqLen] == p.max_seq_len;
+    // the header's fields in one round of loads (no short-circuit between them)
+    const bool ok = (pl[kPhMagic] == kPlanMagic) & (pl[kPhBatch] == p.batch) & (pl[kPhParts] == p.nparts) &
+                    (pl[kPhKvBsLog2] == p.cache.kv_bs_log2) & (pl[kPhPieceCost] == p.piece_cost) &
+                    (pl[kPhMaxSeqLen] == p.max_seq_len);
     if (!ok) {
         if (threadIdx.x == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadPlan);
+        // the merge reads a negative total as "no records"
+        if (blockIdx.x == 0 && threadIdx.x == 0 && p.ws_prefix) p.ws_prefix[p.batch] = -1;
         return;
     }
     const StepPlanLayout L = step_plan_layout(p.batch, p.nparts);
+    // the plan's cut-axis prefix to the workspace, where the merge reads it
+    // (one entry per workgroup, so no workgroup's start waits on more)
+    if (p.ws_prefix && threadIdx.x == 0)
+        for (int b = blockIdx.x; b <= p.batch; b += gridDim.x) p.ws_prefix[b] = pl[L.pref + b];
     const int r0 = pl[L.range + part], r1 = pl[L.range + part + 1];
     const int bs_mask = (1 << p.cache.kv_bs_log2) - 1;
 

@@ -213,10 +213,13 @@ def test_heavy_tails_and_guard_rows():
     say(f"  worst err/tol {w:.3f}")
 
 
-def test_many_kv_heads():
-    # 12 KV heads: two workgroups per range, the second one partly idle
-    say("[decode] nkv=12")
-    w = _decode_case([300, 45, 1], 24, 12, 32, seed=12, nparts_list=[0, 4])
+@pytest.mark.parametrize("nq,nkv", [(24, 12), (20, 10), (40, 10)])
+def test_many_kv_heads(nq, nkv):
+    # more KV heads than one workgroup takes: at G = 2 workgroups of 4 waves
+    # (12 heads: three per range; 10 heads: three, two waves of the last one
+    # idle), at G = 4 of up to 8 (10 heads: two workgroups of 5 waves)
+    say(f"[decode] nq={nq} nkv={nkv}")
+    w = _decode_case([300, 45, 1], nq, nkv, 32, seed=nq + nkv, nparts_list=[0, 4])
     say(f"  worst err/tol {w:.3f}")
 
 
