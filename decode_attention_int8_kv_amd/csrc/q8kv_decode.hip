@@ -800,13 +800,7 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
         pl.piece_cost = 0;
         pl.chunk_tiles = kInvariantChunkTiles;
         // the most chunks a sequence of at most max_seq_len positions has
-        const int tiles_ub = (batch.max_seq_len + kTile - 1) / kTile;
-        const int short_ub = tiles_ub < 64 * kInvariantChunkTiles ? tiles_ub : 64 * kInvariantChunkTiles - 1;
-        const int long_chunks = tiles_ub >= 64 * kInvariantChunkTiles
-                                    ? (tiles_ub + 2 * kInvariantChunkTiles - 1) / (2 * kInvariantChunkTiles) : 0;
-        const int short_chunks = (short_ub + kInvariantChunkTiles - 1) / kInvariantChunkTiles;
-        pl.max_chunks = long_chunks > short_chunks ? long_chunks : short_chunks;
-        if (pl.max_chunks < 1) pl.max_chunks = 1;
+        pl.max_chunks = max_chunks_of((batch.max_seq_len + kTile - 1) / kTile, kInvariantChunkTiles);
         pl.merge_slices = 1;
         pl.merge_waves = 4;
         records = (size_t)batch.batch * pl.max_chunks;

@@ -30,18 +30,40 @@ constexpr int kPieceCost = 2;
 
 // The batch-invariant cut (Q8_BATCH_INVARIANT): chunks of this many 32-token
 // tiles counted from each sequence's start (Q8_INVARIANT_CHUNK_TOKENS
-// positions); about four chunks per range on a batched step keep the ranges'
-// work within a chunk of each other.  A sequence of 64 chunks or more uses
-// chunks twice as long (chunk_tiles_of): half the chunk starts and records
-// where they cost most, and still at least 32 chunks to spread.
-constexpr int kInvariantChunkTiles = 8;
+// positions) for sequences under 32 such chunks, twice as long up to 128 and
+// four times as long beyond (chunk_tiles_of).  Short chunks spread a short
+// sequence over many ranges (its latency at batch 1); long sequences get
+// longer chunks, whose fewer starts, flushes and records cost less on a full
+// batch, and still at least 32 of them.
+constexpr int kInvariantChunkTiles = 4;
 
 // Tiles per chunk of a sequence of `tiles` tiles under the batch-invariant
 // cut with base chunk length `base` (a function of the sequence's own length
 // only).
+// Chunks of the base length up to kChunkBand1 chunks' worth of tiles, then
+// twice as long up to kChunkBand2 base chunks' worth, then four times.
+constexpr int kChunkBand1 = 32, kChunkBand2 = 128;
 __host__ __device__ inline int chunk_tiles_of(int tiles, int base)
 {
-    return tiles >= 64 * base ? 2 * base : base;
+    return tiles >= kChunkBand2 * base ? 4 * base : tiles >= kChunkBand1 * base ? 2 * base : base;
+}
+
+// The most chunks a sequence of at most tiles_ub tiles has (the count grows
+// with the length inside each band and drops where the chunk length doubles,
+// so it is the largest of the bands' tops).
+__host__ __device__ inline int max_chunks_of(int tiles_ub, int base)
+{
+    auto ceil_div = [](int a, int b) { return (a + b - 1) / b; };
+    int m = ceil_div(tiles_ub < kChunkBand1 * base ? tiles_ub : kChunkBand1 * base - 1, base);
+    if (tiles_ub >= kChunkBand1 * base) {
+        const int c = ceil_div(tiles_ub < kChunkBand2 * base ? tiles_ub : kChunkBand2 * base - 1, 2 * base);
+        m = c > m ? c : m;
+    }
+    if (tiles_ub >= kChunkBand2 * base) {
+        const int c = ceil_div(tiles_ub, 4 * base);
+        m = c > m ? c : m;
+    }
+    return m > 1 ? m : 1;
 }
 
 DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, int nparts);

@@ -109,8 +109,9 @@ typedef struct q8_kv_layer {
  * arrays changed is not -- make a new plan whenever they change.
  * flags: 0, or Q8_BATCH_INVARIANT: the decode entry points then cut every
  * sequence into chunks of Q8_INVARIANT_CHUNK_TOKENS positions counted from its
- * start (twice that for a sequence of 64 such chunks or more; the last chunk
- * shorter), give every chunk its own partial state and
+ * start (twice that for a sequence of 4096 positions or more, four times for
+ * 16384 or more; the last chunk shorter), give every chunk its own partial
+ * state and
  * combine a sequence's chunk states in chunk order with a fixed association
  * -- the online-softmax rescale rule of "9-2 flash_attn_single_q_q8_neon"
  * §2 segment 2 applied to partial states, one division at the end -- so a
@@ -118,10 +119,10 @@ typedef struct q8_kv_layer {
  * not on the other sequences of the batch, their order, the partition count
  * or the placement of its blocks.  Chunks are shared out over the ranges by
  * their first position, which balances the work less evenly than the default
- * cut.  The workspace holds up to batch * ceil(max_seq_len / 256) records per
- * query head.  Such a batch carries no step plan (Q8_EINVAL). */
+ * cut.  The workspace holds up to batch * max(64, ceil(max_seq_len / 512))
+ * records per query head.  Such a batch carries no step plan (Q8_EINVAL). */
 #define Q8_BATCH_INVARIANT 0x1
-#define Q8_INVARIANT_CHUNK_TOKENS 256
+#define Q8_INVARIANT_CHUNK_TOKENS 128
 typedef struct q8_batch {
     int32_t batch;
     int32_t max_blocks_per_seq;

@@ -331,9 +331,32 @@ def test_batch_flags_and_the_invariant_cut(q8):
     assert call_decode(q8, L, batch(q8, invariant=True, plan=FAKE)) == -1
     assert lib.q8_decode_plan_bytes(ctypes.byref(L.c()), ctypes.byref(inv.c()), 16, 0) == 0
     assert lib.q8_decode_plan(ctypes.byref(L.c()), ctypes.byref(inv.c()), 16, 0, FAKE, 1 << 20, None, None) == -1
-    # one record per chunk of 256 positions per sequence and query head, for any partition count
+    # one record per chunk per sequence and query head, for any partition count
     for nparts in (0, 1, 4, 1000):
         need = q8.decode_attn_workspace_bytes(L, inv, 16, nparts)
-        chunks = 4 * ((300 + 255) // 256)
+        chunks = 4 * ((300 + 127) // 128)
         assert need >= chunks * 16 * (128 + 2) * 4
         assert call_decode(q8, L, inv, ws_bytes=need - 1, nparts=nparts) == -3
+
+
+def _invariant_chunks(n):
+    # the header's rule: chunks of 128 positions, 256 from 4096 positions on,
+    # 512 from 16384 on (the last chunk shorter)
+    tiles = (n + 31) // 32
+    length = 512 if n >= 16384 else 256 if n >= 4096 else 128
+    return (tiles * 32 + length - 1) // length if tiles else 0
+
+
+@pytest.mark.parametrize("max_seq_len", [1, 127, 128, 4064, 4095, 4096, 4097, 8191, 16352, 16383, 16384,
+                                         40000, 1 << 20])
+def test_invariant_workspace_holds_the_most_chunks_a_length_has(q8, max_seq_len):
+    # the workspace's record count is the largest chunk count of any length up
+    # to max_seq_len (at the top of a band of the rule, just below a doubling
+    # of the chunk length, a shorter sequence can have more chunks)
+    most = max(_invariant_chunks(n) for n in range(0, max_seq_len + 1, 1 if max_seq_len < 70000 else 32))
+    if max_seq_len >= 70000:
+        most = max(most, _invariant_chunks(max_seq_len))
+    inv = batch(q8, invariant=True, max_seq_len=max_seq_len, max_blocks_per_seq=(max_seq_len + 31) // 32)
+    need = q8.decode_attn_workspace_bytes(layer(q8), inv, 16, 0)
+    payload = 4 * max(most, 1) * 16 * (128 + 2) * 4
+    assert payload <= need <= payload + 2 * 256 + 4 * 5

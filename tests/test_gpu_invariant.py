@@ -1,9 +1,10 @@
 """GPU tests of the batch-invariant cut (q8_batch.flags = Q8_BATCH_INVARIANT),
 through the C ABI.
 
-Every sequence is cut into chunks of 256 positions counted from its own
-start, each chunk leaves its own partial state, and the chunk states of a
-sequence are combined in chunk order by a merge whose shape is fixed.  So a
+Every sequence is cut into chunks counted from its own start (128 positions,
+256 from 4096 positions on, 512 from 16384 on), each chunk leaves its own
+partial state, and the chunk states of a sequence are combined in chunk order
+by a merge whose shape is fixed.  So a
 sequence's output bits may depend on nothing but its own length, K, V and q:
 the same sequence decoded alone, inside a larger batch, in another order, with
 another partition count or with its blocks elsewhere in the pool gives the
@@ -190,11 +191,13 @@ def test_invariant_graph_replays_match_eager():
     assert dc.status_word() == 0
 
 
-def test_long_sequences_use_longer_chunks_and_stay_invariant():
-    # 511 tiles (64 chunks of 256 positions), 512 tiles and more (chunks of
-    # 512 positions): the chunk length follows the sequence's own length only
-    say("[invariant] chunk length threshold")
-    lens = np.array([16352, 16384, 17000, 300], np.int32)
+@pytest.mark.parametrize("lens", [[4064, 4096, 4097, 300], [16352, 16384, 17000, 300]])
+def test_long_sequences_use_longer_chunks_and_stay_invariant(lens):
+    # either side of each doubling of the chunk length (127 / 128 / 129 tiles:
+    # 128 -> 256 positions; 511 / 512 / 532 tiles: 256 -> 512 positions): the
+    # chunk length follows the sequence's own length only
+    say(f"[invariant] chunk length thresholds {lens}")
+    lens = np.array(lens, np.int32)
     k, v = dense_kv(lens, 2, seed=2600)
     q = np.random.default_rng(2601).standard_normal((lens.size, 4, 128)).astype(np.float32)
     dc = _cache(lens, 2, 32, k, v, seed=37)
