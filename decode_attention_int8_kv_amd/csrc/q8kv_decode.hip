@@ -45,7 +45,7 @@ template <int G> struct PipeDepth { static constexpr int value = 2; };
 template <int G, bool Big, bool Runs>
 __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
                                              int lt0, int lt1, int n, bool whole, int part,
-                                             int slot, const TileBlocks *first, int chunk)
+                                             int slot, const TileBlocks *first, int chunk, float *runbuf)
 {
     const int c = lane & 7, tslot = lane >> 3;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
@@ -209,13 +209,13 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
         }
     };
 
-    // The state (M, S, acc) to the output rows or to record `rec`.  The 16 G
-    // accumulators of every lane are summed over the token slots scattered
-    // (slot_reduce_scatter): token slot s ends with 2 G consecutive dims of
-    // head s G / 8, which its 8 lanes write.
-    auto finish = [&](bool to_out, int rec) {
-        constexpr int N = 16 * G, P = N / 8;
-        float v[N];
+    // The state's sums over the token slots, scattered (slot_reduce_scatter):
+    // token slot s ends with 2 G consecutive dims of head s G / 8, which its 8
+    // lanes hold in z, with the head's M and S.
+    constexpr int P = 2 * G;
+    const int gh = (tslot * G) >> 3, j0 = (tslot * P) & 15, h = kh * G + gh;
+    auto sums = [&](float (&z)[P], float &mr, float &sr) {
+        float v[16 * G];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -225,27 +225,58 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
                 else
                     v[16 * g + j] = acc[g][j];
             }
-        float z[P];
-        slot_reduce_scatter<N>(v, z, lane);
-        const int gh = (tslot * G) >> 3, j0 = (tslot * P) & 15;
-        float sr = 0.0f, mr = 0.0f;
+        slot_reduce_scatter<16 * G>(v, z, lane);
+        sr = 0.0f;
+        mr = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float sg = sum_over_slots(S[g]);
             sr = gh == g ? sg : sr;
             mr = gh == g ? M[g] : mr;
         }
-        const int h = kh * G + gh;
+    };
+    auto write_rec = [&](int rec, const float (&z)[P], float mr, float sr) {
+        const size_t idx = (size_t)rec * p.nq + h;
+        store_floats<P>(p.ws_acc + idx * kHeadDim + 16 * c + j0, z);
+        if (c == 0 && j0 == 0) p.ws_ms[idx] = make_float2(mr, sr);
+    };
+    // the state to the output rows or to record `rec`
+    auto finish = [&](bool to_out, int rec) {
+        float z[P], mr, sr;
+        sums(z, mr, sr);
         if (to_out) {
             // one division at the end ("9-2" §2 segment 3)
 #pragma unroll
             for (int k = 0; k < P; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
             store_floats<P>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c + j0, z);
         } else {
-            const size_t idx = (size_t)rec * p.nq + h;
-            store_floats<P>(p.ws_acc + idx * kHeadDim + 16 * c + j0, z);
-            if (c == 0 && j0 == 0) p.ws_ms[idx] = make_float2(mr, sr);
+            write_rec(rec, z, mr, sr);
         }
+    };
+    // A run's chunk records wait in LDS (lane-private slots of runbuf,
+    // p.run_slots of them) and are written out when the slots are full or the
+    // run ends: stores issued between the tile loads would hold up every later
+    // tile wait, the vector memory counter being in order.
+    int held = 0, held_rec = 0;
+    auto drain = [&]() {
+        for (int i = 0; i < held; ++i) {
+            float z[P];
+#pragma unroll
+            for (int k = 0; k < P; ++k) z[k] = runbuf[(i * (P + 2) + k) * 64 + lane];
+            write_rec(held_rec + i, z, runbuf[(i * (P + 2) + P) * 64 + lane], runbuf[(i * (P + 2) + P + 1) * 64 + lane]);
+        }
+        held = 0;
+    };
+    auto hold = [&](int rec) {
+        float z[P], mr, sr;
+        sums(z, mr, sr);
+        if (held == p.run_slots) drain();
+        if (held == 0) held_rec = rec;
+#pragma unroll
+        for (int k = 0; k < P; ++k) runbuf[(held * (P + 2) + k) * 64 + lane] = z[k];
+        runbuf[(held * (P + 2) + P) * 64 + lane] = mr;
+        runbuf[(held * (P + 2) + P + 1) * 64 + lane] = sr;
+        ++held;
     };
 
     // D register tiles (the first D - 1 loaded above): while tile i is
@@ -271,7 +302,10 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
             ++lt;
             if constexpr (Runs) {
                 if (d == D - 1 && lt == cut && lt < lt1) {   // a chunk of the run ends
-                    finish(false, rec++);
+                    if (p.run_slots > 0)
+                        hold(rec++);
+                    else
+                        finish(false, rec++);
                     fresh();
                     cut += chunk;
                 }
@@ -279,6 +313,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
         }
     }
     finish(whole, rec);
+    if constexpr (Runs) drain();
 }
 
 // Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores
@@ -310,7 +345,7 @@ __device__ __forceinline__ float row16_sum(float v)
 template <bool Runs>
 __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, int kh, int lane, int lt0, int lt1,
                                                 int n, bool whole, int part, int slot, const TileBlocks *first,
-                                                int chunk)
+                                                int chunk, float *runbuf)
 {
     constexpr int G = 4;
     const int c = lane & 7, tslot = lane >> 3;
@@ -426,30 +461,60 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         (void)m2;
     };
 
-    // the state to the output rows or to record `rec`, summed over the token
-    // slots scattered (as in attend_piece): slot s holds dims 8 (s & 1) + k of
-    // head s / 2 = lg, whose sum row16_sum(Sl) gives in the same lanes
-    auto finish = [&](bool to_out, int rec) {
+    // the state's sums over the token slots, scattered (as in attend_piece):
+    // slot s holds dims 8 (s & 1) + k of head s / 2 = lg, whose sum
+    // row16_sum(Sl) gives in the same lanes
+    constexpr int P = 2 * G;
+    const int h = kh * G + lg, d0 = 16 * c + 8 * (tslot & 1);
+    auto sums = [&](float (&z)[P], float &mr, float &sr) {
         float v[16 * G];
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) v[16 * g + jj] = accm[jj][g];
-        float z[2 * G];
         slot_reduce_scatter<16 * G>(v, z, lane);
-        const float sr = row16_sum(Sl);
-        const float mr = lg == 0 ? M[0] : lg == 1 ? M[1] : lg == 2 ? M[2] : M[3];
-        const int h = kh * G + lg, d0 = 16 * c + 8 * (tslot & 1);
+        sr = row16_sum(Sl);
+        mr = lg == 0 ? M[0] : lg == 1 ? M[1] : lg == 2 ? M[2] : M[3];
+    };
+    auto write_rec = [&](int rec, const float (&z)[P], float mr, float sr) {
+        const size_t idx = (size_t)rec * p.nq + h;
+        store_floats<P>(p.ws_acc + idx * kHeadDim + d0, z);
+        if (c == 0 && (tslot & 1) == 0) p.ws_ms[idx] = make_float2(mr, sr);
+    };
+    auto finish = [&](bool to_out, int rec) {
+        float z[P], mr, sr;
+        sums(z, mr, sr);
         if (to_out) {
             // one division at the end ("9-2" §2 segment 3)
 #pragma unroll
-            for (int k = 0; k < 2 * G; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
-            store_floats<2 * G>(p.out + ((size_t)b * p.nq + h) * kHeadDim + d0, z);
+            for (int k = 0; k < P; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
+            store_floats<P>(p.out + ((size_t)b * p.nq + h) * kHeadDim + d0, z);
         } else {
-            const size_t idx = (size_t)rec * p.nq + h;
-            store_floats<2 * G>(p.ws_acc + idx * kHeadDim + d0, z);
-            if (c == 0 && (tslot & 1) == 0) p.ws_ms[idx] = make_float2(mr, sr);
+            write_rec(rec, z, mr, sr);
         }
+    };
+    // a run's chunk records held in LDS until the slots are full or the run
+    // ends (as in attend_piece)
+    int held = 0, held_rec = 0;
+    auto drain = [&]() {
+        for (int i = 0; i < held; ++i) {
+            float z[P];
+#pragma unroll
+            for (int k = 0; k < P; ++k) z[k] = runbuf[(i * (P + 2) + k) * 64 + lane];
+            write_rec(held_rec + i, z, runbuf[(i * (P + 2) + P) * 64 + lane], runbuf[(i * (P + 2) + P + 1) * 64 + lane]);
+        }
+        held = 0;
+    };
+    auto hold = [&](int rec) {
+        float z[P], mr, sr;
+        sums(z, mr, sr);
+        if (held == p.run_slots) drain();
+        if (held == 0) held_rec = rec;
+#pragma unroll
+        for (int k = 0; k < P; ++k) runbuf[(held * (P + 2) + k) * 64 + lane] = z[k];
+        runbuf[(held * (P + 2) + P) * 64 + lane] = mr;
+        runbuf[(held * (P + 2) + P + 1) * 64 + lane] = sr;
+        ++held;
     };
 
     // rounds and the chunk boundaries of a run as in attend_piece
@@ -465,7 +530,10 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
             ++lt;
             if constexpr (Runs) {
                 if (d == D - 1 && lt == cut && lt < lt1) {
-                    finish(false, rec++);
+                    if (p.run_slots > 0)
+                        hold(rec++);
+                    else
+                        finish(false, rec++);
                     fresh();
                     cut += chunk;
                 }
@@ -473,7 +541,12 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         }
     }
     finish(whole, rec);
+    if constexpr (Runs) drain();
 }
+
+// Ints of dynamic LDS before the invariant cut's run buffers (the batch
+// arrays, rounded up to 16 bytes).
+__host__ __device__ inline int run_buf_offset(int batch) { return (2 * batch + 1 + 3) & ~3; }
 
 // The partial kernel of either cut: Chunked walks the invariant cut
 // (p.chunk_tiles > 0) in chunk runs, else the balanced cut or a step plan.
@@ -482,14 +555,20 @@ static_assert(kInvariantChunkTiles % 2 == 0, "a chunk boundary must fall after a
 template <int G, bool Big, bool Chunked>
 __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(DecodeParams p)
 {
-    extern __shared__ int lds_batch[];   // [batch + 1] tile prefix, then [batch] lengths
+    // [batch + 1] tile prefix, [batch] lengths, then (invariant cut) each
+    // wave's run_slots held chunk records of 2 G + 2 floats per lane
+    extern __shared__ int lds_batch[];
+    float *runbuf = nullptr;
+    if constexpr (Chunked)
+        runbuf = reinterpret_cast<float *>(lds_batch + run_buf_offset(p.batch)) +
+                 (threadIdx.x >> 6) * p.run_slots * (2 * G + 2) * 64;
     auto attend = [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
                       const TileBlocks *first, int chunk) __attribute__((always_inline)) {
         // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
         if constexpr (G == 4 && Big)
-            attend_piece_mf<Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk);
+            attend_piece_mf<Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, runbuf);
         else
-            attend_piece<G, Big, Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk);
+            attend_piece<G, Big, Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, runbuf);
     };
     if constexpr (Chunked)
         walk_chunks<true>(p, lds_batch, lds_batch + p.batch + 1, attend);
@@ -791,6 +870,7 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
     pl.merge_waves = mw;
     pl.chunk_tiles = 0;
     pl.max_chunks = 0;
+    pl.run_slots = 0;
     size_t records = 2 * (size_t)pl.nparts;   // (range, slot) records per query head
     if (batch.flags & Q8_BATCH_INVARIANT) {
         // chunks counted from each sequence's start, no units charged per
@@ -801,6 +881,16 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
         pl.chunk_tiles = kInvariantChunkTiles;
         // the most chunks a sequence of at most max_seq_len positions has
         pl.max_chunks = max_chunks_of((batch.max_seq_len + kTile - 1) / kTile, kInvariantChunkTiles);
+        // chunk records a wave holds in LDS within a run: up to 8 (3 at G = 4,
+        // none at G = 8), as many as keep the workgroup's LDS within 64 KB;
+        // none when the batch has no more chunks than ranges (then a range
+        // walks about one chunk, and the larger LDS request measured slower)
+        const int group = nq / layer.nkv_heads;
+        int slots = group <= 2 ? 8 : group == 4 ? 3 : 0;
+        if ((long long)batch.batch * pl.max_chunks <= pl.nparts) slots = 0;
+        const size_t per_slot = (size_t)pl.waves * 64 * (2 * group + 2) * sizeof(float);
+        while (slots > 0 && (size_t)run_buf_offset(batch.batch) * sizeof(int) + slots * per_slot > 65536) --slots;
+        pl.run_slots = slots;
         pl.merge_slices = 1;
         pl.merge_waves = 4;
         records = (size_t)batch.batch * pl.max_chunks;
@@ -847,6 +937,7 @@ DecodeParams fill_decode_params(const q8_kv_layer &layer, const q8_batch &batch,
     p.piece_cost = plan.piece_cost;
     p.chunk_tiles = plan.chunk_tiles;
     p.max_chunks = plan.max_chunks;
+    p.run_slots = plan.run_slots;
     p.sc = (float)((double)scale * 1.4426950408889634);
     return p;
 }
@@ -862,7 +953,11 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
     const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile, plan.chunk_tiles > 0);
     void *args[] = {&p};
-    const hipError_t e = hipLaunchKernel(fn, grid, block, args, partial_lds_bytes(batch.batch), stream);
+    const size_t lds = plan.run_slots > 0 ? (size_t)run_buf_offset(batch.batch) * sizeof(int) +
+                                                (size_t)plan.run_slots * plan.waves * 64 *
+                                                    (2 * (nq / layer.nkv_heads) + 2) * sizeof(float)
+                                          : partial_lds_bytes(batch.batch);
+    const hipError_t e = hipLaunchKernel(fn, grid, block, args, lds, stream);
     return e != hipSuccess ? e : hipGetLastError();
 }
 

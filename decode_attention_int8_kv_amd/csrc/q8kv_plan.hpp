@@ -12,13 +12,14 @@ namespace q8kv {
 // Resolved launch plan of one decode call.
 struct DecodePlan {
     int nparts;          // equal ranges of the batch's tile sequence
-    int head_groups;     // workgroups per range (8 KV heads each)
+    int head_groups;     // workgroups per range (`waves` KV heads each)
     int waves;           // waves per decode workgroup
     int merge_waves;     // waves per merge workgroup
     int merge_slices;    // merge workgroups per (sequence, query head): dim slices 1, 2 or 4
     int piece_cost;      // cut-axis units charged per non-empty sequence (see q8kv_ranges.hpp)
     int chunk_tiles;     // batch-invariant cut: tiles per chunk (walk_chunks), or 0
     int max_chunks;      // batch-invariant cut: chunk records per sequence
+    int run_slots;       // batch-invariant cut: chunk records a wave holds in LDS within a run (0: none)
     size_t off_prefix, off_ms, off_acc, bytes;
 };
 

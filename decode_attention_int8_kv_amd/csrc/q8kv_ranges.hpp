@@ -49,6 +49,9 @@ struct DecodeParams {
     // records per sequence (record of chunk c of sequence b: b * max_chunks + c)
     int32_t chunk_tiles;
     int32_t max_chunks;
+    // chunk records a wave of the invariant cut's kernel holds in LDS (after
+    // the batch arrays) before writing them out, or 0
+    int32_t run_slots;
     float sc;             // softmax scale * log2(e)
 };
 
