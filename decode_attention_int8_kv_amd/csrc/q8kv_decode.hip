@@ -34,6 +34,67 @@ namespace q8kv {
 // 1.5% slower on the ragged 2B batch.
 template <int G> struct PipeDepth { static constexpr int value = 2; };
 
+// Where a wave's state goes after the slot sums (slot_reduce_scatter): token
+// slot s holds 2 G consecutive dims, from 16 c + (s 2 G) % 16, of head s G / 8
+// of its KV head, with that head's M and S.  key >= 0: record `key` of the
+// workspace; key < 0: output row -key - 1 (z already divided by S).
+template <int G>
+__device__ __forceinline__ void write_state(const DecodeParams &p, int kh, int lane, int key,
+                                            const float (&z)[2 * G], float mr, float sr)
+{
+    constexpr int P = 2 * G;
+    const int c = lane & 7, tslot = lane >> 3;
+    const int j0 = (tslot * P) & 15, h = kh * G + ((tslot * G) >> 3);
+    if (key >= 0) {
+        const size_t idx = (size_t)key * p.nq + h;
+        store_floats<P>(p.ws_acc + idx * kHeadDim + 16 * c + j0, z);
+        if (c == 0 && j0 == 0) p.ws_ms[idx] = make_float2(mr, sr);
+    } else {
+        store_floats<P>(p.out + ((size_t)(-key - 1) * p.nq + h) * kHeadDim + 16 * c + j0, z);
+    }
+}
+
+// A wave's finished states waiting in LDS (lane-private slots of P + 3 words:
+// the dims, M, S and the key) until the slots are full or the workgroup's walk
+// ends.  Stores issued between tile loads would hold up every later tile wait
+// (the vector memory counter counts in order), so a state is written only
+// after the wave's last tile, unless the slots run out first.  slots = 0:
+// every state is written at once.
+template <int G>
+struct HeldStates {
+    static constexpr int P = 2 * G, W = P + 3;
+    float *buf;   // [slots][W][64]
+    int slots;
+    int n;        // held (uniform)
+
+    __device__ __forceinline__ void drain(const DecodeParams &p, int kh, int lane)
+    {
+        for (int i = 0; i < n; ++i) {
+            float z[P];
+#pragma unroll
+            for (int k = 0; k < P; ++k) z[k] = buf[(i * W + k) * 64 + lane];
+            write_state<G>(p, kh, lane, __float_as_int(buf[(i * W + P + 2) * 64 + lane]), z,
+                           buf[(i * W + P) * 64 + lane], buf[(i * W + P + 1) * 64 + lane]);
+        }
+        n = 0;
+    }
+    __device__ __forceinline__ void put(const DecodeParams &p, int kh, int lane, int key, const float (&z)[P],
+                                        float mr, float sr)
+    {
+        if (slots == 0) {
+            write_state<G>(p, kh, lane, key, z, mr, sr);
+            return;
+        }
+        if (n == slots) drain(p, kh, lane);
+#pragma unroll
+        for (int k = 0; k < P; ++k) buf[(n * W + k) * 64 + lane] = z[k];
+        buf[(n * W + P) * 64 + lane] = mr;
+        buf[(n * W + P + 1) * 64 + lane] = sr;
+        buf[(n * W + P + 2) * 64 + lane] = __int_as_float(key);
+        ++n;
+    }
+};
+
 // One wave: attention of the G query heads of KV head kh over tiles
 // [lt0, lt1) of sequence b (length n).  The state goes to the output rows
 // (whole) or to slot `slot` of record `part`, i.e. to record 2 part + slot.
@@ -45,7 +106,7 @@ template <int G> struct PipeDepth { static constexpr int value = 2; };
 template <int G, bool Big, bool Runs>
 __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int kh, int lane,
                                              int lt0, int lt1, int n, bool whole, int part,
-                                             int slot, const TileBlocks *first, int chunk, float *runbuf)
+                                             int slot, const TileBlocks *first, int chunk, HeldStates<G> &held)
 {
     const int c = lane & 7, tslot = lane >> 3;
     const uint32_t m1 = (c & 1) ? 0xffffffffu : 0u, m2 = (c & 2) ? 0xffffffffu : 0u;
@@ -213,7 +274,7 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
     // token slot s ends with 2 G consecutive dims of head s G / 8, which its 8
     // lanes hold in z, with the head's M and S.
     constexpr int P = 2 * G;
-    const int gh = (tslot * G) >> 3, j0 = (tslot * P) & 15, h = kh * G + gh;
+    const int gh = (tslot * G) >> 3;   // the head whose dims the lane ends with
     auto sums = [&](float (&z)[P], float &mr, float &sr) {
         float v[16 * G];
 #pragma unroll
@@ -235,48 +296,17 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
             mr = gh == g ? M[g] : mr;
         }
     };
-    auto write_rec = [&](int rec, const float (&z)[P], float mr, float sr) {
-        const size_t idx = (size_t)rec * p.nq + h;
-        store_floats<P>(p.ws_acc + idx * kHeadDim + 16 * c + j0, z);
-        if (c == 0 && j0 == 0) p.ws_ms[idx] = make_float2(mr, sr);
-    };
-    // the state to the output rows or to record `rec`
-    auto finish = [&](bool to_out, int rec) {
+    // the state to the output rows (divided by S) or to record `rec`, through
+    // the wave's held states
+    auto emit = [&](bool to_out, int rec) {
         float z[P], mr, sr;
         sums(z, mr, sr);
         if (to_out) {
             // one division at the end ("9-2" §2 segment 3)
 #pragma unroll
             for (int k = 0; k < P; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
-            store_floats<P>(p.out + ((size_t)b * p.nq + h) * kHeadDim + 16 * c + j0, z);
-        } else {
-            write_rec(rec, z, mr, sr);
         }
-    };
-    // A run's chunk records wait in LDS (lane-private slots of runbuf,
-    // p.run_slots of them) and are written out when the slots are full or the
-    // run ends: stores issued between the tile loads would hold up every later
-    // tile wait, the vector memory counter being in order.
-    int held = 0, held_rec = 0;
-    auto drain = [&]() {
-        for (int i = 0; i < held; ++i) {
-            float z[P];
-#pragma unroll
-            for (int k = 0; k < P; ++k) z[k] = runbuf[(i * (P + 2) + k) * 64 + lane];
-            write_rec(held_rec + i, z, runbuf[(i * (P + 2) + P) * 64 + lane], runbuf[(i * (P + 2) + P + 1) * 64 + lane]);
-        }
-        held = 0;
-    };
-    auto hold = [&](int rec) {
-        float z[P], mr, sr;
-        sums(z, mr, sr);
-        if (held == p.run_slots) drain();
-        if (held == 0) held_rec = rec;
-#pragma unroll
-        for (int k = 0; k < P; ++k) runbuf[(held * (P + 2) + k) * 64 + lane] = z[k];
-        runbuf[(held * (P + 2) + P) * 64 + lane] = mr;
-        runbuf[(held * (P + 2) + P + 1) * 64 + lane] = sr;
-        ++held;
+        held.put(p, kh, lane, to_out ? -(b + 1) : rec, z, mr, sr);
     };
 
     // D register tiles (the first D - 1 loaded above): while tile i is
@@ -302,18 +332,14 @@ __device__ __forceinline__ void attend_piece(const DecodeParams &p, int b, int k
             ++lt;
             if constexpr (Runs) {
                 if (d == D - 1 && lt == cut && lt < lt1) {   // a chunk of the run ends
-                    if (p.run_slots > 0)
-                        hold(rec++);
-                    else
-                        finish(false, rec++);
+                    emit(false, rec++);
                     fresh();
                     cut += chunk;
                 }
             }
         }
     }
-    finish(whole, rec);
-    if constexpr (Runs) drain();
+    emit(whole, rec);
 }
 
 // Four query heads per KV head, kv_bs >= 32: the scores on the matrix cores
@@ -345,7 +371,7 @@ __device__ __forceinline__ float row16_sum(float v)
 template <bool Runs>
 __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, int kh, int lane, int lt0, int lt1,
                                                 int n, bool whole, int part, int slot, const TileBlocks *first,
-                                                int chunk, float *runbuf)
+                                                int chunk, HeldStates<4> &held)
 {
     constexpr int G = 4;
     const int c = lane & 7, tslot = lane >> 3;
@@ -465,7 +491,6 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
     // slot s holds dims 8 (s & 1) + k of head s / 2 = lg, whose sum
     // row16_sum(Sl) gives in the same lanes
     constexpr int P = 2 * G;
-    const int h = kh * G + lg, d0 = 16 * c + 8 * (tslot & 1);
     auto sums = [&](float (&z)[P], float &mr, float &sr) {
         float v[16 * G];
 #pragma unroll
@@ -476,45 +501,15 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
         sr = row16_sum(Sl);
         mr = lg == 0 ? M[0] : lg == 1 ? M[1] : lg == 2 ? M[2] : M[3];
     };
-    auto write_rec = [&](int rec, const float (&z)[P], float mr, float sr) {
-        const size_t idx = (size_t)rec * p.nq + h;
-        store_floats<P>(p.ws_acc + idx * kHeadDim + d0, z);
-        if (c == 0 && (tslot & 1) == 0) p.ws_ms[idx] = make_float2(mr, sr);
-    };
-    auto finish = [&](bool to_out, int rec) {
+    auto emit = [&](bool to_out, int rec) {
         float z[P], mr, sr;
         sums(z, mr, sr);
         if (to_out) {
             // one division at the end ("9-2" §2 segment 3)
 #pragma unroll
             for (int k = 0; k < P; ++k) z[k] = sr > 0.0f ? z[k] / sr : 0.0f;
-            store_floats<P>(p.out + ((size_t)b * p.nq + h) * kHeadDim + d0, z);
-        } else {
-            write_rec(rec, z, mr, sr);
         }
-    };
-    // a run's chunk records held in LDS until the slots are full or the run
-    // ends (as in attend_piece)
-    int held = 0, held_rec = 0;
-    auto drain = [&]() {
-        for (int i = 0; i < held; ++i) {
-            float z[P];
-#pragma unroll
-            for (int k = 0; k < P; ++k) z[k] = runbuf[(i * (P + 2) + k) * 64 + lane];
-            write_rec(held_rec + i, z, runbuf[(i * (P + 2) + P) * 64 + lane], runbuf[(i * (P + 2) + P + 1) * 64 + lane]);
-        }
-        held = 0;
-    };
-    auto hold = [&](int rec) {
-        float z[P], mr, sr;
-        sums(z, mr, sr);
-        if (held == p.run_slots) drain();
-        if (held == 0) held_rec = rec;
-#pragma unroll
-        for (int k = 0; k < P; ++k) runbuf[(held * (P + 2) + k) * 64 + lane] = z[k];
-        runbuf[(held * (P + 2) + P) * 64 + lane] = mr;
-        runbuf[(held * (P + 2) + P + 1) * 64 + lane] = sr;
-        ++held;
+        held.put(p, kh, lane, to_out ? -(b + 1) : rec, z, mr, sr);
     };
 
     // rounds and the chunk boundaries of a run as in attend_piece
@@ -530,22 +525,18 @@ __device__ __forceinline__ void attend_piece_mf(const DecodeParams &p, int b, in
             ++lt;
             if constexpr (Runs) {
                 if (d == D - 1 && lt == cut && lt < lt1) {
-                    if (p.run_slots > 0)
-                        hold(rec++);
-                    else
-                        finish(false, rec++);
+                    emit(false, rec++);
                     fresh();
                     cut += chunk;
                 }
             }
         }
     }
-    finish(whole, rec);
-    if constexpr (Runs) drain();
+    emit(whole, rec);
 }
 
-// Ints of dynamic LDS before the invariant cut's run buffers (the batch
-// arrays, rounded up to 16 bytes).
+// Ints of dynamic LDS before the waves' held states (the batch arrays,
+// rounded up to 16 bytes).
 __host__ __device__ inline int run_buf_offset(int batch) { return (2 * batch + 1 + 3) & ~3; }
 
 // The partial kernel of either cut: Chunked walks the invariant cut
@@ -558,22 +549,25 @@ __global__ __launch_bounds__(64 * kMaxWavesPerWG) void q8_attn_partial_kernel(De
     // [batch + 1] tile prefix, [batch] lengths, then (invariant cut) each
     // wave's run_slots held chunk records of 2 G + 2 floats per lane
     extern __shared__ int lds_batch[];
-    float *runbuf = nullptr;
-    if constexpr (Chunked)
-        runbuf = reinterpret_cast<float *>(lds_batch + run_buf_offset(p.batch)) +
-                 (threadIdx.x >> 6) * p.run_slots * (2 * G + 2) * 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    HeldStates<G> held{reinterpret_cast<float *>(lds_batch + run_buf_offset(p.batch)) +
+                           wave * p.run_slots * HeldStates<G>::W * 64,
+                       p.run_slots, 0};
     auto attend = [&](int b, int kh, int lane, int lt0, int lt1, int n, bool whole, int part, int slot,
                       const TileBlocks *first, int chunk) __attribute__((always_inline)) {
         // the matrix-core score path exactly where decode_uses_mfma_scores(G, kv_bs) holds
         if constexpr (G == 4 && Big)
-            attend_piece_mf<Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, runbuf);
+            attend_piece_mf<Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, held);
         else
-            attend_piece<G, Big, Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, runbuf);
+            attend_piece<G, Big, Chunked>(p, b, kh, lane, lt0, lt1, n, whole, part, slot, first, chunk, held);
     };
     if constexpr (Chunked)
         walk_chunks<true>(p, lds_batch, lds_batch + p.batch + 1, attend);
     else
         walk_balanced(p, lds_batch, lds_batch + p.batch + 1, attend);
+    // the held states, once the wave's last tile is in (its KV head as in the walks)
+    const int hg = blockIdx.x % p.head_groups;
+    held.drain(p, hg * (int)(blockDim.x >> 6) + wave, lane);
 }
 
 // ---------------------------------------------------------------- merge ----
@@ -780,8 +774,13 @@ static const void *partial_kernel(int group, bool big, bool chunked)
     }
 }
 
-// LDS of one partial workgroup: the batch's tile prefix and lengths.
-static size_t partial_lds_bytes(int batch) { return (size_t)(2 * batch + 1) * sizeof(int); }
+// LDS of one partial workgroup: the batch's tile prefix and lengths, and
+// (slots > 0) each wave's held states (HeldStates) after them.
+static size_t partial_lds_bytes(int batch, int waves = 0, int group = 0, int slots = 0)
+{
+    if (slots <= 0) return (size_t)(2 * batch + 1) * sizeof(int);
+    return (size_t)run_buf_offset(batch) * sizeof(int) + (size_t)slots * waves * 64 * (2 * group + 3) * sizeof(float);
+}
 
 int decode_blocks_per_cu(int group, int waves, int batch)
 {
@@ -881,19 +880,21 @@ DecodePlan make_plan(const q8_kv_layer &layer, const q8_batch &batch, int nq, in
         pl.chunk_tiles = kInvariantChunkTiles;
         // the most chunks a sequence of at most max_seq_len positions has
         pl.max_chunks = max_chunks_of((batch.max_seq_len + kTile - 1) / kTile, kInvariantChunkTiles);
-        // chunk records a wave holds in LDS within a run: up to 8 (3 at G = 4,
-        // none at G = 8), as many as keep the workgroup's LDS within 64 KB;
-        // none when the batch has no more chunks than ranges (then a range
-        // walks about one chunk, and the larger LDS request measured slower)
-        const int group = nq / layer.nkv_heads;
-        int slots = group <= 2 ? 8 : group == 4 ? 3 : 0;
-        if ((long long)batch.batch * pl.max_chunks <= pl.nparts) slots = 0;
-        const size_t per_slot = (size_t)pl.waves * 64 * (2 * group + 2) * sizeof(float);
-        while (slots > 0 && (size_t)run_buf_offset(batch.batch) * sizeof(int) + slots * per_slot > 65536) --slots;
-        pl.run_slots = slots;
         pl.merge_slices = 1;
         pl.merge_waves = 4;
         records = (size_t)batch.batch * pl.max_chunks;
+    }
+    // states a wave holds in LDS until its walk ends (HeldStates): up to 8 (3
+    // at G = 4, none at G = 8), as many as keep the workgroup's LDS within 64
+    // KB; none where a range walks about one piece (one sequence; or, for the
+    // invariant cut, no more chunks than ranges), since the larger LDS
+    // request then measured slower
+    {
+        const int group = nq / layer.nkv_heads;
+        int slots = group <= 2 ? 8 : group == 4 ? 3 : 0;
+        if (pl.chunk_tiles > 0 ? (long long)batch.batch * pl.max_chunks <= pl.nparts : batch.batch <= 1) slots = 0;
+        while (slots > 0 && partial_lds_bytes(batch.batch, pl.waves, group, slots) > 65536) --slots;
+        pl.run_slots = slots;
     }
     pl.off_prefix = 0;
     pl.off_ms = align_up(sizeof(int32_t) * ((size_t)batch.batch + 1), 256);
@@ -953,10 +954,7 @@ hipError_t launch_decode_partial(const q8_kv_layer &layer, const q8_batch &batch
     const dim3 grid(plan.nparts * plan.head_groups), block(plan.waves * 64);
     const void *fn = partial_kernel(nq / layer.nkv_heads, layer.kv_bs >= kTile, plan.chunk_tiles > 0);
     void *args[] = {&p};
-    const size_t lds = plan.run_slots > 0 ? (size_t)run_buf_offset(batch.batch) * sizeof(int) +
-                                                (size_t)plan.run_slots * plan.waves * 64 *
-                                                    (2 * (nq / layer.nkv_heads) + 2) * sizeof(float)
-                                          : partial_lds_bytes(batch.batch);
+    const size_t lds = partial_lds_bytes(batch.batch, plan.waves, nq / layer.nkv_heads, plan.run_slots);
     const hipError_t e = hipLaunchKernel(fn, grid, block, args, lds, stream);
     return e != hipSuccess ? e : hipGetLastError();
 }
