@@ -7,60 +7,73 @@
 // before the call); query row r at position p attends to positions 0..p.
 // Each query row is quantized like the decode query (per 32-block step
 // m * fl(1/127), codes truncated), and its attention is the decode's:
-// s_t = ((sum_beta float(P_beta) * qs_beta) * ks_t) * scale with exact int32
+// s_t = ((sum_beta float(P_beta) * qs_beta) * ks_t) * scale with exact
 // block partials P_beta, softmax over t <= p, weights times V codes and V
 // steps, one division at the end ("9-2 flash_attn_single_q_q8_neon" §2).
 //
-// A wave owns 32 query rows of one KV head (two sets of 16): row rho =
-// position * G + head of the flattened (position, query head) list.  It
-// walks the keys 0..p_max of its rows in tiles of 16 tokens (for a fresh
-// prompt, a quarter of them: see prefill_segments); each tile's loads, V
-// transpose and V operands serve both sets:
-//   scores  S^T = K Q^T with v_mfma_i32_16x16x32_i8, one instruction per
-//           32-block beta (A: token j's bytes 32 beta + [8 lg, 8 lg + 8) in
-//           lane (lg, j); B: the query codes in the same places), so lane
-//           (lg, j) receives the exact partials of query j with tokens
-//           4 lg .. 4 lg + 3 and forms their fp32 scores in place;
-//   softmax online per query (log2 domain): the tile max across the 4 lane
-//           groups with v_permlane16/32_swap, one rescale of S and the
-//           accumulators per tile;
-//   values  O^T += V^T P^T on the bf16 matrix cores.  P^T arrives in
-//           exactly the B layout (query j, tokens 4 lg + e); each weight
-//           w = p * vs is split exactly into three bf16 terms
-//           (w = hi + mid + lo by truncation; the "bf16x3" form of an fp32
-//           product), and V codes (|code| <= 127) are exact in bf16, so the
-//           products are exact and only the fp32 accumulation order differs
-//           from a scalar loop.  The hi and mid terms go through one
-//           v_mfma_f32_16x16x32_bf16 (same cost as a K = 16 product, twice
-//           the work): its A operand holds the lane's 4 V values twice and its
-//           B operand the 4 hi then the 4 mid weights, so each k slot pairs a
-//           token's V code with one of its terms (A and B hold the same k
-//           slots in a lane, whatever their order); lo uses
-//           v_mfma_f32_16x16x16_bf16.  V^T is staged per tile through LDS: each
-//           lane loads 4 bytes of 8 token rows, transposes them with v_perm
-//           and writes one dword (4 tokens of one dim) per dim.
+// A workgroup owns 128 query rows of one KV head (row rho = position * G +
+// head of the flattened (position, query head) list) and splits their key
+// range 0..p_max in two: each half is walked by a group of four waves, one
+// wave per 32 rows (two sets of 16).  The four waves of a group walk the
+// same 32-token key tiles, so each tile is loaded from HBM once per group
+// and converted once into matrix-core operands in LDS, which all four read:
+//   K  as fp16 codes (exact; two codes per byte permute and one packed fp16
+//      subtraction, below);
+//   V^T as bf16 (codes are exact in bf16), each dim row holding the 32 tokens
+//      in the order of the weight operand below.
+// Per tile and query set:
+//   scores  S^T = K Q^T with v_mfma_f32_16x16x32_f16, one instruction per
+//           32-block beta and half tile: every product and partial sum is an
+//           integer of magnitude below 2^19, so the result is the exact block
+//           partial P_beta, as an int32 product would give it; lane (lg, j)
+//           then holds query j's partials with tokens 16 h + 4 lg + e;
+//   softmax online per query (log2 domain) with a reference max (below);
+//   values  O^T += V^T P^T on the bf16 matrix cores: the lane's 8 weights are
+//           already one k-slice of the B operand (slot 4 h + e is token
+//           16 h + 4 lg + e); each fp32 weight w = p * vs is split exactly
+//           into three bf16 terms (w = hi + mid + lo by truncation, the
+//           "bf16x3" form of an fp32 product) and V codes are exact in bf16,
+//           so every product is exact and only the fp32 accumulation order
+//           differs from a scalar loop: three v_mfma_f32_16x16x32_bf16 per 16
+//           dims.
+// The second group's states are folded into the first's at the end through
+// LDS (the decode merge rule), so the result is deterministic.
 #include "q8kv_tile.hpp"
 #include "q8kv_internal.hpp"
 
 namespace q8kv {
 
-typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
-typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 
-// Eight bf16 from two groups of four (the operand of a K = 32 product).
-__device__ __forceinline__ v8bf_t cat_bf16(v4s_t a, v4s_t b)
-{
-    const uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
-    return __builtin_bit_cast(v8bf_t, make_uint4(x.x, x.y, y.x, y.y));
-}
+constexpr int kPfGroups = 2;                          // key-range halves per workgroup
+constexpr int kPfRowWaves = 4;                        // waves per half, one per 32 rows
+constexpr int kPfWaves = kPfGroups * kPfRowWaves;
+constexpr int kSets = 2;                              // 16-row query sets per wave
+constexpr int kPfRows = 16 * kSets;                   // query rows per wave
+constexpr int kPfBlockRows = kPfRowWaves * kPfRows;   // query rows per workgroup
+constexpr int kKeyTile = 32;                          // tokens per step
+constexpr int kKRow = 136;                            // halves per staged K row (128 + 8 pad)
+constexpr int kVRow = 40;                             // halves per staged V^T row (32 + 8 pad)
 
-constexpr int kPrefillWaves = 4;   // query tiles per workgroup
-constexpr int kSets = 2;           // 16-row query sets per wave (share each key tile's loads and V operands)
-constexpr int kPrefillRows = 16 * kSets;   // query rows per wave
-constexpr int kKeyTile = 16;       // tokens per step
-constexpr int kVtStride = 5;       // dwords per dim row of the staged V^T tile (4 token quads + 1 pad)
+// One staged key tile of one group.
+struct Stage {
+    uint16_t k[kKeyTile * kKRow];     // K rows, fp16 codes, dims in order
+    uint16_t vt[kHeadDim * kVRow];    // V^T rows, bf16 codes; slot 8 lg + 4 h + e = token 16 h + 4 lg + e
+                                      // (chunk lg stored at vt_chunk(d, lg))
+    float kss[kKeyTile];              // ks * scale * log2(e)
+    float vs[kKeyTile];
+    uint32_t good;                    // bit t: token t's block id is valid
+    uint32_t pad[3];
+};
+// Second group's per-lane states for the fold: [row wave][set][32 accumulators, M, S][lane].
+constexpr int kCombVals = 8 * 4 + 2;
+constexpr size_t kStageBytes = sizeof(Stage) * kPfGroups * 2;
+constexpr size_t kCombBytes = sizeof(float) * kPfRowWaves * kSets * kCombVals * 64;
+constexpr size_t kPfLds = kStageBytes > kCombBytes ? kStageBytes : kCombBytes;
+static_assert(sizeof(Stage) % 16 == 0, "stages stay 16-byte aligned");
 
 struct PrefillParams {
     CacheView cache;
@@ -71,154 +84,216 @@ struct PrefillParams {
     float *out;
     int32_t *dev_status;
     int32_t nq, max_blocks_per_seq, max_seq_len, max_new, total_q, log2g;
-    int32_t ks;   // key segments per query tile (1, 2 or 4 waves of a workgroup)
     float sc;     // softmax scale * log2(e)
 };
 
-// Partial states of the key segments other than the first, per lane:
-// [slot][set][32 accumulators, M, S][lane].
-constexpr int kCombVals = 8 * 4 + 2;
-// Waves that split one query tile's keys when at least half of them are new
-// (prefill_segments).  The launch halves it (to 2, then 1) only while the
-// grid would exceed 65535 rows of workgroups, i.e. for prompts of more than
-// 2^21 query rows; chunks after a long history use 1.
-constexpr int kPrefillSplit = 4;
+// One thread's share of a key tile as loaded: 16 K bytes of one token, 4 V
+// bytes of 4 tokens, and (lanes 0..31 of the group's first two waves) the K
+// or V step of token lane.
+struct TileRaw {
+    uint4 k;
+    uint32_t v[4];
+    float s;
+    bool good;   // the block id behind the step is valid
+    bool bad;    // some block id behind this thread's loads is not
+};
 
-// 4 int8 codes (one dword) -> 4 bf16 (exact: |code| <= 127 has 7 bits).
-__device__ __forceinline__ v4s_t codes_to_bf16(uint32_t w)
+// The V share of thread gt: token quad a (tokens 4 a .. 4 a + 3, a = 4 h + lg
+// for tokens 16 h + 4 lg + e) and dim quad c (dims 4 c .. 4 c + 3).  Sixteen
+// neighbouring lanes read 64 contiguous bytes of a row, and the 32 lanes of a
+// half wave write 32 different bank pairs of the staged V^T (below).
+__device__ __forceinline__ int v_quad(int gt) { return (((gt >> 4) & 1) << 2) | (gt >> 6); }
+__device__ __forceinline__ int v_dims(int gt) { return (gt & 15) | (((gt >> 5) & 1) << 4); }
+
+// V^T row d keeps its four 16-byte chunks (lane group lg's 8 token slots)
+// at chunk lg ^ ((d / 16) % 4): the readers of a chunk (16 lanes, rows
+// 16 dt .. 16 dt + 15) are unaffected, and the writers of one dim of four
+// tokens (rows 4 c + dd) spread over every bank.
+__device__ __forceinline__ int vt_chunk(int d, int lg) { return lg ^ ((d >> 4) & 3); }
+
+// Block ids of a tile, fetched one tile ahead of its loads.  Big (kv_bs >= 32):
+// the tile lies in one block, one wave-uniform id; otherwise each thread
+// looks up the blocks of its own tokens (tokens past the workgroup's last
+// position are clamped to it: no row attends to them).
+struct TileIds {
+    int k, v, s;
+};
+
+template <bool Big>
+__device__ __forceinline__ TileIds tile_ids(const PrefillParams &p, const int32_t *bt, int t0, int p_hi, int gt)
 {
-    const uint32_t f0 = __float_as_uint((float)(int)(int8_t)(w & 0xff));
-    const uint32_t f1 = __float_as_uint((float)(int)(int8_t)((w >> 8) & 0xff));
-    const uint32_t f2 = __float_as_uint((float)(int)(int8_t)((w >> 16) & 0xff));
-    const uint32_t f3 = __float_as_uint((float)(int)(int8_t)(w >> 24));
-    const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);   // upper halves of f0, f1
-    const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
-    return __builtin_bit_cast(v4s_t, make_uint2(lo, hi));
+    const int log2bs = p.cache.kv_bs_log2;
+    TileIds ids;
+    if (Big) {
+        ids.k = ids.v = ids.s = uniform(((const_i32 *)bt)[t0 >> log2bs]);
+    } else {
+        ids.k = bt[min(t0 + (gt >> 3), p_hi) >> log2bs];
+        ids.v = bt[min(t0 + 4 * v_quad(gt), p_hi) >> log2bs];
+        ids.s = bt[min(t0 + (gt & 31), p_hi) >> log2bs];
+    }
+    return ids;
 }
 
-// Exact split of 4 fp32 weights into three bf16 terms each (truncation: the
+// A thread's byte offsets inside a tile, from the tile's first row: K row
+// gt / 8, bytes 16 (gt % 8); V rows 4 v_quad + u, bytes 4 v_dims.
+struct TileOffsets {
+    uint32_t k, v;
+};
+
+template <bool Big>
+__device__ __forceinline__ void load_tile(const PrefillParams &p, int kh, int t0, int p_hi, int gt,
+                                          const TileOffsets &off, const TileIds &ids, TileRaw &r)
+{
+    const int nkv = p.cache.nkv, row_bytes = nkv * kHeadDim;
+    const int log2bs = p.cache.kv_bs_log2, bmask = (1 << log2bs) - 1;
+    const unsigned nb = (unsigned)p.cache.num_blocks;
+    if (Big) {
+        // one block: buffer resources over the tile's rows (uniform), fixed
+        // per-thread offsets; default caching, since the other row blocks of
+        // the sequence read the same tile from L2
+        r.good = (unsigned)ids.s < nb;
+        r.bad = !r.good;
+        const int id = r.good ? ids.s : 0;
+        const size_t row0 = ((size_t)id << log2bs) + (size_t)(t0 & bmask);
+        const int tile_bytes = kKeyTile * row_bytes;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.cache.k_codes + row0 * row_bytes, tile_bytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.cache.v_codes + row0 * row_bytes, tile_bytes);
+        r.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)off.k, 0, 0));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            r.v[u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(vr, (int)off.v, u * row_bytes, 0));
+        // steps: wave 0 of the group the K steps (lane t: token t), wave 1
+        // the V steps (one wave-uniform resource each)
+        const int sw = uniform(gt >> 6);
+        if (sw < 2) {
+            const size_t s0 = (((size_t)id * nkv + kh) << log2bs) + (size_t)(t0 & bmask);
+            r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                make_rsrc((sw == 0 ? p.cache.k_scale : p.cache.v_scale) + s0, 4 * kKeyTile),
+                                                4 * (gt & 31), 0, 0));
+        }
+        return;
+    }
+    auto row_of = [&](int id, int t) {   // physical row of token t in block id (0 for a bad id)
+        return ((size_t)((unsigned)id < nb ? id : 0) << log2bs) + (size_t)(t & bmask);
+    };
+    {
+        const int t = min(t0 + (gt >> 3), p_hi);
+        r.k = *reinterpret_cast<const uint4 *>(p.cache.k_codes + row_of(ids.k, t) * row_bytes + kh * kHeadDim +
+                                               16 * (gt & 7));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int t = min(t0 + 4 * v_quad(gt) + u, p_hi);
+        r.v[u] = *reinterpret_cast<const uint32_t *>(p.cache.v_codes + row_of(ids.v, t) * row_bytes +
+                                                     kh * kHeadDim + 4 * v_dims(gt));
+    }
+    r.good = (unsigned)ids.s < nb;
+    r.bad = !r.good || (unsigned)ids.k >= nb || (unsigned)ids.v >= nb;
+    if ((gt >> 6) < 2) {
+        const int t = min(t0 + (gt & 31), p_hi);
+        const size_t sidx = ((((size_t)(r.good ? ids.s : 0)) * nkv + kh) << log2bs) + (size_t)(t & bmask);
+        r.s = ((gt >> 6) == 0 ? p.cache.k_scale : p.cache.v_scale)[sidx];
+    }
+}
+
+// Converts a thread's loaded share into the stage's operand layouts.
+__device__ __forceinline__ void stage_tile(const PrefillParams &p, const TileRaw &r, int gt, Stage &s)
+{
+    // K: code c -> fp16 c, as (1024 + (c + 128)) - 1152: the code plus 128 is
+    // the low byte of an fp16 whose exponent field makes it 1024 plus that
+    // byte (one byte permute per two codes), and one packed fp16 subtraction
+    // per two codes is exact
+    const uint32_t kx[4] = {r.k.x ^ 0x80808080u, r.k.y ^ 0x80808080u, r.k.z ^ 0x80808080u, r.k.w ^ 0x80808080u};
+    uint32_t kh16[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kh16[2 * i] = __builtin_amdgcn_perm(0x64646464u, kx[i], 0x04010400u);
+        kh16[2 * i + 1] = __builtin_amdgcn_perm(0x64646464u, kx[i], 0x04030402u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const v2h_t x = __builtin_bit_cast(v2h_t, kh16[i]) - v2h_t{(_Float16)1152.0f, (_Float16)1152.0f};
+        kh16[i] = __builtin_bit_cast(uint32_t, x);
+    }
+    uint4 *kd = reinterpret_cast<uint4 *>(s.k + (gt >> 3) * kKRow + 16 * (gt & 7));
+    kd[0] = make_uint4(kh16[0], kh16[1], kh16[2], kh16[3]);
+    kd[1] = make_uint4(kh16[4], kh16[5], kh16[6], kh16[7]);
+    // V^T: dims 4 c + dd, tokens 4 a .. 4 a + 3 (a = 4 h + lg: slots 8 lg + 4 h ..)
+    const int a = v_quad(gt), c = v_dims(gt);
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+        const int d = 4 * c + dd;
+        const uint32_t f0 = __float_as_uint(byte_f(r.v[0], dd)), f1 = __float_as_uint(byte_f(r.v[1], dd));
+        const uint32_t f2 = __float_as_uint(byte_f(r.v[2], dd)), f3 = __float_as_uint(byte_f(r.v[3], dd));
+        *reinterpret_cast<uint2 *>(s.vt + d * kVRow + 8 * vt_chunk(d, a & 3) + 4 * (a >> 2)) =
+            make_uint2(__builtin_amdgcn_perm(f1, f0, 0x07060302u), __builtin_amdgcn_perm(f3, f2, 0x07060302u));
+    }
+    if ((gt >> 6) == 0) {
+        if (gt < 32) s.kss[gt] = r.s * p.sc;
+        const uint64_t g = __builtin_amdgcn_ballot_w64(r.good);
+        if (gt == 0) s.good = (uint32_t)g;
+    } else if ((gt >> 6) == 1 && (gt & 63) < 32) {
+        s.vs[gt & 31] = r.s;
+    }
+}
+
+// Exact split of 8 fp32 weights into three bf16 terms each (truncation: the
 // first term keeps the top 8 significant bits, the second the next 8, the
 // third the rest; both subtractions are exact).
-__device__ __forceinline__ void split_bf16x3(const float (&w)[4], v4s_t &hi, v4s_t &mid, v4s_t &lo)
+__device__ __forceinline__ void split_bf16x3(const float (&w)[8], v8bf_t &hi, v8bf_t &mid, v8bf_t &lo)
 {
-    uint32_t h[4], m[4], l[4];
+    uint32_t h[8], m[8], l[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
         h[e] = __float_as_uint(w[e]) & 0xffff0000u;
         const float r1 = w[e] - __uint_as_float(h[e]);
         m[e] = __float_as_uint(r1) & 0xffff0000u;
         const float r2 = r1 - __uint_as_float(m[e]);
         l[e] = __float_as_uint(r2);
     }
-    hi = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(h[1], h[0], 0x07060302u),
-                                              __builtin_amdgcn_perm(h[3], h[2], 0x07060302u)));
-    mid = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(m[1], m[0], 0x07060302u),
-                                               __builtin_amdgcn_perm(m[3], m[2], 0x07060302u)));
-    lo = __builtin_bit_cast(v4s_t, make_uint2(__builtin_amdgcn_perm(l[1], l[0], 0x07060302u),
-                                              __builtin_amdgcn_perm(l[3], l[2], 0x07060302u)));
-}
-
-// Loads of one 16-token key tile: K bytes for the score MFMAs, the K and V
-// steps of tokens t0 + 4 lg + e, and 4 bytes of 8 V rows for the transpose.
-struct KeyTile {
-    long ka[4];
-    float ks[4], vs[4];
-    uint32_t vw[8];
-    bool good_lo, good_hi;   // block ids of tokens t0 .. t0 + 7 and t0 + 8 .. t0 + 15 are valid
-};
-
-// Big (kv_bs >= 16): the tile lies in one physical block, which holds only
-// this sequence's rows; the bases are scalar, the lane offsets fixed, and
-// rows past the sequence end inside the block are read (they may hold any
-// bytes) and masked by the caller.  Otherwise (kv_bs = 8) the tile spans
-// two blocks and tokens are clamped to n - 1.
-template <bool Big>
-__device__ __forceinline__ void load_key_tile(const PrefillParams &p, const const_i32 *sbt, int kh, int t0, int n,
-                                              int j, int lg, int vh, int vd, KeyTile &kt)
-{
-    const int nkv = p.cache.nkv, row_bytes = nkv * kHeadDim;
-    const int log2bs = p.cache.kv_bs_log2, bmask = (1 << log2bs) - 1;
-    if (Big) {
-        const int id = sbt[t0 >> log2bs];   // t0 <= n - 1
-        const bool good = (unsigned)id < (unsigned)p.cache.num_blocks;
-        kt.good_lo = kt.good_hi = good;
-        const size_t row0 = ((size_t)(good ? id : 0) << log2bs) + (size_t)(t0 & bmask);
-        const int8_t *kb = p.cache.k_codes + row0 * row_bytes + kh * kHeadDim;
-        const int8_t *vb = p.cache.v_codes + row0 * row_bytes + kh * kHeadDim;
-        const size_t s0 = (((size_t)(good ? id : 0) * nkv + kh) << log2bs) + (size_t)(t0 & bmask);
+    uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
-        for (int beta = 0; beta < 4; ++beta)
-            kt.ka[beta] = *reinterpret_cast<const long *>(kb + j * row_bytes + 32 * beta + 8 * lg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            kt.ks[e] = p.cache.k_scale[s0 + 4 * lg + e];
-            kt.vs[e] = p.cache.v_scale[s0 + 4 * lg + e];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            kt.vw[u] = *reinterpret_cast<const uint32_t *>(vb + (8 * vh + u) * row_bytes + 4 * vd);
-    } else {
-        int id0 = sbt[min(t0, n - 1) >> log2bs];
-        int id1 = sbt[min(t0 + 8, n - 1) >> log2bs];
-        kt.good_lo = (unsigned)id0 < (unsigned)p.cache.num_blocks;
-        kt.good_hi = (unsigned)id1 < (unsigned)p.cache.num_blocks;
-        id0 = kt.good_lo ? id0 : 0;
-        id1 = kt.good_hi ? id1 : 0;
-        auto row_of = [&](int t) {   // t in [t0, t0 + 16), clamped to n - 1
-            const int id = ((t - t0) >> 3) ? id1 : id0;
-            return ((size_t)id << log2bs) + (size_t)(t & bmask);
-        };
-        const int8_t *krow = p.cache.k_codes + row_of(min(t0 + j, n - 1)) * row_bytes + kh * kHeadDim + 8 * lg;
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) kt.ka[beta] = *reinterpret_cast<const long *>(krow + 32 * beta);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const size_t row = row_of(min(t0 + 4 * lg + e, n - 1));
-            const size_t sidx = (((row >> log2bs) * nkv + kh) << log2bs) + (row & bmask);
-            kt.ks[e] = p.cache.k_scale[sidx];
-            kt.vs[e] = p.cache.v_scale[sidx];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const size_t row = row_of(min(t0 + 8 * vh + u, n - 1));
-            kt.vw[u] = *reinterpret_cast<const uint32_t *>(p.cache.v_codes + row * row_bytes + kh * kHeadDim + 4 * vd);
-        }
+    for (int i = 0; i < 4; ++i) {
+        ph[i] = __builtin_amdgcn_perm(h[2 * i + 1], h[2 * i], 0x07060302u);
+        pm[i] = __builtin_amdgcn_perm(m[2 * i + 1], m[2 * i], 0x07060302u);
+        pl[i] = __builtin_amdgcn_perm(l[2 * i + 1], l[2 * i], 0x07060302u);
     }
+    hi = __builtin_bit_cast(v8bf_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    mid = __builtin_bit_cast(v8bf_t, make_uint4(pm[0], pm[1], pm[2], pm[3]));
+    lo = __builtin_bit_cast(v8bf_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 }
 
 template <bool Big>
-__global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillParams p)
+__global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams p)
 {
-    __shared__ uint32_t vt_all[kPrefillWaves][kHeadDim * kVtStride];
-    __shared__ float comb[kPrefillWaves - 1][kSets][kCombVals][64];
+    __shared__ __align__(16) unsigned char lds[kPfLds];
+    // each wave's query operands (read back by the same lanes every tile)
+    __shared__ __align__(16) v8h_t q_lds[kPfWaves][kSets][4][64];
+    Stage *stages = reinterpret_cast<Stage *>(lds);   // [group][buffer]
     const int nkv = p.cache.nkv;
     const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
     const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    uint32_t *vt = vt_all[wave];
-    // With ks > 1 the ks waves of a group share one query tile, each taking a
-    // contiguous segment of its key tiles; their states are combined at the
-    // end.  The last query tiles (the longest key ranges under the causal
-    // mask) are dispatched first, so the short ones fill in behind them.
-    const int ks = p.ks, seg = wave % ks;
-    const int tile = (gridDim.y - 1 - blockIdx.y) * (kPrefillWaves / ks) + wave / ks;
+    const int grp = wave / kPfRowWaves, rw = wave % kPfRowWaves;
+    const int gt = (int)threadIdx.x - grp * 64 * kPfRowWaves;   // thread within the group
+    // the last row blocks (the longest key ranges under the causal mask) are
+    // dispatched first, so the short ones fill in behind them
+    const int rb = gridDim.y - 1 - blockIdx.y;
     const int G = 1 << p.log2g;
     const int j = lane & 15, lg = lane >> 4;
-    // every wave meets the combine barrier (ks > 1), so nothing returns
-    // early: waves without work skip to it
-    bool active = true;
 
     const int r0 = uniform(p.q_start[b]), r1 = uniform(p.q_start[b + 1]);
     const int n = uniform(p.seq_lens[b]);
     const bool range_ok = 0 <= r0 && r0 <= r1 && r1 <= p.total_q;
     const int nn = r1 - r0;
+    const int wrow0 = rb * kPfBlockRows + rw * kPfRows;   // this wave's first row
     if (!range_ok || n < nn || n > p.max_seq_len || nn > p.max_new) {
-        // a bad sequence: reported; its rows that this wave covers are zeros
-        active = false;
-        if (kh == 0 && tile == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
-        if (range_ok && seg == 0) {
+        // a bad sequence (uniform over the workgroup): reported; its rows
+        // that this workgroup covers are zeros
+        if (kh == 0 && rb == 0 && threadIdx.x == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
+        if (range_ok && grp == 0) {
 #pragma unroll
             for (int st = 0; st < kSets; ++st) {
-                const int rho = tile * kPrefillRows + 16 * st + j;
+                const int rho = wrow0 + 16 * st + j;
                 if (rho < (nn << p.log2g)) {
                     const int i = rho >> p.log2g, g = rho & (G - 1);
                     float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
@@ -228,13 +303,61 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
                 }
             }
         }
+        return;
     }
     const int rows = nn << p.log2g;
-    if (tile * kPrefillRows >= rows) active = false;
+    if (rb * kPfBlockRows >= rows) return;   // uniform over the workgroup
 
-    // state of this wave (declared for the combine; set by active waves)
+    // the workgroup's key range, cut into two halves of (almost) equal tile counts
+    const int p0 = n - nn;   // position of the first new token
+    const int p_hi = p0 + (min(rb * kPfBlockRows + kPfBlockRows - 1, rows - 1) >> p.log2g);
+    const int nkt = p_hi / kKeyTile + 1;
+    const int half = nkt >> 1;
+    const int kt_lo = grp == 0 ? 0 : half, cnt = grp == 0 ? half : nkt - half;
+    const int iters = nkt - half;   // the same for every wave: the barrier count
+
+    // this wave's rows: clamped to a real row (lanes past the end are computed
+    // and discarded) and their positions
+    const bool active = wrow0 < rows;
     bool live[kSets] = {};
     int qi[kSets] = {}, qg[kSets] = {}, pos[kSets] = {};
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        const int rho = wrow0 + 16 * st + j;
+        live[st] = rho < rows;
+        const int rr = live[st] ? rho : rows - 1;
+        qi[st] = rr >> p.log2g;
+        qg[st] = rr & (G - 1);
+        pos[st] = p0 + qi[st];
+    }
+    const int pw_hi = p0 + (min(wrow0 + kPfRows - 1, rows - 1) >> p.log2g);   // the wave's largest position
+    const int pw_lo = p0 + (wrow0 >> p.log2g);                                 // and smallest
+
+    // query codes as fp16, the B operands of the score products (dims
+    // 32 beta + 8 lg .. + 7), kept in LDS, and their block steps
+    v8h_t (*qb)[4][64] = q_lds[wave];
+    float qs[kSets][4];
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        const size_t qrow = ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) {
+            const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
+            const float4 a = src[0], c = src[1];
+            const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+            m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
+            const BlockQuant bq = q_block_params(m);
+            v8h_t qc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qc[e] = (_Float16)q_code(x[e], bq.recip);
+            qb[st][beta][lane] = qc;
+            qs[st][beta] = bq.qscale;
+        }
+    }
+
     // M is a reference max per query: the weights exp2(s - M) may exceed 1 by
     // up to 2^kLazyRescale, and S and the accumulators are rescaled only when
     // some query's tile max rises above its M by more than that (the result
@@ -250,127 +373,102 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
         for (int dt = 0; dt < 8; ++dt) acc[st][dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (active) {
-    // this lane's query row in each set (clamped to a real row; lanes past the
-    // end are computed and discarded) and its position
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const int rho = tile * kPrefillRows + 16 * st + j;
-        live[st] = rho < rows;
-        const int rr = live[st] ? rho : rows - 1;
-        qi[st] = rr >> p.log2g;
-        qg[st] = rr & (G - 1);
-        pos[st] = n - nn + qi[st];
-    }
-    const int p_hi = n - nn + (min(tile * kPrefillRows + kPrefillRows - 1, rows - 1) >> p.log2g);
-    const int pos_lo = n - nn + ((tile * kPrefillRows) >> p.log2g);   // the wave's smallest position
-    const int nkt = p_hi / kKeyTile + 1;
-
-    // query codes, the B operands of the score MFMAs: bytes 32 beta + [8 lg, 8 lg + 8)
-    long qb[kSets][4];
-    float qs[kSets][4];
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const size_t qrow = ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) {
-            const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
-            const float4 a = src[0], c = src[1];
-            const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-            float m = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-            m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
-            const BlockQuant bq = q_block_params(m);
-            int cd[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cd[e] = q_code(x[e], bq.recip);
-            const uint32_t w0 = pack4_i8(cd[0], cd[1], cd[2], cd[3]), w1 = pack4_i8(cd[4], cd[5], cd[6], cd[7]);
-            qb[st][beta] = (long)(((uint64_t)w1 << 32) | w0);
-            qs[st][beta] = bq.qscale;
-        }
-    }
-
-    const const_i32 *sbt = (const const_i32 *)(p.block_table + (size_t)b * p.max_blocks_per_seq);
-    const int vh = lane >> 5, vd = lane & 31;   // V staging: tokens 8 vh + u, dims 4 vd .. 4 vd + 3
-
+    const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
     bool bad = false;
-    // tile kt + 1 (block id, K, steps, V rows) is in flight while tile kt is
-    // computed; past the end the last tile is reloaded, unused.  (Loading the
-    // V rows at the start of their own tile, or two tiles used in turn
-    // without the copy, both measured slower.)
-    // this wave's key segment: tiles [kt_lo, kt_hi) of the nkt, split evenly
-    // over the ks waves of the query tile (possibly empty: then nothing is
-    // loaded, since tile positions past the sequence have no table entry)
-    const int kt_lo = (seg * nkt) / ks, kt_hi = ((seg + 1) * nkt) / ks;
-    KeyTile nxt;
-    if (kt_lo < kt_hi) load_key_tile<Big>(p, sbt, kh, kt_lo * kKeyTile, n, j, lg, vh, vd, nxt);
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int t0 = kt * kKeyTile;
-        const KeyTile tl = nxt;
-        load_key_tile<Big>(p, sbt, kh, min(kt + 1, kt_hi - 1) * kKeyTile, n, j, lg, vh, vd, nxt);
-        bad = bad || !tl.good_lo || (t0 + 8 <= p_hi && !tl.good_hi);
-        // every row of the wave sees all 16 tokens of the tile: no masks
-        const bool full = t0 + kKeyTile - 1 <= pos_lo && tl.good_lo && tl.good_hi;
+    // pipeline: while tile i is computed, tile i + 1 is converted into the
+    // other buffer (before the computation, in the same iteration), tile
+    // i + 2's loads and tile i + 3's block ids are in flight
+    const int row_bytes = nkv * kHeadDim;
+    const TileOffsets off = {(uint32_t)((gt >> 3) * row_bytes + kh * kHeadDim + 16 * (gt & 7)),
+                             (uint32_t)(4 * v_quad(gt) * row_bytes + kh * kHeadDim + 4 * v_dims(gt))};
+    TileRaw raw;
+    TileIds ids_next = {0, 0, 0};
+    // stage tile k of the group into its buffer and start the loads of tile k + 1
+    auto advance = [&](int k) {
+        stage_tile(p, raw, gt, stages[2 * grp + (k & 1)]);
+        bad = bad || raw.bad;
+        if (k + 1 < cnt) {
+            const TileIds ids = ids_next;
+            if (k + 2 < cnt) ids_next = tile_ids<Big>(p, bt, (kt_lo + k + 2) * kKeyTile, p_hi, gt);
+            load_tile<Big>(p, kh, (kt_lo + k + 1) * kKeyTile, p_hi, gt, off, ids, raw);
+        }
+    };
+    if (cnt > 0) {
+        const TileIds ids0 = tile_ids<Big>(p, bt, kt_lo * kKeyTile, p_hi, gt);
+        if (cnt > 1) ids_next = tile_ids<Big>(p, bt, (kt_lo + 1) * kKeyTile, p_hi, gt);
+        load_tile<Big>(p, kh, kt_lo * kKeyTile, p_hi, gt, off, ids0, raw);
+        advance(0);
+    }
+    // the lane's operand rows: K token 16 h + j, dims 32 beta + 8 lg ..;
+    // V^T dim 16 dt + j, slots 8 lg .. (chunk vt_chunk(16 dt + j, lg))
+    const int krow = j * kKRow + 8 * lg;
+    for (int i = 0; i < iters; ++i) {
+        // tile i is staged (buffer i % 2); buffer (i + 1) % 2 is free: its
+        // readers finished tile i - 1 before this barrier
+        __syncthreads();
+        const Stage &sg = stages[2 * grp + (i & 1)];
+        const int t0 = (kt_lo + i) * kKeyTile;
+        const bool work = i < cnt && active && t0 <= pw_hi;
+        v8h_t ka[8], qv[4];
+        if (i + 1 < cnt) advance(i + 1);
+        if (!work) continue;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            ka[u] = *reinterpret_cast<const v8h_t *>(sg.k + krow + (u >> 2) * 16 * kKRow + 32 * (u & 3));
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) qv[beta] = qb[0][beta][lane];
 
-        // V^T tile through LDS: dword (dim, token quad) = 4 tokens of one dim;
-        // the bf16 A operands are formed once and serve both query sets
-        uint32_t tq[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint32_t a0 = tl.vw[4 * half], a1 = tl.vw[4 * half + 1], a2 = tl.vw[4 * half + 2],
-                           a3 = tl.vw[4 * half + 3];
-            const uint32_t x01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.b0 a1.b0 a0.b1 a1.b1
-            const uint32_t x01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.b2 a1.b2 a0.b3 a1.b3
-            const uint32_t x23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-            const uint32_t x23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-            tq[4 * half + 0] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);  // byte 0 of a0..a3
-            tq[4 * half + 1] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);  // byte 1
-            tq[4 * half + 2] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);  // byte 2
-            tq[4 * half + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);  // byte 3
-        }
-        asm volatile("" ::: "memory");   // the previous tile's V^T reads come first
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-            vt[(4 * vd + dd) * kVtStride + 2 * vh] = tq[dd];
-            vt[(4 * vd + dd) * kVtStride + 2 * vh + 1] = tq[4 + dd];
-        }
-        asm volatile("" ::: "memory");
-        v4s_t va[8];
-        v8bf_t va2[8];   // the same 4 values twice: the A operand of the paired hi + mid product
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            va[dt] = codes_to_bf16(vt[(16 * dt + j) * kVtStride + lg]);
-            va2[dt] = cat_bf16(va[dt], va[dt]);
-        }
-
+        const uint32_t gmask = sg.good;
+        // every row of the wave sees all 32 tokens of the tile: no masks
+        const bool full = t0 + kKeyTile - 1 <= pw_lo && gmask == 0xffffffffu;
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
-            // scores of query j of this set with tokens t0 + 4 lg + e
-            v4i_t c[4];
+            if (st > 0) {   // the same K operands, the next set's query codes
 #pragma unroll
-            for (int beta = 0; beta < 4; ++beta)
-                c[beta] = __builtin_amdgcn_mfma_i32_16x16x32_i8(tl.ka[beta], qb[st][beta], v4i_t{0, 0, 0, 0}, 0, 0, 0);
-            float s[4];
-            uint32_t keep[4];
+                for (int u = 0; u < 8; ++u)
+                    ka[u] = *reinterpret_cast<const v8h_t *>(sg.k + krow + (u >> 2) * 16 * kKRow + 32 * (u & 3));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float x0 = (float)c[0][e] * qs[st][0], x1 = (float)c[1][e] * qs[st][1];
-                const float x2 = (float)c[2][e] * qs[st][2], x3 = (float)c[3][e] * qs[st][3];
-                const float y = (x0 + x1) + (x3 + x2);
-                s[e] = y * (tl.ks[e] * p.sc);
+                for (int beta = 0; beta < 4; ++beta) qv[beta] = qb[st][beta][lane];
             }
-            if (!full) {
+            // block partials of query j with tokens 16 h + 4 lg + e (u = 4 h + beta)
+            v4f_t c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                c[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u], qv[u & 3], v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            // V operands and steps are read now: the softmax below covers their latency
+            v8bf_t va[8];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                va[dt] = *reinterpret_cast<const v8bf_t *>(sg.vt + (16 * dt + j) * kVRow + 8 * vt_chunk(16 * dt + j, lg));
+            const float4 k0 = *reinterpret_cast<const float4 *>(sg.kss + 4 * lg);
+            const float4 k1 = *reinterpret_cast<const float4 *>(sg.kss + 16 + 4 * lg);
+            __builtin_amdgcn_sched_barrier(0);
+            const float4 v0 = *reinterpret_cast<const float4 *>(sg.vs + 4 * lg);
+            const float4 v1 = *reinterpret_cast<const float4 *>(sg.vs + 16 + 4 * lg);
+            const float kss[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float vsv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            float s[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = t0 + 4 * lg + e;
-                    keep[e] = (t <= pos[st] && ((e + 4 * lg) < 8 ? tl.good_lo : tl.good_hi)) ? 0xffffffffu : 0u;
+                    // (P0 qs0 + P1 qs1) + (P3 qs3 + P2 qs2), the second product of each pair fused
+                    const float y01 = fmaf(c[4 * h + 1][e], qs[st][1], c[4 * h][e] * qs[st][0]);
+                    const float y23 = fmaf(c[4 * h + 2][e], qs[st][2], c[4 * h + 3][e] * qs[st][3]);
+                    s[4 * h + e] = (y01 + y23) * kss[4 * h + e];
+                }
+            uint32_t keep[8];
+            if (!full) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int tt = 16 * (u >> 2) + 4 * lg + (u & 3);   // token within the tile
+                    keep[u] = (t0 + tt <= pos[st] && ((gmask >> tt) & 1u)) ? 0xffffffffu : 0u;
                     // branch-free mask (a select here becomes a divergent
                     // branch); a masked token's step may be any bits, even NaN
-                    s[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(s[e]), 0xff800000u));
+                    s[u] = __uint_as_float(bitsel(keep[u], __float_as_uint(s[u]), 0xff800000u));
                 }
             }
-            float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            float m = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
             m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
             const bool grow = m > M[st] + kLazyRescale;   // also true on the first tile with a finite max
             if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -381,80 +479,68 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= alpha;
             }
-            float w[4], psum = 0.0f;
+            float w[8], psum = 0.0f;
             if (full) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pw = __builtin_amdgcn_exp2f(s[e] - M[st]);
+                for (int u = 0; u < 8; ++u) {
+                    const float pw = __builtin_amdgcn_exp2f(s[u] - M[st]);
                     psum += pw;
-                    w[e] = pw * tl.vs[e];
+                    w[u] = pw * vsv[u];
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int u = 0; u < 8; ++u) {
                     // masked: weight 0 (M may still be -inf, and the step may be NaN)
                     const float pw =
-                        __uint_as_float(bitsel(keep[e], __float_as_uint(__builtin_amdgcn_exp2f(s[e] - M[st])), 0u));
+                        __uint_as_float(bitsel(keep[u], __float_as_uint(__builtin_amdgcn_exp2f(s[u] - M[st])), 0u));
                     psum += pw;
-                    w[e] = __uint_as_float(bitsel(keep[e], __float_as_uint(pw * tl.vs[e]), 0u));
+                    w[u] = __uint_as_float(bitsel(keep[u], __float_as_uint(pw * vsv[u]), 0u));
                 }
             }
             S[st] += psum;
-            v4s_t whi, wmid, wlo;
+            v8bf_t whi, wmid, wlo;
             split_bf16x3(w, whi, wmid, wlo);
-            const v8bf_t whm = cat_bf16(whi, wmid);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va2[dt], whm, acc[st][dt], 0, 0, 0);
-                acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], wlo, acc[st][dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], whi, acc[st][dt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], wmid, acc[st][dt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], wlo, acc[st][dt], 0, 0, 0);
         }
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
 
-    }
-
-    // the other segments' states into the first's: M the largest, S and the
-    // accumulators rescaled to it and summed in segment order ("9-2" §2
-    // segment 2 rule applied to partial states); deterministic
-    if (ks > 1) {
-        const int slot = (wave / ks) * (ks - 1) + seg - 1;
-        if (active && seg > 0) {
+    // the second half's states into the first's: M the larger, S and the
+    // accumulators rescaled to it and summed in key order ("9-2" §2 segment 2
+    // rule applied to partial states); deterministic
+    __syncthreads();   // every wave is done with the stages
+    float(*comb)[kSets][kCombVals][64] = reinterpret_cast<float(*)[kSets][kCombVals][64]>(lds);
+    if (active && grp == 1) {
 #pragma unroll
-            for (int st = 0; st < kSets; ++st) {
+        for (int st = 0; st < kSets; ++st) {
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+            for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) comb[slot][st][4 * dt + e][lane] = acc[st][dt][e];
-                comb[slot][st][32][lane] = M[st];
-                comb[slot][st][33][lane] = S[st];
-            }
-        }
-        __syncthreads();
-        if (active && seg == 0) {
-#pragma unroll
-            for (int st = 0; st < kSets; ++st) {
-                float Mn = M[st];
-                for (int w = 1; w < ks; ++w) Mn = fmaxf(Mn, comb[slot + w][st][32][lane]);
-                const float a0 = M[st] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
-                S[st] *= a0;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= a0;
-                for (int w = 1; w < ks; ++w) {
-                    const float Mw = comb[slot + w][st][32][lane];
-                    const float aw = Mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mw - Mn);
-                    S[st] = fmaf(comb[slot + w][st][33][lane], aw, S[st]);
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[st][dt][e] = fmaf(comb[slot + w][st][4 * dt + e][lane], aw, acc[st][dt][e]);
-                }
-                M[st] = Mn;
-            }
+                for (int e = 0; e < 4; ++e) comb[rw][st][4 * dt + e][lane] = acc[st][dt][e];
+            comb[rw][st][32][lane] = M[st];
+            comb[rw][st][33][lane] = S[st];
         }
     }
-    if (!active || seg != 0) return;
+    __syncthreads();
+    if (!active || grp != 0) return;
+#pragma unroll
+    for (int st = 0; st < kSets; ++st) {
+        const float M1 = comb[rw][st][32][lane];
+        const float Mn = fmaxf(M[st], M1);
+        const float a0 = M[st] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
+        const float a1 = M1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M1 - Mn);
+        S[st] = fmaf(comb[rw][st][33][lane], a1, S[st] * a0);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[st][dt][e] = fmaf(comb[rw][st][4 * dt + e][lane], a1, acc[st][dt][e] * a0);
+    }
 
     float Ssum[kSets];
 #pragma unroll
@@ -473,22 +559,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void q8_prefill_kernel(PrefillP
                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-}
-
-// Key segments per query tile.  When at least half of the keys are new (a
-// fresh prompt, or a chunk as long as its history), the causal triangle makes
-// the last query tiles' key ranges about twice the average, and the waves
-// that walk them alone set the launch time: their keys are split over four
-// waves.  Chunks after a long history have query tiles of nearly equal
-// length and keep one wave per tile.  The grid stays within 65535 rows of
-// workgroups.
-static int prefill_segments(int max_new, int max_seq_len, long long rows)
-{
-    int ks = (2LL * max_new >= max_seq_len) ? kPrefillSplit : 1;
-    while (ks > 1 && (rows + (long long)kPrefillRows * (kPrefillWaves / ks) - 1) /
-                             ((long long)kPrefillRows * (kPrefillWaves / ks)) > 65535)
-        ks >>= 1;
-    return ks;
 }
 
 hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int nq, const int32_t *q_start,
@@ -517,14 +587,11 @@ hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int n
     p.log2g = ilog2(nq / layer.nkv_heads);
     p.sc = (float)((double)scale * 1.4426950408889634);
     const long long rows = (long long)max_new * (nq / layer.nkv_heads);
-    p.ks = prefill_segments(max_new, batch.max_seq_len, rows);
-    const long long rows_per_wg = (long long)kPrefillRows * (kPrefillWaves / p.ks);
-    const dim3 grid(batch.batch * layer.nkv_heads, (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+    const dim3 grid(batch.batch * layer.nkv_heads, (unsigned)((rows + kPfBlockRows - 1) / kPfBlockRows));
     void *args[] = {&p};
     const void *fn = layer.kv_bs >= kKeyTile ? reinterpret_cast<const void *>(&q8_prefill_kernel<true>)
                                              : reinterpret_cast<const void *>(&q8_prefill_kernel<false>);
-    const hipError_t e = hipLaunchKernel(fn, grid,
-                                         dim3(64 * kPrefillWaves), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * kPfWaves), args, 0, stream);
     return e != hipSuccess ? e : hipGetLastError();
 }
 
