@@ -40,7 +40,7 @@ def _case(lens, nbs, nq, nkv, kv_bs, seed, dist="normal"):
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("kv_bs", [8, 32, 64])
+@pytest.mark.parametrize("kv_bs", [8, 16, 32, 64, 256])
 def test_prefill_fresh_prompts(group, kv_bs):
     # the whole prompt is new: row 0 sees only itself, the last row everything
     say(f"[prefill] fresh prompts group={group} kv_bs={kv_bs}")
@@ -89,6 +89,45 @@ def test_bad_q_start_is_reported():
     assert np.all(got[:50] == 0)
     ok = oracle.prefill_attn(dc.host(), q[50:], [0, 0, 10], 4, SCALE)
     assert_rows_close(got[50:], ok, "the good sequence")
+
+
+@pytest.mark.parametrize("kv_bs", [8, 16, 32, 64])
+def test_prefill_bad_block_is_left_out(kv_bs):
+    # an out-of-range id in the middle of sequence 0's table: reported, and
+    # every row attends to its visible tokens without that block's.  Attention
+    # does not depend on the order of its tokens, so the reference for a row
+    # at position p is the oracle's decode over a table with the block removed
+    # and the length reduced by the block's tokens at or before p.
+    say(f"[prefill] bad block id, kv_bs={kv_bs}")
+    nq, nkv = 4, 2
+    lens = np.array([200, 150], np.int32)
+    nbs = np.array([200, 50], np.int32)
+    k, v = dense_kv(lens, nkv, seed=880 + kv_bs)
+    dc = DeviceCache(lens, nkv, kv_bs, seed=880 + kv_bs)
+    dc.append_dense(k, v)
+    bi = 96 // kv_bs   # the block holding token 96
+    dc.table_t[0, bi] = dc.num_blocks + 7
+    qs = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int32)
+    q = np.random.default_rng(881 + kv_bs).standard_normal((int(qs[-1]), nq, 128)).astype(np.float32)
+    got = _run(dc, q, qs, nq)
+    assert dc.status_word() & q8().DEV_BAD_BLOCK_ID
+    h = dc.host()
+    tables, ns = [], []
+    for b in range(2):
+        for i in range(int(nbs[b])):
+            p = int(lens[b] - nbs[b] + i)
+            row = h.block_table[b].copy()
+            n = p + 1
+            if b == 0:
+                row = np.concatenate([np.delete(row, bi), row[:1]])
+                n -= min(max(p + 1 - bi * kv_bs, 0), kv_bs)
+            tables.append(row)
+            ns.append(n)
+    view = oracle.Cache(h.k_codes, h.v_codes, h.k_step, h.v_step, np.stack(tables).astype(np.int32),
+                        np.array(ns, np.int32), nkv, 128)
+    want = oracle.decode_attn(view, q, nq, SCALE)
+    w = assert_rows_close(got, want, f"prefill with a bad block, kv_bs={kv_bs}")
+    say(f"  worst err/tol {w:.3f}")
 
 
 def test_prefill_2b_prompt_4059_sampled():
