@@ -14,28 +14,28 @@
 // A workgroup owns 128 query rows of one KV head (row rho = position * G +
 // head of the flattened (position, query head) list) and splits their key
 // range 0..p_max in two: each half is walked by a group of four waves, one
-// wave per 32 rows (two sets of 16).  The four waves of a group walk the
-// same 32-token key tiles, so each tile is loaded from HBM once per group
-// and converted once into matrix-core operands in LDS, which all four read:
+// wave per 32 rows.  The four waves of a group walk the same 32-token key
+// tiles, so each tile is loaded from HBM once per group and converted once
+// into matrix-core operands in LDS, which all four read:
 //   K  as fp16 codes (exact; two codes per byte permute and one packed fp16
 //      subtraction, below);
 //   V^T as bf16 (codes are exact in bf16), each dim row holding the 32 tokens
 //      in the order of the weight operand below.
-// Per tile and query set:
-//   scores  S^T = K Q^T with v_mfma_f32_16x16x32_f16, one instruction per
-//           32-block beta and half tile: every product and partial sum is an
-//           integer of magnitude below 2^19, so the result is the exact block
-//           partial P_beta, as an int32 product would give it; lane (lg, j)
-//           then holds query j's partials with tokens 16 h + 4 lg + e;
+// Per tile, with 32x32 matrix-core products (lane l: query j = l % 32, half
+// hf = l / 32):
+//   scores  S^T = K Q^T with v_mfma_f32_32x32x16_f16, two k-steps of 16 dims
+//           per 32-block beta: every product and partial sum is an integer of
+//           magnitude below 2^19, so the result is the exact block partial
+//           P_beta, as an int32 product would give it; the lane then holds
+//           query j's partials with tokens 8 g + 4 hf + e (g, e = 0..3);
 //   softmax online per query (log2 domain) with a reference max (below);
-//   values  O^T += V^T P^T on the bf16 matrix cores: the lane's 8 weights are
-//           already one k-slice of the B operand (slot 4 h + e is token
-//           16 h + 4 lg + e); each fp32 weight w = p * vs is split exactly
+//   values  O^T += V^T P^T with v_mfma_f32_32x32x16_bf16: the lane's 16
+//           weights are already its slots of the B operands of the two
+//           16-token k-steps; each fp32 weight w = p * vs is split exactly
 //           into three bf16 terms (w = hi + mid + lo by truncation, the
 //           "bf16x3" form of an fp32 product) and V codes are exact in bf16,
 //           so every product is exact and only the fp32 accumulation order
-//           differs from a scalar loop: three v_mfma_f32_16x16x32_bf16 per 16
-//           dims.
+//           differs from a scalar loop: six products per 32 dims.
 // The second group's states are folded into the first's at the end through
 // LDS (the decode merge rule), so the result is deterministic.
 #include "q8kv_tile.hpp"
@@ -47,12 +47,12 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPfGroups = 2;                          // key-range halves per workgroup
 constexpr int kPfRowWaves = 4;                        // waves per half, one per 32 rows
 constexpr int kPfWaves = kPfGroups * kPfRowWaves;
-constexpr int kSets = 2;                              // 16-row query sets per wave
-constexpr int kPfRows = 16 * kSets;                   // query rows per wave
+constexpr int kPfRows = 32;                           // query rows per wave
 constexpr int kPfBlockRows = kPfRowWaves * kPfRows;   // query rows per workgroup
 constexpr int kKeyTile = 32;                          // tokens per step
 constexpr int kKRow = 136;                            // halves per staged K row (128 + 8 pad)
@@ -61,17 +61,17 @@ constexpr int kVRow = 40;                             // halves per staged V^T r
 // One staged key tile of one group.
 struct Stage {
     uint16_t k[kKeyTile * kKRow];     // K rows, fp16 codes, dims in order
-    uint16_t vt[kHeadDim * kVRow];    // V^T rows, bf16 codes; slot 8 lg + 4 h + e = token 16 h + 4 lg + e
-                                      // (chunk lg stored at vt_chunk(d, lg))
+    uint16_t vt[kHeadDim * kVRow];    // V^T rows, bf16 codes; chunk 2 r + hf, slot 4 g + e = token
+                                      // 16 r + 8 g + 4 hf + e (chunk c stored at vt_chunk(d, c))
     float kss[kKeyTile];              // ks * scale * log2(e)
     float vs[kKeyTile];
     uint32_t good;                    // bit t: token t's block id is valid
     uint32_t pad[3];
 };
-// Second group's per-lane states for the fold: [row wave][set][32 accumulators, M, S][lane].
-constexpr int kCombVals = 8 * 4 + 2;
+// Second group's per-lane states for the fold: [row wave][64 accumulators, M, S][lane].
+constexpr int kCombVals = 4 * 16 + 2;
 constexpr size_t kStageBytes = sizeof(Stage) * kPfGroups * 2;
-constexpr size_t kCombBytes = sizeof(float) * kPfRowWaves * kSets * kCombVals * 64;
+constexpr size_t kCombBytes = sizeof(float) * kPfRowWaves * kCombVals * 64;
 constexpr size_t kPfLds = kStageBytes > kCombBytes ? kStageBytes : kCombBytes;
 static_assert(sizeof(Stage) % 16 == 0, "stages stay 16-byte aligned");
 
@@ -98,18 +98,18 @@ struct TileRaw {
     bool bad;    // some block id behind this thread's loads is not
 };
 
-// The V share of thread gt: token quad a (tokens 4 a .. 4 a + 3, a = 4 h + lg
-// for tokens 16 h + 4 lg + e) and dim quad c (dims 4 c .. 4 c + 3).  Sixteen
-// neighbouring lanes read 64 contiguous bytes of a row, and the 32 lanes of a
-// half wave write 32 different bank pairs of the staged V^T (below).
+// The V share of thread gt: token quad a (tokens 4 a .. 4 a + 3, a = 4 r +
+// 2 g + hf for tokens 16 r + 8 g + 4 hf + e) and dim quad c (dims 4 c ..
+// 4 c + 3).  Sixteen neighbouring lanes read 64 contiguous bytes of a row,
+// and each sixteen write 16 different bank quads of the staged V^T (below).
 __device__ __forceinline__ int v_quad(int gt) { return (((gt >> 4) & 1) << 2) | (gt >> 6); }
 __device__ __forceinline__ int v_dims(int gt) { return (gt & 15) | (((gt >> 5) & 1) << 4); }
 
-// V^T row d keeps its four 16-byte chunks (lane group lg's 8 token slots)
-// at chunk lg ^ ((d / 16) % 4): the readers of a chunk (16 lanes, rows
-// 16 dt .. 16 dt + 15) are unaffected, and the writers of one dim of four
-// tokens (rows 4 c + dd) spread over every bank.
-__device__ __forceinline__ int vt_chunk(int d, int lg) { return lg ^ ((d >> 4) & 3); }
+// V^T row d keeps its four 16-byte chunks (one k-step and lane half's 8
+// token slots) at chunk c ^ ((d / 16) % 4): the readers of a chunk (rows
+// 32 dt + j) keep distinct banks within each 16 rows, and the writers of one
+// dim of four tokens (rows 4 c + dd) spread over every bank.
+__device__ __forceinline__ int vt_chunk(int d, int c) { return c ^ ((d >> 4) & 3); }
 
 // Block ids of a tile, fetched one tile ahead of its loads.  Big (kv_bs >= 32):
 // the tile lies in one block, one wave-uniform id; otherwise each thread
@@ -218,14 +218,14 @@ __device__ __forceinline__ void stage_tile(const PrefillParams &p, const TileRaw
     uint4 *kd = reinterpret_cast<uint4 *>(s.k + (gt >> 3) * kKRow + 16 * (gt & 7));
     kd[0] = make_uint4(kh16[0], kh16[1], kh16[2], kh16[3]);
     kd[1] = make_uint4(kh16[4], kh16[5], kh16[6], kh16[7]);
-    // V^T: dims 4 c + dd, tokens 4 a .. 4 a + 3 (a = 4 h + lg: slots 8 lg + 4 h ..)
+    // V^T: dims 4 c + dd, tokens 4 a .. 4 a + 3 (a = 4 r + 2 g + hf: chunk 2 r + hf, slots 4 g ..)
     const int a = v_quad(gt), c = v_dims(gt);
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd) {
         const int d = 4 * c + dd;
         const uint32_t f0 = __float_as_uint(byte_f(r.v[0], dd)), f1 = __float_as_uint(byte_f(r.v[1], dd));
         const uint32_t f2 = __float_as_uint(byte_f(r.v[2], dd)), f3 = __float_as_uint(byte_f(r.v[3], dd));
-        *reinterpret_cast<uint2 *>(s.vt + d * kVRow + 8 * vt_chunk(d, a & 3) + 4 * (a >> 2)) =
+        *reinterpret_cast<uint2 *>(s.vt + d * kVRow + 8 * vt_chunk(d, 2 * (a >> 2) + (a & 1)) + 4 * ((a >> 1) & 1)) =
             make_uint2(__builtin_amdgcn_perm(f1, f0, 0x07060302u), __builtin_amdgcn_perm(f3, f2, 0x07060302u));
     }
     if ((gt >> 6) == 0) {
@@ -267,8 +267,8 @@ template <bool Big>
 __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams p)
 {
     __shared__ __align__(16) unsigned char lds[kPfLds];
-    // each wave's query operands (read back by the same lanes every tile)
-    __shared__ __align__(16) v8h_t q_lds[kPfWaves][kSets][4][64];
+    // each wave's query operands, k-step s (dims 16 s + 8 hf ..), read back by the same lanes every tile
+    __shared__ __align__(16) v8h_t q_lds[kPfWaves][8][64];
     Stage *stages = reinterpret_cast<Stage *>(lds);   // [group][buffer]
     const int nkv = p.cache.nkv;
     const int b = blockIdx.x / nkv, kh = blockIdx.x - (blockIdx.x / nkv) * nkv;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
     // dispatched first, so the short ones fill in behind them
     const int rb = gridDim.y - 1 - blockIdx.y;
     const int G = 1 << p.log2g;
-    const int j = lane & 15, lg = lane >> 4;
+    const int j = lane & 31, hf = lane >> 5;   // the lane's query row in the wave, and its half
 
     const int r0 = uniform(p.q_start[b]), r1 = uniform(p.q_start[b + 1]);
     const int n = uniform(p.seq_lens[b]);
@@ -290,18 +290,15 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
         // a bad sequence (uniform over the workgroup): reported; its rows
         // that this workgroup covers are zeros
         if (kh == 0 && rb == 0 && threadIdx.x == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadSeqLen);
-        if (range_ok && grp == 0) {
+        const int rho = wrow0 + j;
+        if (range_ok && grp == 0 && rho < (nn << p.log2g)) {
+            const int i = rho >> p.log2g, g = rho & (G - 1);
+            float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
 #pragma unroll
-            for (int st = 0; st < kSets; ++st) {
-                const int rho = wrow0 + 16 * st + j;
-                if (rho < (nn << p.log2g)) {
-                    const int i = rho >> p.log2g, g = rho & (G - 1);
-                    float *o = p.out + ((size_t)(r0 + i) * p.nq + kh * G + g) * kHeadDim;
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-                        reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
+                for (int q4 = 0; q4 < 4; ++q4)
+                    reinterpret_cast<float4 *>(o + 32 * dt + 8 * q4 + 4 * hf)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         return;
     }
@@ -316,62 +313,60 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
     const int kt_lo = grp == 0 ? 0 : half, cnt = grp == 0 ? half : nkt - half;
     const int iters = nkt - half;   // the same for every wave: the barrier count
 
-    // this wave's rows: clamped to a real row (lanes past the end are computed
-    // and discarded) and their positions
+    // this lane's row, clamped to a real row (lanes past the end are computed
+    // and discarded), and its position
     const bool active = wrow0 < rows;
-    bool live[kSets] = {};
-    int qi[kSets] = {}, qg[kSets] = {}, pos[kSets] = {};
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const int rho = wrow0 + 16 * st + j;
-        live[st] = rho < rows;
-        const int rr = live[st] ? rho : rows - 1;
-        qi[st] = rr >> p.log2g;
-        qg[st] = rr & (G - 1);
-        pos[st] = p0 + qi[st];
-    }
+    const int rho = wrow0 + j;
+    const bool live = rho < rows;
+    const int rr = live ? rho : rows - 1;
+    const int qi = rr >> p.log2g, qg = rr & (G - 1);
+    const int pos = p0 + qi;
     const int pw_hi = p0 + (min(wrow0 + kPfRows - 1, rows - 1) >> p.log2g);   // the wave's largest position
     const int pw_lo = p0 + (wrow0 >> p.log2g);                                 // and smallest
 
-    // query codes as fp16, the B operands of the score products (dims
-    // 32 beta + 8 lg .. + 7), kept in LDS, and their block steps
-    v8h_t (*qb)[4][64] = q_lds[wave];
-    float qs[kSets][4];
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const size_t qrow = ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
+    // query codes as fp16, the B operands of the score products (k-step s:
+    // dims 16 s + 8 hf .. + 7 of query j), kept in LDS, and their block steps;
+    // the two halves of a 32-block sit in lanes j and j + 32
+    v8h_t (*qb)[64] = q_lds[wave];
+    float qs[4];
+    {
+        const float *qrow = p.q + ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) {
-            const float4 *src = reinterpret_cast<const float4 *>(p.q + qrow + 32 * beta + 8 * lg);
-            const float4 a = src[0], c = src[1];
-            const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+            const float4 a0 = *reinterpret_cast<const float4 *>(qrow + 32 * beta + 8 * hf);
+            const float4 a1 = *reinterpret_cast<const float4 *>(qrow + 32 * beta + 8 * hf + 4);
+            const float4 b0 = *reinterpret_cast<const float4 *>(qrow + 32 * beta + 16 + 8 * hf);
+            const float4 b1 = *reinterpret_cast<const float4 *>(qrow + 32 * beta + 16 + 8 * hf + 4);
+            const float x[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                                 b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
             float m = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-            m = max_rows32(max_rows16(m));   // the 32-block's max over the four lane groups
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
+            m = max_rows32(m);   // the 32-block's max over the two halves
             const BlockQuant bq = q_block_params(m);
-            v8h_t qc;
+            v8h_t c0, c1;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qc[e] = (_Float16)q_code(x[e], bq.recip);
-            qb[st][beta][lane] = qc;
-            qs[st][beta] = bq.qscale;
+            for (int e = 0; e < 8; ++e) {
+                c0[e] = (_Float16)q_code(x[e], bq.recip);
+                c1[e] = (_Float16)q_code(x[8 + e], bq.recip);
+            }
+            qb[2 * beta][lane] = c0;
+            qb[2 * beta + 1][lane] = c1;
+            qs[beta] = bq.qscale;
         }
     }
 
     // M is a reference max per query: the weights exp2(s - M) may exceed 1 by
     // up to 2^kLazyRescale, and S and the accumulators are rescaled only when
-    // some query's tile max rises above its M by more than that (the result
-    // is the same quantity; only rounding differs)
+    // the query's tile max rises above its M by more than that (the result is
+    // the same quantity; only rounding differs)
     constexpr float kLazyRescale = 8.0f;
-    float M[kSets], S[kSets];
-    v4f_t acc[kSets][8];
+    float M = -INFINITY, S = 0.0f;
+    v16f_t acc[4];
 #pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        M[st] = -INFINITY;
-        S[st] = 0.0f;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[st][dt] = v4f_t{0.f, 0.f, 0.f, 0.f};
-    }
+        for (int v = 0; v < 16; ++v) acc[dt][v] = 0.0f;
 
     const int32_t *bt = p.block_table + (size_t)b * p.max_blocks_per_seq;
     bool bad = false;
@@ -399,9 +394,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
         load_tile<Big>(p, kh, kt_lo * kKeyTile, p_hi, gt, off, ids0, raw);
         advance(0);
     }
-    // the lane's operand rows: K token 16 h + j, dims 32 beta + 8 lg ..;
-    // V^T dim 16 dt + j, slots 8 lg .. (chunk vt_chunk(16 dt + j, lg))
-    const int krow = j * kKRow + 8 * lg;
+    // the lane's K operand row: token j, dims 16 s + 8 hf ..
+    const int krow = j * kKRow + 8 * hf;
     for (int i = 0; i < iters; ++i) {
         // tile i is staged (buffer i % 2); buffer (i + 1) % 2 is free: its
         // readers finished tile i - 1 before this barrier
@@ -409,105 +403,115 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
         const Stage &sg = stages[2 * grp + (i & 1)];
         const int t0 = (kt_lo + i) * kKeyTile;
         const bool work = i < cnt && active && t0 <= pw_hi;
-        v8h_t ka[8], qv[4];
         if (i + 1 < cnt) advance(i + 1);
         if (!work) continue;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            ka[u] = *reinterpret_cast<const v8h_t *>(sg.k + krow + (u >> 2) * 16 * kKRow + 32 * (u & 3));
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) qv[beta] = qb[0][beta][lane];
 
         const uint32_t gmask = sg.good;
         // every row of the wave sees all 32 tokens of the tile: no masks
         const bool full = t0 + kKeyTile - 1 <= pw_lo && gmask == 0xffffffffu;
+        // block partials: c[beta][v] for token 8 (v / 4) + 4 hf + v % 4 of
+        // query j (two k-steps of 16 dims per block)
+        v16f_t c[4];
 #pragma unroll
-        for (int st = 0; st < kSets; ++st) {
-            if (st > 0) {   // the same K operands, the next set's query codes
+        for (int st = 0; st < 8; ++st) {
+            const v8h_t ka = *reinterpret_cast<const v8h_t *>(sg.k + krow + 16 * st);
+            const v8h_t qv = qb[st][lane];
+            v16f_t z;
+            if (st & 1) z = c[st >> 1];
+            else
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    ka[u] = *reinterpret_cast<const v8h_t *>(sg.k + krow + (u >> 2) * 16 * kKRow + 32 * (u & 3));
-#pragma unroll
-                for (int beta = 0; beta < 4; ++beta) qv[beta] = qb[st][beta][lane];
-            }
-            // block partials of query j with tokens 16 h + 4 lg + e (u = 4 h + beta)
-            v4f_t c[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                c[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u], qv[u & 3], v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            // V operands and steps are read now: the softmax below covers their latency
-            v8bf_t va[8];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                va[dt] = *reinterpret_cast<const v8bf_t *>(sg.vt + (16 * dt + j) * kVRow + 8 * vt_chunk(16 * dt + j, lg));
-            const float4 k0 = *reinterpret_cast<const float4 *>(sg.kss + 4 * lg);
-            const float4 k1 = *reinterpret_cast<const float4 *>(sg.kss + 16 + 4 * lg);
-            __builtin_amdgcn_sched_barrier(0);
-            const float4 v0 = *reinterpret_cast<const float4 *>(sg.vs + 4 * lg);
-            const float4 v1 = *reinterpret_cast<const float4 *>(sg.vs + 16 + 4 * lg);
-            const float kss[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const float vsv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            float s[8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // (P0 qs0 + P1 qs1) + (P3 qs3 + P2 qs2), the second product of each pair fused
-                    const float y01 = fmaf(c[4 * h + 1][e], qs[st][1], c[4 * h][e] * qs[st][0]);
-                    const float y23 = fmaf(c[4 * h + 2][e], qs[st][2], c[4 * h + 3][e] * qs[st][3]);
-                    s[4 * h + e] = (y01 + y23) * kss[4 * h + e];
-                }
-            uint32_t keep[8];
-            if (!full) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int tt = 16 * (u >> 2) + 4 * lg + (u & 3);   // token within the tile
-                    keep[u] = (t0 + tt <= pos[st] && ((gmask >> tt) & 1u)) ? 0xffffffffu : 0u;
-                    // branch-free mask (a select here becomes a divergent
-                    // branch); a masked token's step may be any bits, even NaN
-                    s[u] = __uint_as_float(bitsel(keep[u], __float_as_uint(s[u]), 0xff800000u));
-                }
-            }
-            float m = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-            m = max_rows32(max_rows16(m));   // the tile max of query j over the four lane groups
-            const bool grow = m > M[st] + kLazyRescale;   // also true on the first tile with a finite max
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                const float Mn = grow ? m : M[st];
-                const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
-                M[st] = Mn;
-                S[st] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[st][dt] *= alpha;
-            }
-            float w[8], psum = 0.0f;
-            if (full) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float pw = __builtin_amdgcn_exp2f(s[u] - M[st]);
-                    psum += pw;
-                    w[u] = pw * vsv[u];
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    // masked: weight 0 (M may still be -inf, and the step may be NaN)
-                    const float pw =
-                        __uint_as_float(bitsel(keep[u], __float_as_uint(__builtin_amdgcn_exp2f(s[u] - M[st])), 0u));
-                    psum += pw;
-                    w[u] = __uint_as_float(bitsel(keep[u], __float_as_uint(pw * vsv[u]), 0u));
-                }
-            }
-            S[st] += psum;
-            v8bf_t whi, wmid, wlo;
-            split_bf16x3(w, whi, wmid, wlo);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], whi, acc[st][dt], 0, 0, 0);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], wmid, acc[st][dt], 0, 0, 0);
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[st][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], wlo, acc[st][dt], 0, 0, 0);
+                for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+            c[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qv, z, 0, 0, 0);
         }
+        // V operands: dims 32 dt + j, k-step r = tokens 16 r + 8 g + 4 hf + e
+        // (chunk 2 r + hf); read now, the softmax covers their latency
+        v8bf_t va[8];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int d = 32 * dt + j;
+                va[2 * dt + r] = *reinterpret_cast<const v8bf_t *>(sg.vt + d * kVRow + 8 * vt_chunk(d, 2 * r + hf));
+            }
+        float kss[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 k4 = *reinterpret_cast<const float4 *>(sg.kss + 8 * q4 + 4 * hf);
+            kss[4 * q4] = k4.x; kss[4 * q4 + 1] = k4.y; kss[4 * q4 + 2] = k4.z; kss[4 * q4 + 3] = k4.w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float s[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            // (P0 qs0 + P1 qs1) + (P3 qs3 + P2 qs2), the second product of each pair fused
+            const float y01 = fmaf(c[1][v], qs[1], c[0][v] * qs[0]);
+            const float y23 = fmaf(c[2][v], qs[2], c[3][v] * qs[3]);
+            s[v] = (y01 + y23) * kss[v];
+        }
+        uint32_t keep[16];
+        if (!full) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tt = 8 * (v >> 2) + 4 * hf + (v & 3);   // token within the tile
+                keep[v] = (t0 + tt <= pos && ((gmask >> tt) & 1u)) ? 0xffffffffu : 0u;
+                // branch-free mask (a select here becomes a divergent
+                // branch); a masked token's step may be any bits, even NaN
+                s[v] = __uint_as_float(bitsel(keep[v], __float_as_uint(s[v]), 0xff800000u));
+            }
+        }
+        float m = s[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) m = fmaxf(m, s[v]);
+        m = max_rows32(m);   // the tile max of query j over both halves
+        const bool grow = m > M + kLazyRescale;   // also true on the first tile with a finite max
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float Mn = grow ? m : M;
+            const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+            M = Mn;
+            S *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+        }
+        float vsv[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(sg.vs + 8 * q4 + 4 * hf);
+            vsv[4 * q4] = v4.x; vsv[4 * q4 + 1] = v4.y; vsv[4 * q4 + 2] = v4.z; vsv[4 * q4 + 3] = v4.w;
+        }
+        float w[16], psum = 0.0f;
+        if (full) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float pw = __builtin_amdgcn_exp2f(s[v] - M);
+                psum += pw;
+                w[v] = pw * vsv[v];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                // masked: weight 0 (M may still be -inf, and the step may be NaN)
+                const float pw =
+                    __uint_as_float(bitsel(keep[v], __float_as_uint(__builtin_amdgcn_exp2f(s[v] - M)), 0u));
+                psum += pw;
+                w[v] = __uint_as_float(bitsel(keep[v], __float_as_uint(pw * vsv[v]), 0u));
+            }
+        }
+        S += psum;
+        v8bf_t wt[3][2];   // [term][k-step]: the lane's weights v = 8 r .. 8 r + 7
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float w8[8] = {w[8 * r], w[8 * r + 1], w[8 * r + 2], w[8 * r + 3],
+                                 w[8 * r + 4], w[8 * r + 5], w[8 * r + 6], w[8 * r + 7]};
+            split_bf16x3(w8, wt[0][r], wt[1][r], wt[2][r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * dt + r], wt[term][r], acc[dt], 0, 0, 0);
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, kDevBadBlockId);
 
@@ -515,50 +519,42 @@ __global__ __launch_bounds__(64 * kPfWaves) void q8_prefill_kernel(PrefillParams
     // accumulators rescaled to it and summed in key order ("9-2" §2 segment 2
     // rule applied to partial states); deterministic
     __syncthreads();   // every wave is done with the stages
-    float(*comb)[kSets][kCombVals][64] = reinterpret_cast<float(*)[kSets][kCombVals][64]>(lds);
+    float(*comb)[kCombVals][64] = reinterpret_cast<float(*)[kCombVals][64]>(lds);
     if (active && grp == 1) {
 #pragma unroll
-        for (int st = 0; st < kSets; ++st) {
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) comb[rw][st][4 * dt + e][lane] = acc[st][dt][e];
-            comb[rw][st][32][lane] = M[st];
-            comb[rw][st][33][lane] = S[st];
-        }
+            for (int v = 0; v < 16; ++v) comb[rw][16 * dt + v][lane] = acc[dt][v];
+        comb[rw][64][lane] = M;
+        comb[rw][65][lane] = S;
     }
     __syncthreads();
     if (!active || grp != 0) return;
-#pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const float M1 = comb[rw][st][32][lane];
-        const float Mn = fmaxf(M[st], M1);
-        const float a0 = M[st] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M[st] - Mn);
+    {
+        const float M1 = comb[rw][64][lane];
+        const float Mn = fmaxf(M, M1);
+        const float a0 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
         const float a1 = M1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M1 - Mn);
-        S[st] = fmaf(comb[rw][st][33][lane], a1, S[st] * a0);
+        S = fmaf(comb[rw][65][lane], a1, S * a0);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[st][dt][e] = fmaf(comb[rw][st][4 * dt + e][lane], a1, acc[st][dt][e] * a0);
+            for (int v = 0; v < 16; ++v) acc[dt][v] = fmaf(comb[rw][16 * dt + v][lane], a1, acc[dt][v] * a0);
     }
-
-    float Ssum[kSets];
+    const float Ssum = sum_rows32(S);   // the two halves hold different tokens
+    if (!live) return;
+    float *o = p.out + ((size_t)(r0 + qi) * p.nq + kh * G + qg) * kHeadDim;
 #pragma unroll
-    for (int st = 0; st < kSets; ++st) Ssum[st] = sum_rows32(sum_rows16(S[st]));   // lane groups hold different tokens
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int st = 0; st < kSets; ++st) {
-        const float Sst = Ssum[st];
-        if (!live[st]) continue;
-        float *o = p.out + ((size_t)(r0 + qi[st]) * p.nq + kh * G + qg[st]) * kHeadDim;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            // one division at the end, per element
-            const v4f_t a = acc[st][dt];
-            reinterpret_cast<float4 *>(o + 16 * dt + 4 * lg)[0] =
-                Sst > 0.0f ? make_float4(a[0] / Sst, a[1] / Sst, a[2] / Sst, a[3] / Sst)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            // dims 32 dt + 8 q4 + 4 hf + e; one division at the end, per element
+            const v16f_t &a = acc[dt];
+            reinterpret_cast<float4 *>(o + 32 * dt + 8 * q4 + 4 * hf)[0] =
+                Ssum > 0.0f ? make_float4(a[4 * q4] / Ssum, a[4 * q4 + 1] / Ssum, a[4 * q4 + 2] / Ssum,
+                                          a[4 * q4 + 3] / Ssum)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    }
 }
 
 hipError_t launch_prefill(const q8_kv_layer &layer, const q8_batch &batch, int nq, const int32_t *q_start,
