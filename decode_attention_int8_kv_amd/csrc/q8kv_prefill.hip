@@ -43,7 +43,6 @@
 
 namespace q8kv {
 
-typedef float v4f_t __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
