@@ -70,3 +70,5 @@ def test_streaming_kernels_keep_their_occupancy(resources):
     assert occ("q8_attn_partial_kernelILi2ELb1ELb1E") >= 3
     assert occ("q8_attn_f32_partial_kernelILi2E") >= 4
     assert occ("q8_attn_partial_kernelILi4ELb1E") >= 2
+    # the prefill's 8-wave workgroup needs two waves per SIMD (one workgroup per CU)
+    assert occ("q8_prefill_kernel") >= 2
