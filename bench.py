@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="only measure the read ceiling: stream a buffer of this many MiB once per launch "
                          "(q8_stream_read), plain and non-temporal, over 256 / 512 / 1024 workgroups")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="only measure instruction issue (q8_issue_probe): VALU waves alone, matrix-core waves "
+                         "alone, both on the same SIMDs, and two or four VALU waves per SIMD")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "q8_attn_partial_kernel_hbm_traffic.json"),
@@ -586,6 +589,9 @@ def main():
     if args.read_probe:
         read_probe(torch, q8, dev, args.read_probe, args.steps, args.warmup)
         return
+    if args.issue_probe:
+        issue_probe(torch, q8, dev, args.steps, args.warmup)
+        return
     w = workloads.WORKLOADS[args.workload]
     if args.path == "prefill":
         if w.append_per_step <= 1:
@@ -705,6 +711,39 @@ def read_probe(torch, q8, dev, mib, reps, warmup):
     print(json.dumps({"read_probe_bytes": buf.numel(), "reps": reps, "results": res,
                       "best_GBps": best["GBps"], "best_pct_of_hbm_peak": round(100 * best["GBps"] / HBM_PEAK_GBS, 2)}),
           flush=True)
+
+
+def issue_probe(torch, q8, dev, reps, warmup):
+    """Instruction issue on the CUs (q8_issue_probe, one workgroup per CU):
+    cycles at 2.4 GHz per launch for each mode, and the cycles per VALU FMA
+    and per matrix-core product of one wave that they imply."""
+    wg, vit, mit = 256, 4096, 512
+    out = torch.empty(wg * 1024, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    reps = max(reps, 3)
+    names = ["1 VALU wave per SIMD", "1 matrix-core wave per SIMD", "1 VALU + 1 matrix-core wave per SIMD",
+             "2 VALU waves per SIMD", "4 VALU waves per SIMD"]
+    res = {}
+    for mode in range(5):
+        for _ in range(max(warmup, 1)):
+            q8.issue_probe(out, mode, vit, mit, wg)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            q8.issue_probe(out, mode, vit, mit, wg)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])) * 1e3
+        res[names[mode]] = {"us": round(us, 2), "cycles": round(us * 2400.0)}
+    fma = vit * 8   # FMAs per VALU wave
+    mm = mit * 4    # products per matrix-core wave
+    c = [res[n]["cycles"] for n in names]
+    print(json.dumps({"issue_probe": res, "valu_fmas_per_wave": fma, "mfma_products_per_wave": mm,
+                      "cycles_per_fma_one_wave": round(c[0] / fma, 2),
+                      "cycles_per_fma_per_simd_two_waves": round(c[3] / (2 * fma), 2),
+                      "cycles_per_fma_per_simd_four_waves": round(c[4] / (4 * fma), 2),
+                      "cycles_per_product_one_wave": round(c[1] / mm, 2),
+                      "both_over_valu_alone": round(c[2] / c[0], 3)}), flush=True)
 
 
 # the sources that define the q8 decode partial kernel and its launch plan

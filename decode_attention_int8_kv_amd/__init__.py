@@ -10,7 +10,7 @@ Entry points (same names as the C ABI, without the ``q8_`` prefix):
   kv_append, decode_attn, decode_attn_partial, decode_attn_merge,
   decode_attn_workspace_bytes, decode_attn_auto_parts, decode_step,
   decode_step_partial, decode_attn_f32, decode_attn_f32_partial,
-  decode_attn_sparse, decode_attn_sparse_workspace_bytes, prefill_attn,
+  decode_attn_sparse, decode_attn_sparse_workspace_bytes, prefill_attn, issue_probe,
   quantize_q, qk_block_partials, abi_version, status_string, last_error.
 
 Every entry point checks the tensors it passes on (dtype, contiguity, size,
@@ -505,6 +505,21 @@ def stream_read(buf, workgroups: int, nontemporal: bool, sink, stream=None):
     st = _load().q8_stream_read(_ptr(buf), _nbytes(buf), int(workgroups), int(bool(nontemporal)), _ptr(sink),
                                 _stream(stream))
     _check(st, "q8_stream_read")
+
+
+def issue_probe(out, mode: int, valu_iters: int, mfma_iters: int, workgroups: int, stream=None):
+    """q8_issue_probe measurement hook (VALU and matrix-core issue on one CU);
+    out: fp32 GPU scratch tensor of at least workgroups * 1024 elements."""
+    import torch
+    lib = _load()
+    if not getattr(lib, "_issue_probe_typed", False):
+        lib.q8_issue_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p]
+        lib.q8_issue_probe.restype = ctypes.c_int32
+        lib._issue_probe_typed = True
+    _Args().need(out, "out", torch.float32, int(workgroups) * 1024).done()
+    st = lib.q8_issue_probe(_ptr(out), int(mode), int(valu_iters), int(mfma_iters), int(workgroups), _stream(stream))
+    _check(st, "q8_issue_probe")
 
 
 def abi_version() -> int:

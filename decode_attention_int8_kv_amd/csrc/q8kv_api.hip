@@ -357,6 +357,17 @@ q8_status q8_stream_read(const void *buf, size_t bytes, int32_t workgroups, int3
     return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_stream_read");
 }
 
+q8_status q8_issue_probe(float *out, int32_t mode, int32_t valu_iters, int32_t mfma_iters, int32_t workgroups,
+                         void *stream)
+{
+    if (!out || !aligned(out, 4) || mode < 0 || mode > 4) return Q8_EINVAL;
+    if (valu_iters < 1 || valu_iters > (1 << 20) || mfma_iters < 1 || mfma_iters > (1 << 20)) return Q8_EINVAL;
+    if (workgroups < 1 || workgroups > 65536) return Q8_EINVAL;
+    hipError_t e = q8kv::launch_issue_probe(out, mode, valu_iters, mfma_iters, workgroups,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8_OK : hip_fail(e, "q8_issue_probe");
+}
+
 const char *q8_status_string(int32_t status)
 {
     switch (status) {

@@ -75,5 +75,7 @@ hipError_t launch_step_plan(const q8_kv_layer &layer, const q8_batch &batch, int
 
 hipError_t launch_stream_read(const void *buf, size_t bytes, int workgroups, int nontemporal, uint32_t *sink,
                               hipStream_t stream);
+hipError_t launch_issue_probe(float *out, int mode, int valu_iters, int mfma_iters, int workgroups,
+                              hipStream_t stream);
 
 }  // namespace q8kv

@@ -7,6 +7,12 @@
 // lanes, every lane four 16-byte loads in flight, plain or non-temporal (the
 // hint the decode's cache loads carry), and a value folded from every load
 // written only if it equals a constant (so no load can be dropped).
+//
+// A second hook measures instruction issue on one CU: how fast one or more
+// waves of a SIMD issue fp32 FMAs, how fast one wave issues 32x32x16 bf16
+// matrix-core products, and whether a SIMD runs one wave's matrix-core
+// products while another wave issues VALU (the prefill's waves alternate
+// between the two).
 #include "q8kv_internal.hpp"
 
 namespace q8kv {
@@ -48,6 +54,60 @@ hipError_t launch_stream_read(const void *buf, size_t bytes, int workgroups, int
     else
         hipLaunchKernelGGL(q8_stream_read_kernel<false>, dim3(workgroups), dim3(kProbeLanes), 0, stream, b, n16,
                            sink);
+    return hipGetLastError();
+}
+
+// Waves 0-3 of an 8-wave workgroup (wave w and w + 4 share SIMD w % 4 on
+// this GPU) run eight independent FMA chains for valu_iters rounds, waves 4-7
+// four independent v_mfma_f32_32x32x16_bf16 chains for mfma_iters rounds.
+// mode 0: the VALU waves only; 1: the matrix-core waves only; 2: both;
+// 3: all eight waves VALU; 4: a 16-wave workgroup, all VALU.  Each thread
+// writes one value to out (so nothing is removed as dead).
+typedef float v16f_probe __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf_probe __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(1024) void q8_issue_probe_kernel(float *out, int valu_iters, int mfma_iters, int mode)
+{
+    const int wave = threadIdx.x >> 6;
+    float r = 0.0f;
+    if ((wave < 4 && mode != 1) || mode >= 3) {
+        float a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = threadIdx.x * 0.001f + k;
+        for (int i = 0; i < valu_iters; ++i) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = fmaf(a[k], 0.999f, 0.5f);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r += a[k];
+    }
+    if (wave >= 4 && (mode == 1 || mode == 2)) {
+        v8bf_probe x, y;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            x[k] = (__bf16)(0.001f * k);
+            y[k] = (__bf16)(0.002f * k);
+        }
+        v16f_probe c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) c[q][k] = 0.0f;
+        for (int i = 0; i < mfma_iters; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c[q], 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r += c[q][0];
+    }
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+hipError_t launch_issue_probe(float *out, int mode, int valu_iters, int mfma_iters, int workgroups,
+                              hipStream_t stream)
+{
+    hipLaunchKernelGGL(q8_issue_probe_kernel, dim3(workgroups), dim3(mode == 4 ? 1024 : 512), 0, stream, out,
+                       valu_iters, mfma_iters, mode);
     return hipGetLastError();
 }
 

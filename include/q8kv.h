@@ -377,6 +377,23 @@ q8_status q8_qk_block_partials(const q8_kv_layer *layer, const q8_batch *batch, 
 q8_status q8_stream_read(const void *buf, size_t bytes, int32_t workgroups, int32_t nontemporal,
                          uint32_t *sink, void *stream);
 
+/* Measurement hook: instruction issue on the matrix cores and the VALU.  Each
+ * of `workgroups` workgroups (512 lanes; 1024 in mode 4) runs, in waves 0-3,
+ * eight independent fp32 FMA chains for valu_iters rounds (8 FMAs per round)
+ * and, in waves 4-7, four independent v_mfma_f32_32x32x16_bf16 chains for
+ * mfma_iters rounds (4 products per round); waves w and w + 4 share a SIMD.
+ * mode 0: VALU waves only (one per SIMD); 1: matrix-core waves only; 2: both;
+ * 3: all eight waves VALU (two per SIMD); 4: sixteen VALU waves (four per
+ * SIMD).  The times of the modes show the VALU rate one wave reaches, the
+ * rate several waves reach, and whether a SIMD overlaps one wave's
+ * matrix-core products with another wave's VALU -- what bounds the batched
+ * prefill, whose waves alternate between the two.  out: device fp32 scratch
+ * of workgroups * 1024 elements (4-byte aligned; written, values
+ * meaningless).  mode in [0, 4], iteration counts in [1, 2^20], workgroups
+ * in [1, 65536]. */
+q8_status q8_issue_probe(float *out, int32_t mode, int32_t valu_iters, int32_t mfma_iters, int32_t workgroups,
+                         void *stream);
+
 /* Short English name of a status code (static string). */
 const char *q8_status_string(int32_t status);
 /* Text of the last Q8_EHIP error on the calling thread ("" if none). */

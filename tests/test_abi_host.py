@@ -182,6 +182,20 @@ def test_stream_read_validation(q8):
     assert lib.q8_stream_read(FAKE, 1024, 256, 1, None, None) == -1
 
 
+def test_issue_probe_validation(q8):
+    lib = q8.lib()
+    f = lib.q8_issue_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 0, 16, 16, 256, None) == -1       # no buffer
+    assert f(FAKE + 2, 0, 16, 16, 256, None) == -1   # misaligned
+    assert f(FAKE, 5, 16, 16, 256, None) == -1       # unknown mode
+    assert f(FAKE, -1, 16, 16, 256, None) == -1
+    assert f(FAKE, 0, 0, 16, 256, None) == -1        # iteration counts
+    assert f(FAKE, 0, 16, (1 << 20) + 1, 256, None) == -1
+    assert f(FAKE, 0, 16, 16, 0, None) == -1         # workgroups
+    assert f(FAKE, 0, 16, 16, 65537, None) == -1
+
+
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     import decode_attention_int8_kv_amd as m
     monkeypatch.setattr(m, "_lib", None)
