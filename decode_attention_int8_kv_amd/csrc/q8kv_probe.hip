@@ -74,7 +74,15 @@ __global__ __launch_bounds__(1024) void q8_issue_probe_kernel(float *out, int va
         float a[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) a[k] = threadIdx.x * 0.001f + k;
-        for (int i = 0; i < valu_iters; ++i) {
+        // eight rounds per loop trip: 64 FMAs per branch
+        int i = 0;
+        for (; i + 8 <= valu_iters; i += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) a[k] = fmaf(a[k], 0.999f, 0.5f);
+        }
+        for (; i < valu_iters; ++i) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) a[k] = fmaf(a[k], 0.999f, 0.5f);
         }
@@ -93,7 +101,15 @@ __global__ __launch_bounds__(1024) void q8_issue_probe_kernel(float *out, int va
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int k = 0; k < 16; ++k) c[q][k] = 0.0f;
-        for (int i = 0; i < mfma_iters; ++i) {
+        // four rounds per loop trip: 16 products per branch
+        int i = 0;
+        for (; i + 4 <= mfma_iters; i += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c[q], 0, 0, 0);
+        }
+        for (; i < mfma_iters; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c[q], 0, 0, 0);
         }
